@@ -1,0 +1,199 @@
+"""Pins of the oracle's three GEMMs, fused bias and bias gradient (CPU).
+
+Checked against exact rational arithmetic (tiny shapes, every index written
+out as a loop so a transposed operand or wrong index fails), torch's CPU
+float64 matmul over torch-decoded float8 operands (an independent decoder
+and product), closed forms (identity weight, constant gradient) and the
+pages' statement that the fused bias is within one bf16 ulp of the split
+path.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import fp8_oracle as O
+
+TF8 = {O.E4M3: torch.float8_e4m3fn, O.E5M2: torch.float8_e5m2}
+
+
+def _codes(shape, fmt, rng):
+    """Random finite codes of the format."""
+    tab = O.decode_table(fmt)
+    finite = np.array([c for c in range(256) if np.isfinite(tab[c])], np.uint8)
+    return rng.choice(finite, size=shape)
+
+
+def _frac(code, fmt):
+    return Fraction(O.decode(int(code), fmt))
+
+
+def _bf16_of_fraction(fr: Fraction) -> int:
+    """Exact RNE of a rational to bf16 bits (independent of O.bf16_bits)."""
+    if fr == 0:
+        return 0
+    sign = 0x8000 if fr < 0 else 0
+    a = abs(fr)
+    e = 0
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    sp = Fraction(2) ** (e - 7)
+    q = a / sp
+    fl = q.numerator // q.denominator
+    rem = q - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    v = np.array([float(fl * sp)], np.float32).view(np.uint32)[0]
+    return sign | int(v >> 16)
+
+
+# ---------------------------------------------------------------- exact
+
+@pytest.mark.parametrize("fmt_a,fmt_b", [(O.E4M3, O.E4M3), (O.E5M2, O.E4M3)])
+def test_three_gemms_exact_rational_tiny(fmt_a, fmt_b):
+    rng = np.random.default_rng(11)
+    M, N, K = 3, 5, 7
+    sa, sb = np.float32(3.5), np.float32(0.625)
+    # forward: Y[m,n] = sum_k x[m,k] w[n,k] / (sx sw) + b[n]   (both fmt_b)
+    x8 = _codes((M, K), fmt_b, rng)
+    w8 = _codes((N, K), fmt_b, rng)
+    bias = rng.standard_normal(N).astype(np.float32)
+    bias_bits = O.bf16_bits(bias.astype(np.float64))
+    ref = O.linear_fwd(x8, w8, fmt_b, sa, sb, O.bias_values(bias_bits, "bf16"))
+    for m in range(M):
+        for n in range(N):
+            acc = sum(_frac(x8[m, k], fmt_b) * _frac(w8[n, k], fmt_b) for k in range(K))
+            exact = acc / (Fraction(float(sa)) * Fraction(float(sb))) + \
+                Fraction(float(O.bf16_value(bias_bits[n])))
+            assert ref.y_bits[m, n] == _bf16_of_fraction(exact)
+            assert abs(Fraction(float(ref.r[m, n])) - exact) <= abs(exact) * Fraction(1, 2**50)
+    # dX[m,k] = sum_n g[m,n] w[n,k] / (sg sw)
+    g8 = _codes((M, N), fmt_a, rng)
+    ref = O.linear_bwd_dx(g8, fmt_a, w8, fmt_b, sa, sb)
+    for m in range(M):
+        for k in range(K):
+            acc = sum(_frac(g8[m, n], fmt_a) * _frac(w8[n, k], fmt_b) for n in range(N))
+            exact = acc / (Fraction(float(sa)) * Fraction(float(sb)))
+            assert ref.y_bits[m, k] == _bf16_of_fraction(exact)
+    # dW[n,k] = sum_m g[m,n] x[m,k] / (sg sx)
+    ref = O.linear_bwd_dw(g8, fmt_a, x8, fmt_b, sa, sb)
+    for n in range(N):
+        for k in range(K):
+            acc = sum(_frac(g8[m, n], fmt_a) * _frac(x8[m, k], fmt_b) for m in range(M))
+            exact = acc / (Fraction(float(sa)) * Fraction(float(sb)))
+            assert ref.y_bits[n, k] == _bf16_of_fraction(exact)
+
+
+def test_fp64_accumulation_exact_for_e4m3():
+    """e4m3 values are multiples of 2^-9 below 2^9: with K = 4096 every partial
+    sum fits 53 bits, so the fp64 matmul equals the exact integer sum."""
+    rng = np.random.default_rng(5)
+    x8 = _codes((4, 4096), O.E4M3, rng)
+    w8 = _codes((3, 4096), O.E4M3, rng)
+    X = O.decode_array(x8, O.E4M3)
+    W = O.decode_array(w8, O.E4M3)
+    Xi = (X * 2 ** 9).astype(np.int64)
+    Wi = (W * 2 ** 9).astype(np.int64)
+    exact = (Xi[:, None, :] * Wi[None, :, :]).sum(-1)
+    ref = O.linear_fwd(x8, w8, O.E4M3, 1.0, 1.0)
+    assert np.array_equal(ref.r * 2 ** 18, exact.astype(np.float64))
+
+
+# ---------------------------------------------------------------- torch
+
+@pytest.mark.parametrize("which", ["fwd", "dx", "dw"])
+def test_gemms_match_torch_float64(which):
+    rng = np.random.default_rng(21)
+    M, N, K = 64, 48, 80
+    x8 = _codes((M, K), O.E4M3, rng)
+    w8 = _codes((N, K), O.E4M3, rng)
+    g8 = _codes((M, N), O.E5M2, rng)
+    sx, sw, sg = np.float32(20.0), np.float32(900.0), np.float32(3.0e4)
+
+    def t(q, fmt):
+        return torch.from_numpy(q).view(TF8[fmt]).to(torch.float64)
+
+    if which == "fwd":
+        ref = O.linear_fwd(x8, w8, O.E4M3, sx, sw)
+        tr = (t(x8, O.E4M3) @ t(w8, O.E4M3).T) / (float(sx) * float(sw))
+    elif which == "dx":
+        ref = O.linear_bwd_dx(g8, O.E5M2, w8, O.E4M3, sg, sw)
+        tr = (t(g8, O.E5M2) @ t(w8, O.E4M3)) / (float(sg) * float(sw))
+    else:
+        ref = O.linear_bwd_dw(g8, O.E5M2, x8, O.E4M3, sg, sx)
+        tr = (t(g8, O.E5M2).T @ t(x8, O.E4M3)) / (float(sg) * float(sx))
+    assert np.allclose(ref.r, tr.numpy(), rtol=1e-13, atol=0)
+    assert np.array_equal(
+        ref.y_bits, tr.to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ) or np.abs(O.bf16_value(ref.y_bits) - tr.numpy()).max() <= O.bf16_ulp(tr.numpy()).max()
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_identity_weight():
+    rng = np.random.default_rng(2)
+    x8 = _codes((128, 256), O.E4M3, rng)
+    w8 = np.where(np.eye(256, dtype=bool), 0x38, 0x00).astype(np.uint8)  # 1.0 on the diagonal
+    sx, sw = np.float32(64.0), np.float32(2.0)
+    beta = O.bf16_value(O.bf16_bits(rng.standard_normal(256) * 0.01))
+    ref = O.linear_fwd(x8, w8, O.E4M3, sx, sw, beta)
+    assert np.array_equal(ref.r, O.decode_array(x8, O.E4M3) / 128.0 + beta)
+
+
+def test_fp8_bias_dequantized_after_operand_scaling():
+    b8 = np.array([0x38, 0xB8, 0x7E, 0x01], np.uint8)  # 1, -1, 448, 2^-9
+    vals = O.bias_values(b8, "e4m3", np.float32(8.0))
+    assert list(vals) == [1 / 8, -1 / 8, 56.0, 2.0 ** -12]
+    x8 = np.zeros((2, 4), np.uint8)
+    w8 = np.zeros((4, 4), np.uint8)
+    ref = O.linear_fwd(x8, w8, O.E4M3, 5.0, 7.0, vals)
+    assert np.array_equal(ref.r, np.tile(vals, (2, 1)))
+
+
+def test_fused_bias_within_one_ulp_of_split_path():
+    rng = np.random.default_rng(9)
+    x8 = _codes((96, 192), O.E4M3, rng)
+    w8 = _codes((64, 192), O.E4M3, rng)
+    beta = O.bf16_value(O.bf16_bits(rng.standard_normal(64) * 50.0))
+    fused = O.linear_fwd(x8, w8, O.E4M3, 30.0, 500.0, beta)
+    plain = O.linear_fwd(x8, w8, O.E4M3, 30.0, 500.0)
+    split = O.bf16_value(O.bf16_bits(O.bf16_value(plain.y_bits) + beta))
+    diff = np.abs(O.bf16_value(fused.y_bits) - split)
+    # one ulp at the larger of the output and the pre-bias product (the
+    # split path rounds once at the product's magnitude)
+    assert np.all(diff <= np.maximum(O.bf16_ulp(fused.r), O.bf16_ulp(plain.r)))
+    assert np.mean(diff == 0) > 0.5
+    # and the fused result is at least as close to the exact value
+    assert np.all(np.abs(O.bf16_value(fused.y_bits) - fused.r) <= np.abs(split - fused.r))
+
+
+def test_bias_grad_closed_form_and_brute_force():
+    M, N = 512, 24
+    c = O.bf16_value(O.bf16_bits(np.full(N, 0.0078125)))
+    g = np.tile(c, (M, 1))
+    ref = O.bias_grad(g)
+    assert np.array_equal(ref.r, M * c)
+    rng = np.random.default_rng(4)
+    g = O.bf16_value(O.bf16_bits(rng.standard_normal((37, 5)) * 1e-3))
+    ref = O.bias_grad(g)
+    for n in range(5):
+        exact = sum(Fraction(float(v)) for v in g[:, n])
+        assert ref.y_bits[n] == _bf16_of_fraction(exact)
+    # pre-quantized gradient: dequantized before the sum
+    g8 = _codes((37, 5), O.E5M2, rng)
+    deq = O.dequantized(g8, O.E5M2, np.float32(4096.0))
+    assert np.array_equal(deq, O.decode_array(g8, O.E5M2) / 4096.0)
+
+
+def test_tolerance_contract_shape():
+    rng = np.random.default_rng(1)
+    x8 = _codes((8, 32), O.E4M3, rng)
+    w8 = _codes((4, 32), O.E4M3, rng)
+    ref = O.linear_fwd(x8, w8, O.E4M3, 2.0, 4.0)
+    tol = O.gemm_tolerance(ref)
+    X, W = O.decode_array(x8, O.E4M3), O.decode_array(w8, O.E4M3)
+    assert np.allclose(tol, 2.0 ** -7 * (np.abs(X) @ np.abs(W).T) / 8.0 + O.bf16_ulp(ref.r))
