@@ -1,0 +1,241 @@
+/*
+ * fp8linear.h -- C ABI of the MI355X (gfx950) FP8 linear-layer hot path.
+ *
+ * One library, libfp8linear.so, hand-written HIP for CDNA4.  Four entry
+ * points do the work of one FP8 linear layer in training:
+ *
+ *   fp8_quantize        per-tensor quantize with on-device amax and the
+ *                       delayed-scaling ring finalize in the same launch
+ *   fp8_linear_fwd      quantize X and W (unless pre-quantized), then
+ *                       Y = X8 W8^T / (sx sw) + bias
+ *   fp8_linear_bwd_dx   quantize G (unless pre-quantized), then
+ *                       dX = G8 W8 / (sg sw)
+ *   fp8_linear_bwd_dw   quantize G (unless pre-quantized), then
+ *                       dW = G8^T X8 / (sg sx) and optionally db = sum_m G
+ *
+ * Sources (AstrAI commit-log pages, cited by commit and page path):
+ *   [P1] commit 2eeac02d, page tests/extension
+ *   [P2] commit 2eeac02d, page csrc
+ *   [P3] commit 057c0d33, page astrai/extension/ops
+ *   [P4] commit 4019ddac, page astrai
+ *   [P5] commit 3e57cc80, page astrai/extension/fp8.py
+ *   [OCP] OCP 8-bit Floating Point Specification (OFP8) rev 1.0
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Matrices are row-major and contiguous: X [M,K], W [N,K], Y [M,N],
+ *   G [M,N], dX [M,K], dW [N,K], bias/db [N].  M = tokens, K = in features,
+ *   N = out features.  Any M, N, K >= 0 is computed correctly (ragged tails
+ *   are guarded); the fast paths want multiples of 128 and 16-byte aligned
+ *   buffers.
+ * - Every pointer except the fp8_ring_t / fp8_operand_t structs themselves
+ *   is a DEVICE pointer.  The caller allocates and owns every buffer; the
+ *   library never allocates, frees or synchronizes, and enqueues all work on
+ *   the given stream.  A NULL optional pointer means "absent" ([P2] entry on
+ *   null defaults for optional pointer members).
+ * - Outputs must not alias inputs.  Scale outputs must not alias a ring's
+ *   own scale slot (the snapshot rule of [P3]: the GEMM dequantizes with the
+ *   scale the quantize used, not with the one the ring publishes next).
+ * - Validation completes before anything is enqueued: on any error status
+ *   nothing runs and nothing is modified (ring->seeded included).
+ * - Errors: FP8_OK = 0; otherwise one of fp8_status_t.  FP8_ERR_HIP means a
+ *   launch failed after validation (hipGetLastError); work enqueued before
+ *   the failing launch may have run.
+ */
+#ifndef FP8LINEAR_H
+#define FP8LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8_ABI_VERSION 1
+#define FP8_RING_MAX_HIST 1024
+
+typedef enum {
+  FP8_OK = 0,
+  FP8_ERR_NULL = 1,   /* a required pointer is NULL */
+  FP8_ERR_SHAPE = 2,  /* a size is negative or a byte count overflows int64 */
+  FP8_ERR_DTYPE = 3,  /* unknown format/dtype enum, or an fp8 operand whose
+                         format does not match the call's format ([P3] entry
+                         validating the fmt enum; [P1] pre-quantized operands
+                         must match fmt) */
+  FP8_ERR_RING = 4,   /* ring hist_len outside [1, 1024], dev NULL or not
+                         256-byte aligned, or a scale output aliasing it */
+  FP8_ERR_HIP = 5     /* a kernel launch failed */
+} fp8_status_t;
+
+/* Formats: OCP E4M3 (max 448, no inf) and E5M2 (max 57344) [OCP]. */
+typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_format_t;
+
+/* Element types of tensors crossing the boundary. */
+typedef enum {
+  FP8_DT_F32 = 0,
+  FP8_DT_F16 = 1,
+  FP8_DT_BF16 = 2,
+  FP8_DT_E4M3 = 3,
+  FP8_DT_E5M2 = 4
+} fp8_dtype_t;
+
+/*
+ * An operand that is either high precision (F32/F16/BF16: the call
+ * quantizes it) or already quantized (E4M3/E5M2 matching the call's format:
+ * the call skips its quantize, [P3] entry on g/x/w arriving bf16 or
+ * pre-quantized).  scale: device float, the QUANTIZATION multiplier s of a
+ * pre-quantized operand (q ~ x * s; the GEMM multiplies by 1/s); required
+ * iff dtype is fp8, ignored otherwise.
+ */
+typedef struct {
+  const void* data;
+  int32_t dtype;
+  const float* scale;
+} fp8_operand_t;
+
+/*
+ * Delayed-scaling state of one operand ([P1] entries on finalizing scale
+ * rings in the quantize kernel and on one ring per operand; [P3] entry on
+ * the scale snapshot).  Host struct owned by the caller.
+ *   dev       device buffer of fp8_ring_bytes(hist_len) bytes, 256-byte
+ *             aligned: a 64-byte header {float scale; u32 amax_acc (float
+ *             bits); u32 counter; u32 idx; u32 hist_len; u32 seeded; ...}
+ *             followed by float hist[hist_len].
+ *   hist_len  H, 1..1024.
+ *   seeded    host mirror, 0 until the first quantize through the ring has
+ *             been enqueued.  That first quantize seeds the scale from its
+ *             own amax (two passes over the input); later ones run one pass
+ *             with the scale published by the previous step.
+ * Byte-copying dev plus seeded resumes the scale sequence exactly.  A ring
+ * must not be used by two calls that may run concurrently.
+ */
+typedef struct {
+  void* dev;
+  int32_t hist_len;
+  int32_t seeded;
+} fp8_ring_t;
+
+/* Library ABI version (FP8_ABI_VERSION). */
+int fp8_abi_version(void);
+
+/* Static description of a status code. */
+const char* fp8_status_str(int status);
+
+/* Bytes of a ring's device buffer: 64 + 4 * hist_len (0 if out of range). */
+size_t fp8_ring_bytes(int32_t hist_len);
+
+/*
+ * Bind dev to ring and enqueue its reset: scale = 1, hist = 0, idx = 0,
+ * counter = 0, amax_acc = 0; sets ring->hist_len and ring->seeded = 0.
+ * Errors: FP8_ERR_NULL (ring or dev NULL), FP8_ERR_RING (hist_len out of
+ * range, dev misaligned), FP8_ERR_HIP.
+ */
+int fp8_ring_init(fp8_ring_t* ring, void* dev, int32_t hist_len, hipStream_t stream);
+
+/*
+ * Per-tensor quantize ([P3] entries on the quantize primitive templated on
+ * bf16/fp16/fp32 input and on fp32-domain amax; [P1] entry on the ring
+ * finalize in the kernel's last block; [P4] entry on the atomic ticket).
+ *
+ *   x          device, n elements of in_dtype (F32, F16 or BF16).
+ *   n          element count, >= 0 (n = 0 folds amax = 0 into the ring).
+ *   fmt        FP8_E4M3 or FP8_E5M2.
+ *   q          device, n bytes out: q_i = enc_fmt(fl32(x_i * s_used)),
+ *              round-to-nearest-even, saturating to +-max; NaN -> 0x7F|sign.
+ *   ring       NULL: dynamic scaling, s_used = fmt_max / amax(x) (two
+ *              passes).  Otherwise delayed scaling: s_used = the ring's
+ *              current scale (seeded from amax(x) on the ring's first use);
+ *              the launch's last block folds amax(x) into hist[idx],
+ *              advances idx and publishes fmt_max / max(hist) as the next
+ *              scale (kept unchanged if that max is 0 or not finite).
+ *   scale_used device float out, required: the s the bytes were made with.
+ *   amax_out   device float out: max |x_i| over the input values.
+ *              Required when ring is NULL (it is also the accumulator),
+ *              optional otherwise.
+ */
+int fp8_quantize(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, uint8_t* q,
+                 fp8_ring_t* ring, float* scale_used, float* amax_out, hipStream_t stream);
+
+/*
+ * Forward of one FP8 linear layer ([P1] entries on optional ring arguments,
+ * pre-quantized w8 with amax_w = 0, and the bias fused into the epilogue
+ * with bias_scale; [P4] entry on the bias added in fp32 before the single
+ * bf16 rounding; [P3] entry on bf16 output).
+ *
+ *   x        [M,K]: F32/F16/BF16 (quantized here with ring_x into x8_out)
+ *            or fp8 of format fmt with its scale.
+ *   w        [N,K]: same choices, ring_w, w8_out.
+ *   bias     [N]: data NULL = no bias; BF16 values; or fp8 codes (E4M3 or
+ *            E5M2) with scale = bias_scale, contributing dec(b8)/bias_scale.
+ *   fmt      format of X8 and W8.
+ *   y        [M,N] bf16 out: RNE_bf16(sum_k x8 w8 / (sx sw) + bias), with
+ *            fp32 accumulation.
+ *   x8_out   [M,K] bytes out, required when x is high precision (keep it
+ *            with sx_used for the backward: [P3] entry on the forward's
+ *            scale reaching the backward).  w8_out likewise for w.
+ *   sx_used  device float out: the scale X8 was made with; required when x
+ *            is high precision, optional (copied from x.scale) otherwise.
+ *            sw_used likewise.
+ *   amax_x   device float out, max |x|; required when x is high precision
+ *            and ring_x is NULL (dynamic), else optional; 0 is written for a
+ *            pre-quantized operand.  amax_w likewise.
+ */
+int fp8_linear_fwd(int64_t M, int64_t N, int64_t K, fp8_operand_t x, fp8_operand_t w,
+                   fp8_operand_t bias, int32_t fmt, fp8_ring_t* ring_x, fp8_ring_t* ring_w,
+                   void* y, uint8_t* x8_out, uint8_t* w8_out, float* sx_used, float* sw_used,
+                   float* amax_x, float* amax_w, hipStream_t stream);
+
+/*
+ * Input gradient ([P3] entries on bf16 grad outputs and on the forward's
+ * scale reused by the backward; [P2] entry on the crosswise-B operand).
+ *
+ *   g        [M,N]: F32/F16/BF16 (quantized here with ring_g into g8_out in
+ *            format fmt_g) or fp8 of format fmt_g with its scale.
+ *   w8       [N,K] fp8 (E4M3 or E5M2) with its scale (sw_used of the
+ *            forward).
+ *   dx       [M,K] bf16 out: RNE_bf16(sum_n g8 w8 / (sg sw)).
+ *   g8_out, sg_used, amax_g: as x8_out / sx_used / amax_x of the forward.
+ */
+int fp8_linear_bwd_dx(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
+                      fp8_ring_t* ring_g, fp8_operand_t w8, void* dx, uint8_t* g8_out,
+                      float* sg_used, float* amax_g, hipStream_t stream);
+
+/*
+ * Bytes of the fp32 workspace fp8_linear_bwd_dw needs for db:
+ * 4 * N * ceil(M / 32).
+ */
+size_t fp8_db_workspace_bytes(int64_t M, int64_t N);
+
+/*
+ * Weight and bias gradients ([P4] entry on computing the bias column sum
+ * only when the bias needs a gradient; [P3] entry on a pre-quantized g being
+ * dequantized before that sum; [P1] entry on crosswise A and B operands).
+ *
+ *   g        [M,N] as in fp8_linear_bwd_dx.
+ *   x8       [M,K] fp8 (E4M3 or E5M2) with its scale (sx_used of the
+ *            forward).
+ *   dw       [N,K] bf16 out: RNE_bf16(sum_m g8 x8 / (sg sx)).
+ *   db       [N] bf16 out or NULL.  When g is high precision, db sums the
+ *            g values as given; when g is pre-quantized, it sums
+ *            dec(g8)/sg.  fp32 accumulation, one bf16 rounding.
+ *   db_ws    device fp32 workspace of fp8_db_workspace_bytes(M, N) bytes,
+ *            required iff db is not NULL and M > 0; contents on entry are
+ *            ignored.
+ *   g8_out, sg_used, amax_g: as in fp8_linear_bwd_dx.
+ *
+ * Calling order within one backward: call fp8_linear_bwd_dw with the
+ * high-precision g first (one quantize, one ring fold, db from g itself),
+ * then fp8_linear_bwd_dx with g = {g8_out, fp8 dtype, sg_used}.
+ */
+int fp8_linear_bwd_dw(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
+                      fp8_ring_t* ring_g, fp8_operand_t x8, void* dw, void* db, float* db_ws,
+                      uint8_t* g8_out, float* sg_used, float* amax_g, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8LINEAR_H */

@@ -120,7 +120,8 @@ def encode(p, fmt: int) -> np.ndarray:
     """
     p = np.asarray(p, dtype=np.float32)
     vals, codes = _positive_finite(fmt)
-    a = np.abs(p.astype(np.float64))
+    with np.errstate(invalid="ignore"):
+        a = np.abs(p.astype(np.float64))
     neg = np.signbit(p).astype(np.int64)
     i = np.searchsorted(vals, a, side="right") - 1
     i = np.clip(i, 0, len(vals) - 2)

@@ -1,0 +1,197 @@
+"""Python binding of libfp8linear.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls and maps
+torch tensors (device memory) to the pointers and sizes of the C ABI
+declared in include/fp8linear.h.  No step of the computation runs in
+Python; without the built library every call raises.
+
+Conventions: fmt / dtype values are the C enums below; pre-quantized
+operands are passed as ``Quantized(codes_uint8, fmt, scale_f32)``; rings are
+``ScaleRing`` objects that own their device buffer and the C struct.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from ._build import LIB_PATH
+
+FP8_E4M3, FP8_E5M2 = 0, 1
+FP8_DT_F32, FP8_DT_F16, FP8_DT_BF16, FP8_DT_E4M3, FP8_DT_E5M2 = 0, 1, 2, 3, 4
+FP8_OK, FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_DTYPE, FP8_ERR_RING, FP8_ERR_HIP = range(6)
+
+_TORCH_DT = {torch.float32: FP8_DT_F32, torch.float16: FP8_DT_F16, torch.bfloat16: FP8_DT_BF16}
+_FMT_DT = {FP8_E4M3: FP8_DT_E4M3, FP8_E5M2: FP8_DT_E5M2}
+
+C_SYMBOLS = (
+    "fp8_abi_version", "fp8_status_str", "fp8_ring_bytes", "fp8_ring_init", "fp8_quantize",
+    "fp8_linear_fwd", "fp8_linear_bwd_dx", "fp8_db_workspace_bytes", "fp8_linear_bwd_dw",
+)
+
+
+class Fp8Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+class _Operand(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("scale", ctypes.c_void_p)]
+
+
+class _Ring(ctypes.Structure):
+    _fields_ = [("dev", ctypes.c_void_p), ("hist_len", ctypes.c_int32), ("seeded", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        op, rp = _Operand, ctypes.POINTER(_Ring)
+        L.fp8_abi_version.restype = ctypes.c_int
+        L.fp8_status_str.restype = ctypes.c_char_p
+        L.fp8_status_str.argtypes = [ctypes.c_int]
+        L.fp8_ring_bytes.restype = sz
+        L.fp8_ring_bytes.argtypes = [i32]
+        L.fp8_db_workspace_bytes.restype = sz
+        L.fp8_db_workspace_bytes.argtypes = [i64, i64]
+        L.fp8_ring_init.argtypes = [rp, vp, i32, vp]
+        L.fp8_quantize.argtypes = [vp, i32, i64, i32, vp, rp, vp, vp, vp]
+        L.fp8_linear_fwd.argtypes = [i64, i64, i64, op, op, op, i32, rp, rp, vp, vp, vp, vp, vp, vp,
+                                     vp, vp]
+        L.fp8_linear_bwd_dx.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp]
+        L.fp8_linear_bwd_dw.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp, vp, vp]
+        for name in ("fp8_ring_init", "fp8_quantize", "fp8_linear_fwd", "fp8_linear_bwd_dx",
+                     "fp8_linear_bwd_dw"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().fp8_status_str(status).decode()
+
+
+def fp8_abi_version() -> int:
+    return lib().fp8_abi_version()
+
+
+def fp8_ring_bytes(hist_len: int) -> int:
+    return lib().fp8_ring_bytes(hist_len)
+
+
+def fp8_db_workspace_bytes(M: int, N: int) -> int:
+    return lib().fp8_db_workspace_bytes(M, N)
+
+
+# ---------------------------------------------------------------- marshalling
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != FP8_OK:
+        raise Fp8Error(status, where)
+
+
+@dataclass
+class Quantized:
+    """Pre-quantized operand: uint8 codes, format, device float32 scale [1]."""
+    codes: torch.Tensor
+    fmt: int
+    scale: torch.Tensor
+
+
+def _operand(t) -> _Operand:
+    if t is None:
+        return _Operand(None, FP8_DT_BF16, None)
+    if isinstance(t, Quantized):
+        return _Operand(_ptr(t.codes), _FMT_DT[t.fmt], _ptr(t.scale))
+    return _Operand(_ptr(t), _TORCH_DT[t.dtype], None)
+
+
+class ScaleRing:
+    """Delayed-scaling ring: device buffer plus the C struct (seeded mirror)."""
+
+    def __init__(self, hist_len: int, device="cuda", stream=None):
+        nbytes = fp8_ring_bytes(hist_len)
+        if nbytes == 0:
+            raise Fp8Error(FP8_ERR_RING, "ScaleRing")
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.c = _Ring()
+        _check(lib().fp8_ring_init(ctypes.byref(self.c), self.buf.data_ptr(), hist_len,
+                                   _stream(stream)), "fp8_ring_init")
+
+    @property
+    def seeded(self) -> bool:
+        return bool(self.c.seeded)
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _ring(r):
+    return None if r is None else r.ref()
+
+
+# ---------------------------------------------------------------- entry points
+
+def fp8_quantize(x, fmt, q, ring=None, scale_used=None, amax_out=None, stream=None):
+    st = lib().fp8_quantize(_ptr(x), _TORCH_DT[x.dtype], x.numel(), fmt, _ptr(q), _ring(ring),
+                            _ptr(scale_used), _ptr(amax_out), _stream(stream))
+    _check(st, "fp8_quantize")
+
+
+def fp8_linear_fwd(x, w, bias, fmt, y, ring_x=None, ring_w=None, x8_out=None, w8_out=None,
+                   sx_used=None, sw_used=None, amax_x=None, amax_w=None, stream=None):
+    """x: [M,K] tensor or Quantized; w: [N,K] tensor or Quantized; bias: None,
+    a bf16 [N] tensor or Quantized (fp8 codes with bias_scale)."""
+    xd = x.codes if isinstance(x, Quantized) else x
+    wd = w.codes if isinstance(w, Quantized) else w
+    M, K = xd.shape
+    N = wd.shape[0]
+    st = lib().fp8_linear_fwd(M, N, K, _operand(x), _operand(w), _operand(bias), fmt,
+                              _ring(ring_x), _ring(ring_w), _ptr(y), _ptr(x8_out), _ptr(w8_out),
+                              _ptr(sx_used), _ptr(sw_used), _ptr(amax_x), _ptr(amax_w),
+                              _stream(stream))
+    _check(st, "fp8_linear_fwd")
+
+
+def fp8_linear_bwd_dx(g, fmt_g, w8, dx, ring_g=None, g8_out=None, sg_used=None, amax_g=None,
+                      stream=None):
+    gd = g.codes if isinstance(g, Quantized) else g
+    M, N = gd.shape
+    K = w8.codes.shape[1]
+    st = lib().fp8_linear_bwd_dx(M, N, K, _operand(g), fmt_g, _ring(ring_g), _operand(w8),
+                                 _ptr(dx), _ptr(g8_out), _ptr(sg_used), _ptr(amax_g),
+                                 _stream(stream))
+    _check(st, "fp8_linear_bwd_dx")
+
+
+def fp8_linear_bwd_dw(g, fmt_g, x8, dw, db=None, db_ws=None, ring_g=None, g8_out=None,
+                      sg_used=None, amax_g=None, stream=None):
+    gd = g.codes if isinstance(g, Quantized) else g
+    M, N = gd.shape
+    K = x8.codes.shape[1]
+    st = lib().fp8_linear_bwd_dw(M, N, K, _operand(g), fmt_g, _ring(ring_g), _operand(x8),
+                                 _ptr(dw), _ptr(db), _ptr(db_ws), _ptr(g8_out), _ptr(sg_used),
+                                 _ptr(amax_g), _stream(stream))
+    _check(st, "fp8_linear_bwd_dw")

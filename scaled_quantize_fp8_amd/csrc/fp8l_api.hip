@@ -1,0 +1,438 @@
+// C ABI of libfp8linear.so: argument validation, then launches on the
+// caller's stream.  No allocation, no synchronization.
+//
+// The four entry points follow the two-primitive API of [P3] (quantize, and
+// a GEMM that consumes quantized operands and their scales) with the
+// optional per-operand rings of [P1] and the pre-quantized operands of
+// [P1]/[P3].  Every check below runs before the first launch, so an error
+// status means nothing was enqueued.
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/fp8linear.h"
+#include "fp8l_device.hpp"
+#include "fp8l_gemm.hpp"
+#include "fp8l_quantize.hpp"
+
+namespace fp8l {
+namespace {
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool is_hp(int32_t dt) { return dt == FP8_DT_F32 || dt == FP8_DT_F16 || dt == FP8_DT_BF16; }
+bool is_f8(int32_t dt) { return dt == FP8_DT_E4M3 || dt == FP8_DT_E5M2; }
+bool valid_fmt(int32_t f) { return f == FP8_E4M3 || f == FP8_E5M2; }
+int32_t fmt_dtype(int32_t f) { return f == FP8_E4M3 ? FP8_DT_E4M3 : FP8_DT_E5M2; }
+int dtype_fmt(int32_t dt) { return dt == FP8_DT_E4M3 ? kE4M3 : kE5M2; }
+
+// a * b fits in int64 (a, b >= 0)
+bool mul_ok(int64_t a, int64_t b) { return a == 0 || b <= INT64_MAX / 4 / a; }
+
+int check_ring(const fp8_ring_t* r) {
+  if (!r) return FP8_OK;
+  if (!r->dev) return FP8_ERR_NULL;
+  if (r->hist_len < 1 || r->hist_len > FP8_RING_MAX_HIST) return FP8_ERR_RING;
+  if (((uintptr_t)r->dev & 255u) != 0) return FP8_ERR_RING;
+  return FP8_OK;
+}
+
+// a scale output must not be the ring's own scale slot
+int check_alias(const fp8_ring_t* r, const float* scale_out) {
+  if (r && scale_out && (const void*)scale_out >= r->dev &&
+      (const char*)scale_out < (const char*)r->dev + sizeof(RingHdr))
+    return FP8_ERR_RING;
+  return FP8_OK;
+}
+
+// Checks for one quantize (shared by the four entry points).
+int check_quant(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, const uint8_t* q,
+                const fp8_ring_t* ring, const float* scale_used, const float* amax_out) {
+  if (n < 0) return FP8_ERR_SHAPE;
+  if (!is_hp(in_dtype) || !valid_fmt(fmt)) return FP8_ERR_DTYPE;
+  if (n > 0 && (!x || !q)) return FP8_ERR_NULL;
+  if (!scale_used) return FP8_ERR_NULL;
+  if (!ring && !amax_out) return FP8_ERR_NULL;
+  int st = check_ring(ring);
+  if (st) return st;
+  return check_alias(ring, scale_used);
+}
+
+struct ColsumSpec {
+  int64_t rows, cols;
+  float* ws;
+};
+
+template <int IN, int FMT, int SMODE>
+void launch_convert(const QArgs& a, const ColsumSpec* cs, hipStream_t st) {
+  if (cs && cs->rows > 0 && cs->cols > 0) {
+    dim3 grid((unsigned)((cs->cols + kColStrip - 1) / kColStrip),
+              (unsigned)((cs->rows + kColRowsPerChunk - 1) / kColRowsPerChunk));
+    hipLaunchKernelGGL((quantize_colsum_kernel<IN, FMT, SMODE>), grid, dim3(kQThreads), 0, st, a);
+  } else {
+    const int64_t nch = (a.n + kQVec - 1) / kQVec;
+    int64_t blocks = (nch + kQThreads - 1) / kQThreads;
+    const int64_t cap = (int64_t)cu_count() * 8;
+    blocks = blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
+    hipLaunchKernelGGL((quantize_flat_kernel<IN, FMT, SMODE>), dim3((unsigned)blocks),
+                       dim3(kQThreads), 0, st, a);
+  }
+}
+
+template <int IN>
+void launch_amax(const void* x, int64_t n, int vec_ok, uint32_t* target, hipStream_t st) {
+  const int64_t nch = (n + kQVec - 1) / kQVec;
+  int64_t blocks = (nch + kQThreads - 1) / kQThreads;
+  const int64_t cap = (int64_t)cu_count() * 8;
+  blocks = blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
+  hipLaunchKernelGGL((amax_kernel<IN>), dim3((unsigned)blocks), dim3(kQThreads), 0, st, x, n,
+                     vec_ok, target);
+}
+
+template <int IN, int FMT>
+void enqueue_quant_t(const void* x, int64_t n, uint8_t* q, fp8_ring_t* ring, float* scale_used,
+                     float* amax_out, const ColsumSpec* cs, hipStream_t st) {
+  QArgs a = {};
+  a.x = x;
+  a.q = q;
+  a.n = n;
+  a.scale_used = scale_used;
+  a.amax_out = amax_out;
+  a.vec_ok = aligned16(x) && aligned16(q);
+  if (cs) {
+    a.rows = cs->rows;
+    a.cols = cs->cols;
+    a.colsum = cs->ws;
+    a.vec_ok = a.vec_ok && (cs->cols % 16 == 0);
+  }
+  if (ring) {
+    a.ring = reinterpret_cast<RingHdr*>(ring->dev);
+    a.hist = reinterpret_cast<float*>(reinterpret_cast<char*>(ring->dev) + sizeof(RingHdr));
+    a.hist_len = ring->hist_len;
+    if (ring->seeded) {
+      launch_convert<IN, FMT, kScaleRing>(a, cs, st);
+    } else {
+      // first use: measure amax into the ring's accumulator (0 between
+      // launches), seed the scale from it, then convert and fold.
+      launch_amax<IN>(x, n, aligned16(x), &a.ring->amax_acc, st);
+      launch_convert<IN, FMT, kScaleSeed>(a, cs, st);
+      ring->seeded = 1;
+    }
+  } else {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, reinterpret_cast<uint32_t*>(amax_out));
+    launch_amax<IN>(x, n, aligned16(x), reinterpret_cast<uint32_t*>(amax_out), st);
+    launch_convert<IN, FMT, kScaleDyn>(a, cs, st);
+  }
+}
+
+template <int IN>
+void enqueue_quant_in(const void* x, int64_t n, int32_t fmt, uint8_t* q, fp8_ring_t* ring,
+                      float* scale_used, float* amax_out, const ColsumSpec* cs, hipStream_t st) {
+  if (fmt == FP8_E4M3)
+    enqueue_quant_t<IN, kE4M3>(x, n, q, ring, scale_used, amax_out, cs, st);
+  else
+    enqueue_quant_t<IN, kE5M2>(x, n, q, ring, scale_used, amax_out, cs, st);
+}
+
+void enqueue_quant(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, uint8_t* q,
+                   fp8_ring_t* ring, float* scale_used, float* amax_out, const ColsumSpec* cs,
+                   hipStream_t st) {
+  if (in_dtype == FP8_DT_F32)
+    enqueue_quant_in<kInF32>(x, n, fmt, q, ring, scale_used, amax_out, cs, st);
+  else if (in_dtype == FP8_DT_F16)
+    enqueue_quant_in<kInF16>(x, n, fmt, q, ring, scale_used, amax_out, cs, st);
+  else
+    enqueue_quant_in<kInBF16>(x, n, fmt, q, ring, scale_used, amax_out, cs, st);
+}
+
+template <int LA, int LB, int FA, int FB>
+void launch_gemm_t(GemmArgs& g, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_kernel<LA, LB, FA, FB>), dim3((unsigned)(g.tiles_m * g.tiles_n)),
+                     dim3(kGThreads), 0, st, g);
+}
+
+template <int LA, int LB>
+void launch_gemm_l(GemmArgs& g, int fa, int fb, hipStream_t st) {
+  if (fa == kE4M3 && fb == kE4M3) launch_gemm_t<LA, LB, kE4M3, kE4M3>(g, st);
+  else if (fa == kE4M3 && fb == kE5M2) launch_gemm_t<LA, LB, kE4M3, kE5M2>(g, st);
+  else if (fa == kE5M2 && fb == kE4M3) launch_gemm_t<LA, LB, kE5M2, kE4M3>(g, st);
+  else launch_gemm_t<LA, LB, kE5M2, kE5M2>(g, st);
+}
+
+void finish_gemm_args(GemmArgs& g) {
+  const int64_t tm = (g.Mc + kBM - 1) / kBM, tn = (g.Nc + kBN - 1) / kBN;
+  g.tiles_m = (int32_t)(tm < 1 ? 1 : tm);
+  g.tiles_n = (int32_t)(tn < 1 ? 1 : tn);
+  g.a_vec = aligned16(g.a) && g.lda % 16 == 0;
+  g.b_vec = aligned16(g.b) && g.ldb % 16 == 0;
+  g.c_vec = ((uintptr_t)g.c & 7u) == 0 && g.ldc % 4 == 0;
+}
+
+int hip_status() { return hipGetLastError() == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
+
+}  // namespace
+}  // namespace fp8l
+
+using namespace fp8l;
+
+extern "C" {
+
+int fp8_abi_version(void) { return FP8_ABI_VERSION; }
+
+const char* fp8_status_str(int status) {
+  switch (status) {
+    case FP8_OK: return "ok";
+    case FP8_ERR_NULL: return "a required pointer is NULL";
+    case FP8_ERR_SHAPE: return "invalid size (negative or overflowing)";
+    case FP8_ERR_DTYPE: return "invalid or mismatched dtype/format";
+    case FP8_ERR_RING: return "invalid scale ring (hist_len, alignment or aliasing)";
+    case FP8_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+size_t fp8_ring_bytes(int32_t hist_len) {
+  if (hist_len < 1 || hist_len > FP8_RING_MAX_HIST) return 0;
+  return sizeof(RingHdr) + 4u * (size_t)hist_len;
+}
+
+size_t fp8_db_workspace_bytes(int64_t M, int64_t N) {
+  if (M < 0 || N < 0) return 0;
+  const int64_t R = (M + kColRowsPerChunk - 1) / kColRowsPerChunk;
+  return (size_t)(4 * R * N);
+}
+
+int fp8_ring_init(fp8_ring_t* ring, void* dev, int32_t hist_len, hipStream_t stream) {
+  if (!ring || !dev) return FP8_ERR_NULL;
+  if (hist_len < 1 || hist_len > FP8_RING_MAX_HIST || ((uintptr_t)dev & 255u)) return FP8_ERR_RING;
+  hipLaunchKernelGGL(ring_init_kernel, dim3(1), dim3(256), 0, stream, reinterpret_cast<RingHdr*>(dev),
+                     reinterpret_cast<float*>(reinterpret_cast<char*>(dev) + sizeof(RingHdr)),
+                     (int)hist_len);
+  const int st = hip_status();
+  if (st) return st;
+  ring->dev = dev;
+  ring->hist_len = hist_len;
+  ring->seeded = 0;
+  return FP8_OK;
+}
+
+int fp8_quantize(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, uint8_t* q,
+                 fp8_ring_t* ring, float* scale_used, float* amax_out, hipStream_t stream) {
+  int st = check_quant(x, in_dtype, n, fmt, q, ring, scale_used, amax_out);
+  if (st) return st;
+  if (!mul_ok(n, 4)) return FP8_ERR_SHAPE;
+  enqueue_quant(x, in_dtype, n, fmt, q, ring, scale_used, amax_out, nullptr, stream);
+  return hip_status();
+}
+
+int fp8_linear_fwd(int64_t M, int64_t N, int64_t K, fp8_operand_t x, fp8_operand_t w,
+                   fp8_operand_t bias, int32_t fmt, fp8_ring_t* ring_x, fp8_ring_t* ring_w,
+                   void* y, uint8_t* x8_out, uint8_t* w8_out, float* sx_used, float* sw_used,
+                   float* amax_x, float* amax_w, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return FP8_ERR_SHAPE;
+  if (!mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return FP8_ERR_SHAPE;
+  if (!valid_fmt(fmt)) return FP8_ERR_DTYPE;
+  const int32_t f8dt = fmt_dtype(fmt);
+  int st;
+  // X
+  if (is_hp(x.dtype)) {
+    st = check_quant(x.data, x.dtype, M * K, fmt, x8_out, ring_x, sx_used, amax_x);
+    if (st) return st;
+  } else if (x.dtype == f8dt) {
+    if ((M * K > 0 && !x.data) || !x.scale) return FP8_ERR_NULL;
+  } else {
+    return FP8_ERR_DTYPE;
+  }
+  // W
+  if (is_hp(w.dtype)) {
+    st = check_quant(w.data, w.dtype, N * K, fmt, w8_out, ring_w, sw_used, amax_w);
+    if (st) return st;
+  } else if (w.dtype == f8dt) {
+    if ((N * K > 0 && !w.data) || !w.scale) return FP8_ERR_NULL;
+  } else {
+    return FP8_ERR_DTYPE;
+  }
+  if (ring_x && ring_x == ring_w) return FP8_ERR_RING;
+  // bias
+  int bias_kind = kBiasNone;
+  if (bias.data) {
+    if (bias.dtype == FP8_DT_BF16) bias_kind = kBiasBF16;
+    else if (bias.dtype == FP8_DT_E4M3) bias_kind = kBiasE4M3;
+    else if (bias.dtype == FP8_DT_E5M2) bias_kind = kBiasE5M2;
+    else return FP8_ERR_DTYPE;
+    if (bias_kind != kBiasBF16 && !bias.scale) return FP8_ERR_NULL;
+  }
+  if (M * N > 0 && !y) return FP8_ERR_NULL;
+
+  GemmArgs g = {};
+  if (is_hp(x.dtype)) {
+    enqueue_quant(x.data, x.dtype, M * K, fmt, x8_out, ring_x, sx_used, amax_x, nullptr, stream);
+    g.a = x8_out;
+    g.scale_a = sx_used;
+  } else {
+    g.a = reinterpret_cast<const uint8_t*>(x.data);
+    g.scale_a = x.scale;
+    g.aux_scale_dst0 = sx_used;
+    g.aux_scale_src0 = x.scale;
+    g.aux_amax_dst0 = amax_x;
+  }
+  if (is_hp(w.dtype)) {
+    enqueue_quant(w.data, w.dtype, N * K, fmt, w8_out, ring_w, sw_used, amax_w, nullptr, stream);
+    g.b = w8_out;
+    g.scale_b = sw_used;
+  } else {
+    g.b = reinterpret_cast<const uint8_t*>(w.data);
+    g.scale_b = w.scale;
+    g.aux_scale_dst1 = sw_used;
+    g.aux_scale_src1 = w.scale;
+    g.aux_amax_dst1 = amax_w;
+  }
+  g.lda = K;
+  g.ldb = K;
+  g.Mc = M;
+  g.Nc = N;
+  g.Kc = K;
+  g.c = reinterpret_cast<uint16_t*>(y);
+  g.ldc = N;
+  g.bias = bias.data;
+  g.bias_kind = bias_kind;
+  g.bias_scale = bias.scale;
+  finish_gemm_args(g);
+  launch_gemm_l<kKContig, kKContig>(g, fmt, fmt, stream);
+  return hip_status();
+}
+
+// Shared front half of the two backward entry points: validate g and
+// enqueue its quantize if it is high precision.  Outputs the fp8 pointer
+// and scale pointer the GEMM uses.
+static int bwd_prepare(int64_t M, int64_t N, fp8_operand_t g, int32_t fmt_g, fp8_ring_t* ring_g,
+                       uint8_t* g8_out, float* sg_used, float* amax_g, bool validate_only,
+                       const ColsumSpec* cs, hipStream_t stream, const uint8_t** g8,
+                       const float** sg, bool* pre) {
+  if (!valid_fmt(fmt_g)) return FP8_ERR_DTYPE;
+  if (is_hp(g.dtype)) {
+    if (validate_only)
+      return check_quant(g.data, g.dtype, M * N, fmt_g, g8_out, ring_g, sg_used, amax_g);
+    enqueue_quant(g.data, g.dtype, M * N, fmt_g, g8_out, ring_g, sg_used, amax_g, cs, stream);
+    *g8 = g8_out;
+    *sg = sg_used;
+    *pre = false;
+  } else if (g.dtype == fmt_dtype(fmt_g)) {
+    if (validate_only) return ((M * N > 0 && !g.data) || !g.scale) ? FP8_ERR_NULL : FP8_OK;
+    *g8 = reinterpret_cast<const uint8_t*>(g.data);
+    *sg = g.scale;
+    *pre = true;
+  } else {
+    return FP8_ERR_DTYPE;
+  }
+  return FP8_OK;
+}
+
+int fp8_linear_bwd_dx(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
+                      fp8_ring_t* ring_g, fp8_operand_t w8, void* dx, uint8_t* g8_out,
+                      float* sg_used, float* amax_g, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return FP8_ERR_SHAPE;
+  if (!mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return FP8_ERR_SHAPE;
+  const uint8_t* g8 = nullptr;
+  const float* sg = nullptr;
+  bool pre = false;
+  int st = bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, true, nullptr, stream, &g8,
+                       &sg, &pre);
+  if (st) return st;
+  if (!is_f8(w8.dtype)) return FP8_ERR_DTYPE;
+  if ((N * K > 0 && !w8.data) || !w8.scale) return FP8_ERR_NULL;
+  if (M * K > 0 && !dx) return FP8_ERR_NULL;
+  bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, nullptr, stream, &g8, &sg, &pre);
+
+  GemmArgs a = {};
+  a.a = g8;  // [M, N], contraction n contiguous
+  a.lda = N;
+  a.b = reinterpret_cast<const uint8_t*>(w8.data);  // [N, K] read crosswise
+  a.ldb = K;
+  a.Mc = M;
+  a.Nc = K;
+  a.Kc = N;
+  a.c = reinterpret_cast<uint16_t*>(dx);
+  a.ldc = K;
+  a.scale_a = sg;
+  a.scale_b = w8.scale;
+  if (pre) {
+    a.aux_scale_dst0 = sg_used;
+    a.aux_scale_src0 = g.scale;
+    a.aux_amax_dst0 = amax_g;
+  }
+  finish_gemm_args(a);
+  launch_gemm_l<kKContig, kCross>(a, fmt_g, dtype_fmt(w8.dtype), stream);
+  return hip_status();
+}
+
+int fp8_linear_bwd_dw(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
+                      fp8_ring_t* ring_g, fp8_operand_t x8, void* dw, void* db, float* db_ws,
+                      uint8_t* g8_out, float* sg_used, float* amax_g, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return FP8_ERR_SHAPE;
+  if (!mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return FP8_ERR_SHAPE;
+  const uint8_t* g8 = nullptr;
+  const float* sg = nullptr;
+  bool pre = false;
+  int st = bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, true, nullptr, stream, &g8,
+                       &sg, &pre);
+  if (st) return st;
+  if (!is_f8(x8.dtype)) return FP8_ERR_DTYPE;
+  if ((M * K > 0 && !x8.data) || !x8.scale) return FP8_ERR_NULL;
+  if (N * K > 0 && !dw) return FP8_ERR_NULL;
+  if (db && M > 0 && !db_ws) return FP8_ERR_NULL;
+
+  ColsumSpec cs = {M, N, db_ws};
+  const bool want_db = db != nullptr && M > 0;
+  bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, want_db ? &cs : nullptr,
+              stream, &g8, &sg, &pre);
+  if (want_db && pre && N > 0) {
+    dim3 grid((unsigned)((N + kColStrip - 1) / kColStrip),
+              (unsigned)((M + kColRowsPerChunk - 1) / kColRowsPerChunk));
+    if (fmt_g == FP8_E4M3)
+      hipLaunchKernelGGL(colsum_fp8_kernel<kE4M3>, grid, dim3(kQThreads), 0, stream, g8, M, N, db_ws);
+    else
+      hipLaunchKernelGGL(colsum_fp8_kernel<kE5M2>, grid, dim3(kQThreads), 0, stream, g8, M, N, db_ws);
+  }
+
+  GemmArgs a = {};
+  a.a = g8;  // G8 [M, N] as A(i = n, k = m): crosswise
+  a.lda = N;
+  a.b = reinterpret_cast<const uint8_t*>(x8.data);  // X8 [M, K] as B(j = k, k = m): crosswise
+  a.ldb = K;
+  a.Mc = N;
+  a.Nc = K;
+  a.Kc = M;
+  a.c = reinterpret_cast<uint16_t*>(dw);
+  a.ldc = K;
+  a.scale_a = sg;
+  a.scale_b = x8.scale;
+  if (db) {
+    a.db = reinterpret_cast<uint16_t*>(db);
+    a.db_ws = db_ws;
+    a.db_R = (int32_t)((M + kColRowsPerChunk - 1) / kColRowsPerChunk);
+    a.db_scale = pre ? sg : nullptr;
+  }
+  if (pre) {
+    a.aux_scale_dst0 = sg_used;
+    a.aux_scale_src0 = g.scale;
+    a.aux_amax_dst0 = amax_g;
+  }
+  finish_gemm_args(a);
+  launch_gemm_l<kCross, kCross>(a, fmt_g, dtype_fmt(x8.dtype), stream);
+  return hip_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// Device helpers shared by the quantize and GEMM kernels (gfx950 / CDNA4).
+//
+// Sources cited in this library (AstrAI commit-log pages):
+//   [P1] commit 2eeac02d, page tests/extension
+//   [P2] commit 2eeac02d, page csrc
+//   [P3] commit 057c0d33, page astrai/extension/ops
+//   [P4] commit 4019ddac, page astrai
+//   [OCP] OCP 8-bit Floating Point Specification (OFP8) rev 1.0
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8l {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+#define FP8L_DEV __device__ __forceinline__
+
+enum { kE4M3 = 0, kE5M2 = 1 };
+enum { kInF32 = 0, kInF16 = 1, kInBF16 = 2 };
+
+// Largest finite magnitude of each OCP format [OCP]: E4M3 S.1111.110 = 448,
+// E5M2 S.11110.11 = 57344.
+template <int FMT>
+struct FmtTraits;
+template <>
+struct FmtTraits<kE4M3> {
+  static constexpr float kMax = 448.0f;
+};
+template <>
+struct FmtTraits<kE5M2> {
+  static constexpr float kMax = 57344.0f;
+};
+
+// Ring header in device memory (64 bytes, then float hist[H]).
+struct RingHdr {
+  float scale;        // scale the next quantize uses
+  uint32_t amax_acc;  // running max of |x| bits during a launch; 0 between launches
+  uint32_t counter;   // last-block ticket; 0 between launches
+  uint32_t idx;       // next hist slot
+  uint32_t hist_len;
+  uint32_t seeded;
+  uint32_t reserved[10];
+};
+static_assert(sizeof(RingHdr) == 64, "ring header is 64 bytes");
+
+// ---------------------------------------------------------------- scale
+
+// S(m) = fmt_max / m, IEEE fp32 division (correctly rounded: the library is
+// built without fast-math), or prev when m is 0, NaN, inf or the quotient
+// overflows.  The plainest reading of "scale = fmt_max / amax" with a zero
+// margin.
+FP8L_DEV float scale_from_amax(float m, float fmt_max, float prev) {
+  if (m > 0.0f && m <= 3.402823466e38f) {
+    float r = fmt_max / m;
+    if (r <= 3.402823466e38f) return r;
+  }
+  return prev;
+}
+
+// ---------------------------------------------------------------- conversion
+
+// Four fp32 values -> four codes (byte i = value i).  The hardware
+// conversion rounds to nearest even with OCP encodings; it turns overflow
+// into NaN / inf, so values are first clamped to +-max with v_med3_f32
+// (saturation; inf clamps too).  NaN inputs are fixed up by the caller.
+template <int FMT>
+FP8L_DEV uint32_t cvt4(float a, float b, float c, float d) {
+  constexpr float M = FmtTraits<FMT>::kMax;
+  a = __builtin_amdgcn_fmed3f(a, -M, M);
+  b = __builtin_amdgcn_fmed3f(b, -M, M);
+  c = __builtin_amdgcn_fmed3f(c, -M, M);
+  d = __builtin_amdgcn_fmed3f(d, -M, M);
+  int w;
+  if constexpr (FMT == kE4M3) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  }
+  return (uint32_t)w;
+}
+
+// Byte SEL of a packed word, decoded to fp32 (exact).
+template <int FMT, int SEL = 0>
+FP8L_DEV float fp8_to_f32(uint32_t word) {
+  if constexpr (FMT == kE4M3)
+    return __builtin_amdgcn_cvt_f32_fp8((int)word, SEL);
+  else
+    return __builtin_amdgcn_cvt_f32_bf8((int)word, SEL);
+}
+
+FP8L_DEV float fp8_to_f32_rt(uint32_t code, int fmt) {
+  return fmt == kE4M3 ? __builtin_amdgcn_cvt_f32_fp8((int)code, 0)
+                      : __builtin_amdgcn_cvt_f32_bf8((int)code, 0);
+}
+
+FP8L_DEV float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> quiet NaN.
+FP8L_DEV uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---------------------------------------------------------------- reductions
+
+// Max of non-negative float bit patterns across a wave of 64 lanes: DPP row
+// shuffles within each row of 16 lanes, then readlane across the 4 rows.
+// Unsigned order of non-negative floats is their numeric order (NaN above
+// inf), so the max propagates NaN.
+FP8L_DEV uint32_t wave_max_u32(uint32_t v) {
+  // quad_perm [1,0,3,2] and [2,3,0,1]: xor 1, xor 2 inside each quad
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+  // row_ror:4 and row_ror:8 combine the four quads of a row
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));
+  uint32_t r0 = __builtin_amdgcn_readlane(v, 0);
+  uint32_t r1 = __builtin_amdgcn_readlane(v, 16);
+  uint32_t r2 = __builtin_amdgcn_readlane(v, 32);
+  uint32_t r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+FP8L_DEV uint32_t atomic_load_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace fp8l

@@ -1,0 +1,87 @@
+"""Helpers shared by the GPU parity tests: device/host moves, ring read-back
+and the two GEMM acceptance bounds."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import fp8_oracle as O
+
+DEV = "cuda"
+FMT_NAME = {O.E4M3: "e4m3", O.E5M2: "e5m2"}
+
+# The acceptance contract (rel = 2^-7 of sum|a*b|, plus one bf16 ulp) and a
+# diagnostic bound 2^-10 that the gfx950 fp8 MFMA meets with margin (its
+# internal sum of 128 products keeps about 12-13 bits relative to
+# sum|a*b|), tight enough that a dropped or misplaced K block fails.
+CONTRACT_REL = 2.0 ** -7
+TIGHT_REL = 2.0 ** -10
+
+
+def to_dev(a, dtype=None) -> torch.Tensor:
+    if isinstance(a, torch.Tensor):
+        return a.to(DEV)
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(DEV) if dtype is None else t.to(dtype).to(DEV)
+
+
+def scalar_dev(v) -> torch.Tensor:
+    return torch.tensor([float(np.float32(v))], dtype=torch.float32, device=DEV)
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    """Input tensor values as fp32 numpy (exact for bf16/f16/f32)."""
+    return t.detach().to("cpu").to(torch.float32).numpy()
+
+
+def u8(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").numpy().view(np.uint8)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").view(torch.int16).numpy().view(np.uint16)
+
+
+def f32_scalar(t: torch.Tensor) -> np.float32:
+    return np.float32(t.detach().to("cpu").numpy().reshape(-1)[0])
+
+
+def ring_state(ring) -> dict:
+    """Read a device ring back: scale, idx, hist, amax_acc, counter, seeded."""
+    b = ring.buf.detach().to("cpu").numpy()
+    hdr = b[:64].view(np.uint32)
+    H = int(hdr[4])
+    return {
+        "scale": b[:4].view(np.float32)[0],
+        "amax_acc": int(hdr[1]),
+        "counter": int(hdr[2]),
+        "idx": int(hdr[3]),
+        "hist_len": H,
+        "seeded": int(hdr[5]),
+        "hist": b[64:64 + 4 * H].view(np.float32).copy(),
+    }
+
+
+def assert_ring_matches(ring, oring: O.ScaleRing):
+    st = ring_state(ring)
+    assert st["scale"].tobytes() == np.float32(oring.scale).tobytes(), (st["scale"], oring.scale)
+    assert st["idx"] == oring.idx
+    assert st["hist"].tobytes() == oring.hist.astype(np.float32).tobytes()
+    assert st["amax_acc"] == 0 and st["counter"] == 0
+    assert bool(st["seeded"]) == oring.seeded
+
+
+def check_gemm(y_bits: np.ndarray, ref: O.GemmRef, what: str = ""):
+    """Assert the contract bound and the diagnostic bound elementwise."""
+    y = O.bf16_value(y_bits)
+    err = np.abs(y - ref.r)
+    tol = O.gemm_tolerance(ref, CONTRACT_REL)
+    bad = err > tol
+    assert not bad.any(), f"{what}: {bad.sum()} elements outside the 2^-7 contract, max err {err.max()}"
+    tight = O.gemm_tolerance(ref, TIGHT_REL)
+    bad = err > tight
+    assert not bad.any(), (
+        f"{what}: {bad.sum()} elements outside the 2^-10 diagnostic bound; "
+        f"worst err/sum|ab| = {np.max((err - O.bf16_ulp(ref.r)) / np.maximum(ref.abs_sum, 1e-300))}")
+    return float(np.max((err - O.bf16_ulp(ref.r)).clip(0) / np.maximum(ref.abs_sum, 1e-300)))

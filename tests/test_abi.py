@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/fp8linear.h declares, and rejects bad arguments with
+the documented status before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import scaled_quantize_fp8_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(fp8_[a-z_0-9]+)\s*\(", text, re.M)
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(F.LIB_PATH):
+        pytest.fail("libfp8linear.so is not built: run __graft_entry__.build()")
+    return F.lib()
+
+
+def test_header_declares_the_four_entry_points():
+    names = set(_declared_functions())
+    for must in ("fp8_quantize", "fp8_linear_fwd", "fp8_linear_bwd_dx", "fp8_linear_bwd_dw"):
+        assert must in names
+    assert names == set(F.C_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert F.fp8_abi_version() == 1
+    for st in range(6):
+        assert F.status_str(st)
+    assert F.status_str(99) == "unknown status"
+
+
+def test_sizes(lib):
+    assert F.fp8_ring_bytes(16) == 64 + 64
+    assert F.fp8_ring_bytes(1024) == 64 + 4096
+    assert F.fp8_ring_bytes(0) == 0 and F.fp8_ring_bytes(1025) == 0
+    assert F.fp8_db_workspace_bytes(2048, 6912) == 4 * 64 * 6912
+    assert F.fp8_db_workspace_bytes(33, 10) == 4 * 2 * 10
+    assert F.fp8_db_workspace_bytes(0, 10) == 0
+
+
+P = ctypes.c_void_p(0x100000)  # a non-null "device" address never dereferenced
+
+
+def test_quantize_validation(lib):
+    q = lib.fp8_quantize
+    ring = F._Ring(None, 16, 0)
+    # NULL scale_used
+    assert q(P, F.FP8_DT_BF16, 16, F.FP8_E4M3, P, None, None, P, None) == F.FP8_ERR_NULL
+    # dynamic without amax_out
+    assert q(P, F.FP8_DT_BF16, 16, F.FP8_E4M3, P, None, P, None, None) == F.FP8_ERR_NULL
+    # bad format, bad dtype, negative size
+    assert q(P, F.FP8_DT_BF16, 16, 7, P, None, P, P, None) == F.FP8_ERR_DTYPE
+    assert q(P, F.FP8_DT_E4M3, 16, F.FP8_E4M3, P, None, P, P, None) == F.FP8_ERR_DTYPE
+    assert q(P, F.FP8_DT_BF16, -1, F.FP8_E4M3, P, None, P, P, None) == F.FP8_ERR_SHAPE
+    # ring with NULL dev, bad hist_len, misaligned dev
+    assert q(P, F.FP8_DT_BF16, 16, F.FP8_E4M3, P, ctypes.byref(ring), P, None, None) == F.FP8_ERR_NULL
+    ring = F._Ring(ctypes.c_void_p(0x100000), 0, 0)
+    assert q(P, F.FP8_DT_BF16, 16, F.FP8_E4M3, P, ctypes.byref(ring), P, None, None) == F.FP8_ERR_RING
+    ring = F._Ring(ctypes.c_void_p(0x100010), 16, 0)
+    assert q(P, F.FP8_DT_BF16, 16, F.FP8_E4M3, P, ctypes.byref(ring), P, None, None) == F.FP8_ERR_RING
+    # scale_used aliasing the ring's scale slot
+    ring = F._Ring(ctypes.c_void_p(0x100000), 16, 1)
+    assert q(P, F.FP8_DT_BF16, 16, F.FP8_E4M3, P, ctypes.byref(ring), P, None, None) == F.FP8_ERR_RING
+    assert ring.seeded == 1
+
+
+def test_linear_validation(lib):
+    hp = F._Operand(P, F.FP8_DT_BF16, None)
+    f8 = F._Operand(P, F.FP8_DT_E4M3, P)
+    f8_noscale = F._Operand(P, F.FP8_DT_E4M3, None)
+    f8_wrong = F._Operand(P, F.FP8_DT_E5M2, P)
+    none = F._Operand(None, F.FP8_DT_BF16, None)
+    fwd = lib.fp8_linear_fwd
+    args = lambda x, w, b=none, fmt=F.FP8_E4M3, y=P: (8, 8, 8, x, w, b, fmt, None, None, y, P, P, P, P,
+                                                       P, P, None)
+    assert fwd(*args(hp, f8_noscale)) == F.FP8_ERR_NULL
+    assert fwd(*args(hp, f8_wrong)) == F.FP8_ERR_DTYPE
+    assert fwd(*args(hp, f8, fmt=3)) == F.FP8_ERR_DTYPE
+    assert fwd(*args(hp, f8, b=F._Operand(P, F.FP8_DT_F32, None))) == F.FP8_ERR_DTYPE
+    assert fwd(*args(hp, f8, b=F._Operand(P, F.FP8_DT_E4M3, None))) == F.FP8_ERR_NULL
+    assert fwd(*args(hp, f8, y=None)) == F.FP8_ERR_NULL
+    assert fwd(-1, 8, 8, hp, f8, none, 0, None, None, P, P, P, P, P, P, P, None) == F.FP8_ERR_SHAPE
+    assert fwd(2**40, 2**40, 8, hp, f8, none, 0, None, None, P, P, P, P, P, P, P, None) == F.FP8_ERR_SHAPE
+    # x8_out missing for a high-precision x
+    assert fwd(8, 8, 8, hp, f8, none, 0, None, None, P, None, P, P, P, P, P, None) == F.FP8_ERR_NULL
+    dx = lib.fp8_linear_bwd_dx
+    assert dx(8, 8, 8, hp, F.FP8_E5M2, None, hp, P, P, P, P, None) == F.FP8_ERR_DTYPE
+    assert dx(8, 8, 8, hp, F.FP8_E5M2, None, f8, None, P, P, P, None) == F.FP8_ERR_NULL
+    assert dx(8, 8, 8, f8, F.FP8_E5M2, None, f8, P, P, P, P, None) == F.FP8_ERR_DTYPE
+    dw = lib.fp8_linear_bwd_dw
+    assert dw(8, 8, 8, hp, F.FP8_E5M2, None, f8, P, P, None, P, P, P, None) == F.FP8_ERR_NULL
+    assert dw(8, 8, 8, hp, 9, None, f8, P, None, None, P, P, P, None) == F.FP8_ERR_DTYPE
+
+
+def test_ring_init_validation(lib):
+    r = F._Ring()
+    assert lib.fp8_ring_init(None, P, 16, None) == F.FP8_ERR_NULL
+    assert lib.fp8_ring_init(ctypes.byref(r), None, 16, None) == F.FP8_ERR_NULL
+    assert lib.fp8_ring_init(ctypes.byref(r), P, 0, None) == F.FP8_ERR_RING
+    assert lib.fp8_ring_init(ctypes.byref(r), ctypes.c_void_p(0x100040), 16, None) == F.FP8_ERR_RING

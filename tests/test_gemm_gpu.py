@@ -1,0 +1,188 @@
+"""GPU parity of the three FP8 GEMMs (through fp8_linear_fwd / bwd_dx /
+bwd_dw with pre-quantized operands) against the oracle.
+
+Two kinds of inputs: small-integer fp8 values, for which every partial sum
+is exact and the bf16 output must equal the oracle bit for bit; and random
+codes over the whole finite range, checked against the 2^-7 contract and
+the 2^-10 diagnostic bound.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_quantize_fp8_amd as F
+from oracle import fp8_oracle as O
+from tests.gpu_util import (DEV, bf16_bits, check_gemm, f32_scalar, scalar_dev, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+INT_CODES = {  # value -> code for 0, +-1, +-2
+    O.E4M3: {0: 0x00, 1: 0x38, 2: 0x40, -1: 0xB8, -2: 0xC0},
+    O.E5M2: {0: 0x00, 1: 0x3C, 2: 0x40, -1: 0xBC, -2: 0xC0},
+}
+
+
+def _int_codes(shape, fmt, rng):
+    vals = rng.integers(-2, 3, size=shape)
+    lut = INT_CODES[fmt]
+    return np.vectorize(lambda v: lut[int(v)], otypes=[np.uint8])(vals)
+
+
+def _rand_codes(shape, fmt, rng):
+    tab = O.decode_table(fmt)
+    fin = np.array([c for c in range(256) if np.isfinite(tab[c])], np.uint8)
+    return rng.choice(fin, size=shape)
+
+
+def _q(codes, fmt, s):
+    return F.Quantized(to_dev(codes), fmt, scalar_dev(s))
+
+
+def run_fwd(x8, w8, fmt, sx, sw, bias=None):
+    M, K = x8.shape
+    N = w8.shape[0]
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    F.fp8_linear_fwd(_q(x8, fmt, sx), _q(w8, fmt, sw), bias, fmt, y)
+    torch.cuda.synchronize()
+    return bf16_bits(y)
+
+
+def run_dx(g8, fg, w8, fw, sg, sw):
+    M, N = g8.shape
+    K = w8.shape[1]
+    dx = torch.empty(M, K, dtype=torch.bfloat16, device=DEV)
+    F.fp8_linear_bwd_dx(_q(g8, fg, sg), fg, _q(w8, fw, sw), dx)
+    torch.cuda.synchronize()
+    return bf16_bits(dx)
+
+
+def run_dw(g8, fg, x8, fx, sg, sx, with_db=False):
+    M, N = g8.shape
+    K = x8.shape[1]
+    dw = torch.empty(N, K, dtype=torch.bfloat16, device=DEV)
+    db = ws = None
+    if with_db:
+        db = torch.empty(N, dtype=torch.bfloat16, device=DEV)
+        ws = torch.empty(max(1, F.fp8_db_workspace_bytes(M, N) // 4), dtype=torch.float32, device=DEV)
+    F.fp8_linear_bwd_dw(_q(g8, fg, sg), fg, _q(x8, fx, sx), dw, db, ws)
+    torch.cuda.synchronize()
+    return bf16_bits(dw), (None if db is None else bf16_bits(db))
+
+
+SHAPES = [(128, 128, 128), (256, 384, 512), (200, 136, 300), (1, 1, 1), (33, 17, 129),
+          (130, 260, 1000)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_exact_small_integers_all_three(M, N, K):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    x8 = _int_codes((M, K), O.E4M3, rng)
+    w8 = _int_codes((N, K), O.E4M3, rng)
+    g8 = _int_codes((M, N), O.E5M2, rng)
+    y = run_fwd(x8, w8, O.E4M3, 1.0, 1.0)
+    assert np.array_equal(y, O.linear_fwd(x8, w8, O.E4M3, 1.0, 1.0).y_bits)
+    dx = run_dx(g8, O.E5M2, w8, O.E4M3, 1.0, 1.0)
+    assert np.array_equal(dx, O.linear_bwd_dx(g8, O.E5M2, w8, O.E4M3, 1.0, 1.0).y_bits)
+    dw, _ = run_dw(g8, O.E5M2, x8, O.E4M3, 1.0, 1.0)
+    assert np.array_equal(dw, O.linear_bwd_dw(g8, O.E5M2, x8, O.E4M3, 1.0, 1.0).y_bits)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("fa,fb", [(O.E4M3, O.E4M3), (O.E5M2, O.E4M3), (O.E5M2, O.E5M2),
+                                   (O.E4M3, O.E5M2)])
+def test_random_codes_tolerance(M, N, K, fa, fb):
+    rng = np.random.default_rng(M + N + K + 10 * fa + fb)
+    sa, sb = np.float32(37.5), np.float32(0.0625)
+    x8 = _rand_codes((M, K), fb, rng)
+    w8 = _rand_codes((N, K), fb, rng)
+    g8 = _rand_codes((M, N), fa, rng)
+    check_gemm(run_fwd(x8, w8, fb, sb, sa), O.linear_fwd(x8, w8, fb, sb, sa), "fwd")
+    check_gemm(run_dx(g8, fa, w8, fb, sa, sb), O.linear_bwd_dx(g8, fa, w8, fb, sa, sb), "dx")
+    dw, _ = run_dw(g8, fa, x8, fb, sa, sb)
+    check_gemm(dw, O.linear_bwd_dw(g8, fa, x8, fb, sa, sb), "dw")
+
+
+@pytest.mark.parametrize("bias_kind", ["bf16", "e4m3", "e5m2"])
+@pytest.mark.parametrize("N", [256, 77])
+def test_fused_bias(bias_kind, N):
+    rng = np.random.default_rng(N)
+    M, K = 160, 384
+    x8 = _rand_codes((M, K), O.E4M3, rng)
+    w8 = _rand_codes((N, K), O.E4M3, rng)
+    if bias_kind == "bf16":
+        bits = O.bf16_bits(rng.standard_normal(N) * 3.0)
+        bias = to_dev(bits.view(np.int16)).view(torch.bfloat16)
+        beta = O.bias_values(bits, "bf16")
+    else:
+        fmt = O.E4M3 if bias_kind == "e4m3" else O.E5M2
+        b8 = _rand_codes((N,), fmt, rng)
+        bs = np.float32(24.0)
+        bias = F.Quantized(to_dev(b8), fmt, scalar_dev(bs))
+        beta = O.bias_values(b8, bias_kind, bs)
+    y = run_fwd(x8, w8, O.E4M3, 3.0, 5.0, bias)
+    check_gemm(y, O.linear_fwd(x8, w8, O.E4M3, 3.0, 5.0, beta), "fwd+bias")
+    # small-integer operands with a bf16-exact bias: bit-exact
+    xi = _int_codes((M, K), O.E4M3, rng)
+    wi = _int_codes((N, K), O.E4M3, rng)
+    if bias_kind == "bf16":
+        y = run_fwd(xi, wi, O.E4M3, 1.0, 1.0, bias)
+        assert np.array_equal(y, O.linear_fwd(xi, wi, O.E4M3, 1.0, 1.0, beta).y_bits)
+
+
+def test_identity_weight_special_case():
+    rng = np.random.default_rng(2)
+    x8 = _rand_codes((128, 256), O.E4M3, rng)
+    w8 = np.where(np.eye(256, dtype=bool), 0x38, 0x00).astype(np.uint8)
+    y = run_fwd(x8, w8, O.E4M3, 64.0, 2.0)
+    ref = O.linear_fwd(x8, w8, O.E4M3, 64.0, 2.0)
+    assert np.array_equal(y, ref.y_bits)
+    # closed form dec(x)/(sx sw); a dot product of -0 with +0 terms is +0
+    assert np.array_equal(y, O.bf16_bits(O.decode_array(x8, O.E4M3) / 128.0 + 0.0))
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 48, 0), (0, 48, 64), (48, 0, 64)])
+def test_degenerate_sizes(M, N, K):
+    rng = np.random.default_rng(0)
+    x8 = _rand_codes((M, K), O.E4M3, rng)
+    w8 = _rand_codes((N, K), O.E4M3, rng)
+    g8 = _rand_codes((M, N), O.E5M2, rng)
+    assert np.array_equal(run_fwd(x8, w8, O.E4M3, 2.0, 2.0),
+                          O.linear_fwd(x8, w8, O.E4M3, 2.0, 2.0).y_bits)
+    assert np.array_equal(run_dx(g8, O.E5M2, w8, O.E4M3, 2.0, 2.0),
+                          O.linear_bwd_dx(g8, O.E5M2, w8, O.E4M3, 2.0, 2.0).y_bits)
+    dw, db = run_dw(g8, O.E5M2, x8, O.E4M3, 2.0, 2.0, with_db=True)
+    assert np.array_equal(dw, O.linear_bwd_dw(g8, O.E5M2, x8, O.E4M3, 2.0, 2.0).y_bits)
+    ref_db = O.bias_grad(O.dequantized(g8, O.E5M2, 2.0))
+    assert np.array_equal(db, ref_db.y_bits)
+
+
+@pytest.mark.parametrize("M,N", [(2048, 1536), (100, 40), (37, 300)])
+def test_db_from_prequantized_gradient(M, N):
+    rng = np.random.default_rng(M)
+    g8 = _rand_codes((M, N), O.E5M2, rng)
+    x8 = _rand_codes((M, 64), O.E4M3, rng)
+    sg = np.float32(2048.0)
+    _, db = run_dw(g8, O.E5M2, x8, O.E4M3, sg, 1.0, with_db=True)
+    check_gemm(db, O.bias_grad(O.dequantized(g8, O.E5M2, sg)), "db")
+
+
+def test_full_size_sampled_rows():
+    """dim1536/ffn6912 shapes at M = 2048, full GPU outputs, oracle on a
+    seeded sample of rows plus the first and last rows."""
+    rng = np.random.default_rng(99)
+    for (K, N) in ((1536, 4608), (1536, 1536), (1536, 6912), (6912, 1536)):
+        M = 2048
+        x8 = _rand_codes((M, K), O.E4M3, rng)
+        w8 = _rand_codes((N, K), O.E4M3, rng)
+        g8 = _rand_codes((M, N), O.E5M2, rng)
+        rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 48, replace=False)]))
+        y = run_fwd(x8, w8, O.E4M3, 100.0, 3000.0)
+        check_gemm(y[rows], O.linear_fwd(x8[rows], w8, O.E4M3, 100.0, 3000.0), f"fwd {K}x{N}")
+        dx = run_dx(g8, O.E5M2, w8, O.E4M3, 7.0e3, 3000.0)
+        check_gemm(dx[rows], O.linear_bwd_dx(g8[rows], O.E5M2, w8, O.E4M3, 7.0e3, 3000.0),
+                   f"dx {K}x{N}")
+        dw, _ = run_dw(g8, O.E5M2, x8, O.E4M3, 7.0e3, 100.0)
+        nrows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 48, replace=False)]))
+        check_gemm(dw[nrows], O.linear_bwd_dw(g8[:, nrows], O.E5M2, x8, O.E4M3, 7.0e3, 100.0),
+                   f"dw {K}x{N}")
