@@ -1,0 +1,346 @@
+"""Benchmark of the FP8 linear-layer hot path on one MI355X.
+
+One step = one transformer layer of the dim1536 / ffn6912 model at M = 2048
+tokens: for each of its five linears (qkv, out, up, gate, down) the forward
+(quantize X and W with delayed-scaling rings, Y = X8 W8^T / (sx sw) + bias),
+the weight/bias gradient (quantize G with its ring and column partials,
+dW = G8^T X8 / (sg sx), db) and the input gradient (dX = G8 W8 / (sg sw)):
+15 FP8 GEMMs and 15 quantizes.  Inputs are seeded synthetic bf16 tensors,
+resident in HBM before the timed region.
+
+Prints one JSON line (see the fields below).  --gpus N > 1 is refused: this
+benchmark measures one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MI355X_FP8_DENSE_TFLOPS = 5000.0   # published dense FP8 MFMA peak
+MI355X_HBM_GBPS = 8000.0           # published HBM3E bandwidth
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="dim1536_m2048")
+    p.add_argument("--kernel-reps", type=int, default=20, help="repeats of each isolated kernel timing")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    p.add_argument("--only", default=None,
+                   help="profiling aid: run only this kernel class (fwd, dx, dw, quant, copy) "
+                        "for --steps iterations and exit")
+    return p.parse_args()
+
+
+class Layer:
+    """Device buffers, rings and bound C calls of one linear."""
+
+    def __init__(self, F, WL, wl, li, dev, stream):
+        import torch
+
+        X, W, b, G = WL.layer_inputs(wl, li)
+        self.name = wl.linears[li].name
+        self.M, self.K = X.shape
+        self.N = W.shape[0]
+        M, N, K = self.M, self.N, self.K
+        e = lambda *s, dt=torch.uint8: torch.empty(*s, dtype=dt, device=dev)
+        f = lambda: torch.zeros(1, dtype=torch.float32, device=dev)
+        self.X, self.W, self.b, self.G = X.to(dev), W.to(dev), b.to(dev), G.to(dev)
+        self.x8, self.w8, self.g8 = e(M, K), e(N, K), e(M, N)
+        self.y = e(M, N, dt=torch.bfloat16)
+        self.dx = e(M, K, dt=torch.bfloat16)
+        self.dw = e(N, K, dt=torch.bfloat16)
+        self.db = e(N, dt=torch.bfloat16)
+        self.ws = e(max(1, F.fp8_db_workspace_bytes(M, N) // 4), dt=torch.float32)
+        self.sx, self.sw, self.sg, self.ax, self.aw, self.ag = (f() for _ in range(6))
+        self.rx, self.rw, self.rg = (F.ScaleRing(wl.hist_len, stream=stream) for _ in range(3))
+        self.flops = 2.0 * M * N * K  # per GEMM
+        x8q = F.Quantized(self.x8, F.FP8_E4M3, self.sx)
+        w8q = F.Quantized(self.w8, F.FP8_E4M3, self.sw)
+        g8q = F.Quantized(self.g8, F.FP8_E5M2, self.sg)
+        # the three calls of a training step
+        self.fwd = F.bind_fp8_linear_fwd(self.X, self.W, self.b, F.FP8_E4M3, self.y, self.rx,
+                                         self.rw, self.x8, self.w8, self.sx, self.sw, self.ax,
+                                         self.aw, stream=stream)
+        self.bwd_dw = F.bind_fp8_linear_bwd_dw(self.G, F.FP8_E5M2, x8q, self.dw, self.db, self.ws,
+                                               self.rg, self.g8, self.sg, self.ag, stream=stream)
+        self.bwd_dx = F.bind_fp8_linear_bwd_dx(g8q, F.FP8_E5M2, w8q, self.dx, stream=stream)
+        # single-kernel calls (pre-quantized operands) for isolated timings
+        self.gemm_fwd = F.bind_fp8_linear_fwd(x8q, w8q, self.b, F.FP8_E4M3, self.y, stream=stream)
+        self.gemm_dw = F.bind_fp8_linear_bwd_dw(g8q, F.FP8_E5M2, x8q, self.dw, stream=stream)
+        self.quant = {
+            "X": F.bind_fp8_quantize(self.X, F.FP8_E4M3, self.x8, self.rx, self.sx, self.ax,
+                                     stream=stream),
+            "W": F.bind_fp8_quantize(self.W, F.FP8_E4M3, self.w8, self.rw, self.sw, self.aw,
+                                     stream=stream),
+            "G": F.bind_fp8_quantize(self.G, F.FP8_E5M2, self.g8, self.rg, self.sg, self.ag,
+                                     stream=stream),
+        }
+
+    def quant_bytes(self, which):
+        n = {"X": self.M * self.K, "W": self.N * self.K, "G": self.M * self.N}[which]
+        return 3.0 * n  # bf16 read + fp8 write
+
+
+def event_time_ms(torch, fn, reps, stream):
+    """Average GPU duration of fn() over reps calls: a GPU sleep is queued
+    first so every call is enqueued before the GPU reaches the start event,
+    and the events bracket pure device time."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(2_000_000)
+        start.record(stream)
+        for _ in range(reps):
+            fn()
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "scaled_quantize_fp8_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str):
+    """HBM bytes per launch from the committed PMC summary of this kernel, or
+    None if absent or taken on different kernel sources."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel_key}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(layers_cpu, budget_s):
+    """The oracle (untuned) on a bounded row sample of the same layer: the
+    quantizes of X/W/G and the three GEMMs per linear.  Rate in TFLOP/s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import fp8_oracle as O
+
+    rows = 512
+    flops = 0.0
+    t0 = time.perf_counter()
+    done = 0
+    for (X, W, b, G) in layers_cpu:
+        xs = X[:rows].float().numpy()
+        gs = G[:rows].float().numpy()
+        ws = W.float().numpy()
+        x8, sx, _ = O.quantize_step(xs, O.E4M3, None)
+        w8, sw, _ = O.quantize_step(ws, O.E4M3, None)
+        g8, sg, _ = O.quantize_step(gs, O.E5M2, None)
+        beta = O.bias_values(b.view(__import__("torch").int16).numpy().view(np.uint16), "bf16")
+        O.linear_fwd(x8, w8, O.E4M3, sx, sw, beta)
+        O.linear_bwd_dx(g8, O.E5M2, w8, O.E4M3, sg, sw)
+        O.linear_bwd_dw(g8, O.E5M2, x8, O.E4M3, sg, sx)
+        O.bias_grad(gs.astype(np.float64))
+        K, N = X.shape[1], W.shape[0]
+        flops += 3 * 2.0 * rows * N * K
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {layers_cpu[0][0].shape[0]} rows of X and G, full W, for "
+                      f"{done} of {len(layers_cpu)} linears: quantize X/W/G (dynamic) + fwd/dX/dW "
+                      f"GEMMs + db, fp64 accumulation; {dt:.1f} s on {os.cpu_count()} host cpus"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design note, not a built path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import scaled_quantize_fp8_amd as F
+    from scaled_quantize_fp8_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    F.lib()  # fails loudly if the HIP library is missing
+    wl = WL.WORKLOADS[args.workload]
+    stream = torch.cuda.Stream()
+    layers = [Layer(F, WL, wl, li, dev, stream) for li in range(len(wl.linears))]
+
+    def step():
+        for L in layers:
+            L.fwd()
+            L.bwd_dw()
+            L.bwd_dx()
+
+    if args.only:
+        # profiling aid: one kernel class only, args.steps times
+        step()  # seed the rings
+        torch.cuda.synchronize()
+        src = dst = None
+        if args.only == "copy":
+            src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(args.steps):
+                if args.only == "copy":
+                    dst.copy_(src)
+                    continue
+                for L in layers:
+                    if args.only == "fwd":
+                        L.gemm_fwd()
+                    elif args.only == "dx":
+                        L.bwd_dx()
+                    elif args.only == "dw":
+                        L.gemm_dw()
+                    elif args.only == "quant":
+                        for w in ("X", "W", "G"):
+                            L.quant[w]()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "steps": args.steps}))
+        return
+
+    for _ in range(max(1, args.warmup)):  # the first step seeds the rings
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly args.steps eager steps
+    dx_ev = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        t_start.record(stream)
+        for _ in range(args.steps):
+            for L in layers:
+                L.fwd()
+                L.bwd_dw()
+                a = torch.cuda.Event(enable_timing=True)
+                b_ = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                L.bwd_dx()
+                b_.record(stream)
+                dx_ev.append((a, b_))
+        t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = t_start.elapsed_time(t_end)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    step_flops = sum(3 * L.flops for L in layers)
+    tflops = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    # dX GEMM launches measured live in the timed region (bwd_dx with a
+    # pre-quantized gradient launches exactly one kernel)
+    dx_ms = sum(a.elapsed_time(b_) for a, b_ in dx_ev) / len(dx_ev)
+    dx_flops = sum(L.flops for L in layers) / len(layers)
+
+    # ---- the same step captured as one HIP graph and replayed
+    graph_ms_per_step = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        torch.cuda.synchronize()
+        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            g.replay()
+            gs.record(stream)
+            for _ in range(args.steps):
+                g.replay()
+            ge.record(stream)
+        torch.cuda.synchronize()
+        graph_ms_per_step = gs.elapsed_time(ge) / args.steps
+    except Exception as exc:  # graph capture is an extra measurement only
+        print(f"graph capture skipped: {exc}", file=sys.stderr)
+
+    # ---- isolated per-kernel timings (events behind a GPU sleep)
+    reps = args.kernel_reps
+    per = {}
+    for L in layers:
+        per[L.name] = {
+            "fwd_gemm_us": 1e3 * event_time_ms(torch, L.gemm_fwd, reps, stream),
+            "dx_gemm_us": 1e3 * event_time_ms(torch, L.bwd_dx, reps, stream),
+            "dw_gemm_us": 1e3 * event_time_ms(torch, L.gemm_dw, reps, stream),
+        }
+        for w in ("X", "W", "G"):
+            us = 1e3 * event_time_ms(torch, L.quant[w], reps, stream)
+            per[L.name][f"quant_{w}_us"] = us
+            per[L.name][f"quant_{w}_GBps"] = L.quant_bytes(w) / (us * 1e-6) / 1e9
+    for L in layers:
+        p = per[L.name]
+        for g_ in ("fwd", "dx", "dw"):
+            p[f"{g_}_TFLOPs"] = L.flops / (p[f"{g_}_gemm_us"] * 1e-6) / 1e12
+    tot = {g_: sum(per[L.name][f"{g_}_gemm_us"] for L in layers) for g_ in ("fwd", "dx", "dw")}
+    q_us = sum(per[L.name][f"quant_{w}_us"] for L in layers for w in ("X", "W", "G"))
+    q_bytes = sum(L.quant_bytes(w) for L in layers for w in ("X", "W", "G"))
+    quant_gbps = q_bytes / (q_us * 1e-6) / 1e9
+
+    achieved = dx_flops / (dx_ms * 1e-3) / 1e12
+    traffic = load_traffic("gemm_dx_" + args.workload)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_FP8_DENSE_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP8_DENSE_TFLOPS, 4),
+                "traffic": traffic,
+                "kernel": "gemm_kernel<kKContig,kCross,E5M2,E4M3> (dX = G8 W8, W8 read crosswise)",
+                "launch_avg_us": round(dx_ms * 1e3, 2),
+                "flops_per_launch": dx_flops}
+
+    out = {
+        "metric": "FP8 linear fwd+dX+dW TFLOP/s and % FP8 MFMA peak; quantize GB/s vs HBM peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: dim1536/ffn6912 layer, M={wl.M} tokens, "
+                               "qkv/out/up/gate/down fwd+dW(+db)+dX, delayed scaling H=16",
+                   "global_batch": wl.M, "gemms_per_step": 15},
+        "pct_fp8_peak": round(100 * tflops / MI355X_FP8_DENSE_TFLOPS, 2),
+        "quantize_GBps": round(quant_gbps, 1),
+        "quantize_pct_hbm": round(100 * quant_gbps / MI355X_HBM_GBPS, 2),
+        "wall_s_timed": round(wall, 4),
+        "graph_ms_per_step": None if graph_ms_per_step is None else round(graph_ms_per_step, 4),
+        "graph_TFLOPs": None if graph_ms_per_step is None else
+        round(step_flops / (graph_ms_per_step * 1e-3) / 1e12, 2),
+        "gemm_us_per_step": {g: round(v, 1) for g, v in tot.items()},
+        "quant_us_per_step": round(q_us, 1),
+        "per_linear": {k: {kk: round(vv, 2) for kk, vv in v.items()} for k, v in per.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        layers_cpu = [WL.layer_inputs(wl, li) for li in range(len(wl.linears))]
+        out["cpu_baseline"] = cpu_baseline(layers_cpu, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -101,9 +101,11 @@ typedef struct {
  * rings in the quantize kernel and on one ring per operand; [P3] entry on
  * the scale snapshot).  Host struct owned by the caller.
  *   dev       device buffer of fp8_ring_bytes(hist_len) bytes, 256-byte
- *             aligned: a 64-byte header {float scale; u32 amax_acc (float
- *             bits); u32 counter; u32 idx; u32 hist_len; u32 seeded; ...}
- *             followed by float hist[hist_len].
+ *             aligned: a 128-byte header {float scale; u32 top_count;
+ *             u32 top_amax; u32 idx; u32 hist_len; u32 seeded; ...}, 16
+ *             election groups of 128 bytes {u32 count; ...; u32 amax; ...}
+ *             used by the last-block election of each launch (all zero
+ *             between launches), then float hist[hist_len].
  *   hist_len  H, 1..1024.
  *   seeded    host mirror, 0 until the first quantize through the ring has
  *             been enqueued.  That first quantize seeds the scale from its
@@ -124,12 +126,13 @@ int fp8_abi_version(void);
 /* Static description of a status code. */
 const char* fp8_status_str(int status);
 
-/* Bytes of a ring's device buffer: 64 + 4 * hist_len (0 if out of range). */
+/* Bytes of a ring's device buffer: 2176 + 4 * hist_len (0 if out of range). */
 size_t fp8_ring_bytes(int32_t hist_len);
 
 /*
  * Bind dev to ring and enqueue its reset: scale = 1, hist = 0, idx = 0,
- * counter = 0, amax_acc = 0; sets ring->hist_len and ring->seeded = 0.
+ * every election counter and max = 0; sets ring->hist_len and
+ * ring->seeded = 0.
  * Errors: FP8_ERR_NULL (ring or dev NULL), FP8_ERR_RING (hist_len out of
  * range, dev misaligned), FP8_ERR_HIP.
  */

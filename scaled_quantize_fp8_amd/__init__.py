@@ -153,45 +153,104 @@ def _ring(r):
 
 
 # ---------------------------------------------------------------- entry points
+# Each entry point has a *_args helper that turns tensors into the C argument
+# tuple (marshalling), the call itself, and a bind_* variant that marshals
+# once and returns a zero-argument callable (for launch-bound loops and graph
+# capture: the pointers, sizes and stream are fixed at bind time).
+
+def _vp(t):
+    return ctypes.c_void_p(_ptr(t))
+
+
+def _quantize_args(x, fmt, q, ring, scale_used, amax_out, stream):
+    return (_vp(x), ctypes.c_int32(_TORCH_DT[x.dtype]), ctypes.c_int64(x.numel()),
+            ctypes.c_int32(fmt), _vp(q), _ring(ring), _vp(scale_used), _vp(amax_out),
+            ctypes.c_void_p(_stream(stream)))
+
+
+def _fwd_args(x, w, bias, fmt, y, ring_x, ring_w, x8_out, w8_out, sx_used, sw_used, amax_x,
+              amax_w, stream):
+    xd = x.codes if isinstance(x, Quantized) else x
+    wd = w.codes if isinstance(w, Quantized) else w
+    M, K = xd.shape
+    N = wd.shape[0]
+    return (ctypes.c_int64(M), ctypes.c_int64(N), ctypes.c_int64(K), _operand(x), _operand(w),
+            _operand(bias), ctypes.c_int32(fmt), _ring(ring_x), _ring(ring_w), _vp(y), _vp(x8_out),
+            _vp(w8_out), _vp(sx_used), _vp(sw_used), _vp(amax_x), _vp(amax_w),
+            ctypes.c_void_p(_stream(stream)))
+
+
+def _dx_args(g, fmt_g, w8, dx, ring_g, g8_out, sg_used, amax_g, stream):
+    gd = g.codes if isinstance(g, Quantized) else g
+    M, N = gd.shape
+    K = w8.codes.shape[1]
+    return (ctypes.c_int64(M), ctypes.c_int64(N), ctypes.c_int64(K), _operand(g),
+            ctypes.c_int32(fmt_g), _ring(ring_g), _operand(w8), _vp(dx), _vp(g8_out),
+            _vp(sg_used), _vp(amax_g), ctypes.c_void_p(_stream(stream)))
+
+
+def _dw_args(g, fmt_g, x8, dw, db, db_ws, ring_g, g8_out, sg_used, amax_g, stream):
+    gd = g.codes if isinstance(g, Quantized) else g
+    M, N = gd.shape
+    K = x8.codes.shape[1]
+    return (ctypes.c_int64(M), ctypes.c_int64(N), ctypes.c_int64(K), _operand(g),
+            ctypes.c_int32(fmt_g), _ring(ring_g), _operand(x8), _vp(dw), _vp(db), _vp(db_ws),
+            _vp(g8_out), _vp(sg_used), _vp(amax_g), ctypes.c_void_p(_stream(stream)))
+
+
+def _bind(name, args):
+    fn = getattr(lib(), name)
+
+    def call():
+        st = fn(*args)
+        if st != FP8_OK:
+            raise Fp8Error(st, name)
+    return call
+
 
 def fp8_quantize(x, fmt, q, ring=None, scale_used=None, amax_out=None, stream=None):
-    st = lib().fp8_quantize(_ptr(x), _TORCH_DT[x.dtype], x.numel(), fmt, _ptr(q), _ring(ring),
-                            _ptr(scale_used), _ptr(amax_out), _stream(stream))
-    _check(st, "fp8_quantize")
+    _check(lib().fp8_quantize(*_quantize_args(x, fmt, q, ring, scale_used, amax_out, stream)),
+           "fp8_quantize")
+
+
+def bind_fp8_quantize(x, fmt, q, ring=None, scale_used=None, amax_out=None, stream=None):
+    return _bind("fp8_quantize", _quantize_args(x, fmt, q, ring, scale_used, amax_out, stream))
 
 
 def fp8_linear_fwd(x, w, bias, fmt, y, ring_x=None, ring_w=None, x8_out=None, w8_out=None,
                    sx_used=None, sw_used=None, amax_x=None, amax_w=None, stream=None):
     """x: [M,K] tensor or Quantized; w: [N,K] tensor or Quantized; bias: None,
     a bf16 [N] tensor or Quantized (fp8 codes with bias_scale)."""
-    xd = x.codes if isinstance(x, Quantized) else x
-    wd = w.codes if isinstance(w, Quantized) else w
-    M, K = xd.shape
-    N = wd.shape[0]
-    st = lib().fp8_linear_fwd(M, N, K, _operand(x), _operand(w), _operand(bias), fmt,
-                              _ring(ring_x), _ring(ring_w), _ptr(y), _ptr(x8_out), _ptr(w8_out),
-                              _ptr(sx_used), _ptr(sw_used), _ptr(amax_x), _ptr(amax_w),
-                              _stream(stream))
-    _check(st, "fp8_linear_fwd")
+    _check(lib().fp8_linear_fwd(*_fwd_args(x, w, bias, fmt, y, ring_x, ring_w, x8_out, w8_out,
+                                           sx_used, sw_used, amax_x, amax_w, stream)),
+           "fp8_linear_fwd")
+
+
+def bind_fp8_linear_fwd(x, w, bias, fmt, y, ring_x=None, ring_w=None, x8_out=None, w8_out=None,
+                        sx_used=None, sw_used=None, amax_x=None, amax_w=None, stream=None):
+    return _bind("fp8_linear_fwd", _fwd_args(x, w, bias, fmt, y, ring_x, ring_w, x8_out, w8_out,
+                                             sx_used, sw_used, amax_x, amax_w, stream))
 
 
 def fp8_linear_bwd_dx(g, fmt_g, w8, dx, ring_g=None, g8_out=None, sg_used=None, amax_g=None,
                       stream=None):
-    gd = g.codes if isinstance(g, Quantized) else g
-    M, N = gd.shape
-    K = w8.codes.shape[1]
-    st = lib().fp8_linear_bwd_dx(M, N, K, _operand(g), fmt_g, _ring(ring_g), _operand(w8),
-                                 _ptr(dx), _ptr(g8_out), _ptr(sg_used), _ptr(amax_g),
-                                 _stream(stream))
-    _check(st, "fp8_linear_bwd_dx")
+    _check(lib().fp8_linear_bwd_dx(*_dx_args(g, fmt_g, w8, dx, ring_g, g8_out, sg_used, amax_g,
+                                             stream)), "fp8_linear_bwd_dx")
+
+
+def bind_fp8_linear_bwd_dx(g, fmt_g, w8, dx, ring_g=None, g8_out=None, sg_used=None, amax_g=None,
+                           stream=None):
+    return _bind("fp8_linear_bwd_dx", _dx_args(g, fmt_g, w8, dx, ring_g, g8_out, sg_used, amax_g,
+                                               stream))
 
 
 def fp8_linear_bwd_dw(g, fmt_g, x8, dw, db=None, db_ws=None, ring_g=None, g8_out=None,
                       sg_used=None, amax_g=None, stream=None):
-    gd = g.codes if isinstance(g, Quantized) else g
-    M, N = gd.shape
-    K = x8.codes.shape[1]
-    st = lib().fp8_linear_bwd_dw(M, N, K, _operand(g), fmt_g, _ring(ring_g), _operand(x8),
-                                 _ptr(dw), _ptr(db), _ptr(db_ws), _ptr(g8_out), _ptr(sg_used),
-                                 _ptr(amax_g), _stream(stream))
-    _check(st, "fp8_linear_bwd_dw")
+    _check(lib().fp8_linear_bwd_dw(*_dw_args(g, fmt_g, x8, dw, db, db_ws, ring_g, g8_out,
+                                             sg_used, amax_g, stream)), "fp8_linear_bwd_dw")
+
+
+def bind_fp8_linear_bwd_dw(g, fmt_g, x8, dw, db=None, db_ws=None, ring_g=None, g8_out=None,
+                           sg_used=None, amax_g=None, stream=None):
+    return _bind("fp8_linear_bwd_dw", _dw_args(g, fmt_g, x8, dw, db, db_ws, ring_g, g8_out,
+                                               sg_used, amax_g, stream))

@@ -75,6 +75,11 @@ struct ColsumSpec {
   float* ws;
 };
 
+int64_t flat_blocks(int64_t n, int64_t cap) {
+  int64_t blocks = (n + kBlockChunk - 1) / kBlockChunk;
+  return blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
+}
+
 template <int IN, int FMT, int SMODE>
 void launch_convert(const QArgs& a, const ColsumSpec* cs, hipStream_t st) {
   if (cs && cs->rows > 0 && cs->cols > 0) {
@@ -82,23 +87,10 @@ void launch_convert(const QArgs& a, const ColsumSpec* cs, hipStream_t st) {
               (unsigned)((cs->rows + kColRowsPerChunk - 1) / kColRowsPerChunk));
     hipLaunchKernelGGL((quantize_colsum_kernel<IN, FMT, SMODE>), grid, dim3(kQThreads), 0, st, a);
   } else {
-    const int64_t nch = (a.n + kQVec - 1) / kQVec;
-    int64_t blocks = (nch + kQThreads - 1) / kQThreads;
-    const int64_t cap = (int64_t)cu_count() * 8;
-    blocks = blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
+    const int64_t blocks = flat_blocks(a.n, (int64_t)cu_count() * 8);
     hipLaunchKernelGGL((quantize_flat_kernel<IN, FMT, SMODE>), dim3((unsigned)blocks),
                        dim3(kQThreads), 0, st, a);
   }
-}
-
-template <int IN>
-void launch_amax(const void* x, int64_t n, int vec_ok, uint32_t* target, hipStream_t st) {
-  const int64_t nch = (n + kQVec - 1) / kQVec;
-  int64_t blocks = (nch + kQThreads - 1) / kQThreads;
-  const int64_t cap = (int64_t)cu_count() * 8;
-  blocks = blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
-  hipLaunchKernelGGL((amax_kernel<IN>), dim3((unsigned)blocks), dim3(kQThreads), 0, st, x, n,
-                     vec_ok, target);
 }
 
 template <int IN, int FMT>
@@ -115,8 +107,9 @@ void enqueue_quant_t(const void* x, int64_t n, uint8_t* q, fp8_ring_t* ring, flo
     a.rows = cs->rows;
     a.cols = cs->cols;
     a.colsum = cs->ws;
-    a.vec_ok = a.vec_ok && (cs->cols % 16 == 0);
+    a.vec_ok = a.vec_ok && (cs->cols % 8 == 0);
   }
+  const int vec_x = aligned16(x);
   if (ring) {
     a.ring = reinterpret_cast<RingHdr*>(ring->dev);
     a.hist = reinterpret_cast<float*>(reinterpret_cast<char*>(ring->dev) + sizeof(RingHdr));
@@ -124,15 +117,19 @@ void enqueue_quant_t(const void* x, int64_t n, uint8_t* q, fp8_ring_t* ring, flo
     if (ring->seeded) {
       launch_convert<IN, FMT, kScaleRing>(a, cs, st);
     } else {
-      // first use: measure amax into the ring's accumulator (0 between
-      // launches), seed the scale from it, then convert and fold.
-      launch_amax<IN>(x, n, aligned16(x), &a.ring->amax_acc, st);
+      // first use: the amax pass leaves max |x| in the ring header, the
+      // converting launch seeds the scale from it, converts and folds.
+      const int64_t blocks = flat_blocks(n, (int64_t)cu_count() * 8);
+      hipLaunchKernelGGL((amax_ring_kernel<IN>), dim3((unsigned)blocks), dim3(kQThreads), 0, st, x,
+                         n, vec_x, a.ring);
       launch_convert<IN, FMT, kScaleSeed>(a, cs, st);
       ring->seeded = 1;
     }
   } else {
     hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, st, reinterpret_cast<uint32_t*>(amax_out));
-    launch_amax<IN>(x, n, aligned16(x), reinterpret_cast<uint32_t*>(amax_out), st);
+    const int64_t blocks = flat_blocks(n, (int64_t)cu_count());
+    hipLaunchKernelGGL((amax_dyn_kernel<IN>), dim3((unsigned)blocks), dim3(kQThreads), 0, st, x, n,
+                       vec_x, reinterpret_cast<uint32_t*>(amax_out));
     launch_convert<IN, FMT, kScaleDyn>(a, cs, st);
   }
 }

@@ -35,17 +35,29 @@ struct FmtTraits<kE5M2> {
   static constexpr float kMax = 57344.0f;
 };
 
-// Ring header in device memory (64 bytes, then float hist[H]).
+// Ring buffer in device memory: a 128-byte header, 16 election groups of
+// 128 bytes (each on its own cache line so the blocks of different groups
+// never contend for one address), then float hist[H].
+constexpr int kGroups = 16;
+struct RingGroup {
+  uint32_t count;      // blocks of this group that finished (0 between launches)
+  uint32_t pad0[15];
+  uint32_t amax;       // max |x| bits over those blocks (0 between launches)
+  uint32_t pad1[15];
+};
 struct RingHdr {
-  float scale;        // scale the next quantize uses
-  uint32_t amax_acc;  // running max of |x| bits during a launch; 0 between launches
-  uint32_t counter;   // last-block ticket; 0 between launches
-  uint32_t idx;       // next hist slot
+  float scale;         // scale the next quantize uses
+  uint32_t top_count;  // groups that finished (0 between launches)
+  uint32_t top_amax;   // max |x| bits over finished groups (0 between launches,
+                       // except between the two passes of a seeding quantize)
+  uint32_t idx;        // next hist slot
   uint32_t hist_len;
   uint32_t seeded;
-  uint32_t reserved[10];
+  uint32_t reserved[26];
+  RingGroup group[kGroups];
 };
-static_assert(sizeof(RingHdr) == 64, "ring header is 64 bytes");
+static_assert(sizeof(RingGroup) == 128, "one election group per 128-byte line");
+static_assert(sizeof(RingHdr) == 128 + 16 * 128, "ring header layout");
 
 // ---------------------------------------------------------------- scale
 
@@ -129,8 +141,23 @@ FP8L_DEV uint32_t wave_max_u32(uint32_t v) {
   return max(max(r0, r1), max(r2, r3));
 }
 
-FP8L_DEV uint32_t atomic_load_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+// Device-scope atomics are all relaxed read-modify-writes: they are
+// performed at the device's point of coherence, so no L2 write-back or
+// invalidate (what an agent-scope release/acquire costs on a multi-XCD
+// part) is ever needed; ordering between two of them in one thread is
+// enforced by waiting for the first to return.
+FP8L_DEV uint32_t atom_max(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+FP8L_DEV uint32_t atom_add(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+FP8L_DEV uint32_t atom_xchg(uint32_t* p, uint32_t v) {
+  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+FP8L_DEV uint32_t atom_read(uint32_t* p) {
+  return __hip_atomic_fetch_max(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+FP8L_DEV void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace fp8l

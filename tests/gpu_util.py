@@ -50,16 +50,19 @@ def f32_scalar(t: torch.Tensor) -> np.float32:
 def ring_state(ring) -> dict:
     """Read a device ring back: scale, idx, hist, amax_acc, counter, seeded."""
     b = ring.buf.detach().to("cpu").numpy()
-    hdr = b[:64].view(np.uint32)
+    hdr = b[:128].view(np.uint32)
+    groups = b[128:2176].view(np.uint32).reshape(16, 32)
     H = int(hdr[4])
     return {
         "scale": b[:4].view(np.float32)[0],
-        "amax_acc": int(hdr[1]),
-        "counter": int(hdr[2]),
+        "top_count": int(hdr[1]),
+        "top_amax": int(hdr[2]),
         "idx": int(hdr[3]),
         "hist_len": H,
         "seeded": int(hdr[5]),
-        "hist": b[64:64 + 4 * H].view(np.float32).copy(),
+        "group_count": groups[:, 0].copy(),
+        "group_amax": groups[:, 16].copy(),
+        "hist": b[2176:2176 + 4 * H].view(np.float32).copy(),
     }
 
 
@@ -68,7 +71,9 @@ def assert_ring_matches(ring, oring: O.ScaleRing):
     assert st["scale"].tobytes() == np.float32(oring.scale).tobytes(), (st["scale"], oring.scale)
     assert st["idx"] == oring.idx
     assert st["hist"].tobytes() == oring.hist.astype(np.float32).tobytes()
-    assert st["amax_acc"] == 0 and st["counter"] == 0
+    # every election counter and running max is back at zero between launches
+    assert st["top_amax"] == 0 and st["top_count"] == 0
+    assert not st["group_count"].any() and not st["group_amax"].any()
     assert bool(st["seeded"]) == oring.seeded
 
 

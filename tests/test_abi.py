@@ -51,8 +51,8 @@ def test_version_and_status_strings(lib):
 
 
 def test_sizes(lib):
-    assert F.fp8_ring_bytes(16) == 64 + 64
-    assert F.fp8_ring_bytes(1024) == 64 + 4096
+    assert F.fp8_ring_bytes(16) == 2176 + 64
+    assert F.fp8_ring_bytes(1024) == 2176 + 4096
     assert F.fp8_ring_bytes(0) == 0 and F.fp8_ring_bytes(1025) == 0
     assert F.fp8_db_workspace_bytes(2048, 6912) == 4 * 64 * 6912
     assert F.fp8_db_workspace_bytes(33, 10) == 4 * 2 * 10
