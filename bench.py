@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=20, help="repeats of each isolated kernel timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    p.add_argument("--sweep-tiles", action="store_true",
+                   help="time every GEMM of the step under each tile configuration and exit")
     p.add_argument("--only", default=None,
                    help="profiling aid: run only this kernel class (fwd, dx, dw, quant, copy) "
                         "for --steps iterations and exit")
@@ -195,6 +197,25 @@ def main():
             L.fwd()
             L.bwd_dw()
             L.bwd_dx()
+
+    if args.sweep_tiles:
+        step()  # seed the rings and fill the quantized operands
+        torch.cuda.synchronize()
+        res = {}
+        for tile in ("256x256", "256x128", "128x128", "v1"):
+            os.environ["FP8L_TILE"] = tile
+            for L in layers:
+                for gname, fn in (("fwd", L.gemm_fwd), ("dx", L.bwd_dx), ("dw", L.gemm_dw)):
+                    fn()
+                    us = 1e3 * event_time_ms(torch, fn, args.kernel_reps, stream)
+                    res.setdefault(f"{L.name}.{gname}", {})[tile] = round(us, 2)
+        os.environ.pop("FP8L_TILE", None)
+        for L in layers:
+            for gname, fn in (("fwd", L.gemm_fwd), ("dx", L.bwd_dx), ("dw", L.gemm_dw)):
+                us = 1e3 * event_time_ms(torch, fn, args.kernel_reps, stream)
+                res[f"{L.name}.{gname}"]["auto"] = round(us, 2)
+        print(json.dumps({"sweep_us": res}))
+        return
 
     if args.only:
         # profiling aid: one kernel class only, args.steps times

@@ -7,11 +7,15 @@
 // [P1]/[P3].  Every check below runs before the first launch, so an error
 // status means nothing was enqueued.
 #include <limits.h>
+#include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "../../include/fp8linear.h"
 #include "fp8l_device.hpp"
 #include "fp8l_gemm.hpp"
+#include "fp8l_gemm3.hpp"
 #include "fp8l_quantize.hpp"
 
 namespace fp8l {
@@ -160,8 +164,98 @@ void launch_gemm_t(GemmArgs& g, hipStream_t st) {
                      dim3(kGThreads), 0, st, g);
 }
 
+template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB>
+void launch_gemm3_t(GemmArgs& g, hipStream_t st) {
+  constexpr int lds = gemm3_lds_bytes<BM, BN, WGM, WGN>();
+  static bool attr_set[64] = {false};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+    (void)hipFuncSetAttribute((const void*)gemm3_kernel<BM, BN, WGM, WGN, LA, LB, FA, FB>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr_set[dev] = true;
+  }
+  g.tiles_m = (int32_t)((g.Mc + BM - 1) / BM);
+  g.tiles_n = (int32_t)((g.Nc + BN - 1) / BN);
+  if (g.tiles_m < 1) g.tiles_m = 1;
+  if (g.tiles_n < 1) g.tiles_n = 1;
+  hipLaunchKernelGGL((gemm3_kernel<BM, BN, WGM, WGN, LA, LB, FA, FB>),
+                     dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(64 * WGM * WGN), lds, st, g);
+}
+
+enum { kTileAuto = 0, kTile256x256, kTile256x128, kTile128x128, kTileV1 };
+
+// FP8L_TILE forces a tile configuration (for sweeps and tests): 256x256,
+// 256x128, 128x128 or v1 (the general register-staged kernel).  Read at
+// every launch so one process can compare configurations.
+int forced_tile() {
+  const char* e = getenv("FP8L_TILE");
+  if (!e) return kTileAuto;
+  if (!strcmp(e, "256x256")) return kTile256x256;
+  if (!strcmp(e, "256x128")) return kTile256x128;
+  if (!strcmp(e, "128x128")) return kTile128x128;
+  if (!strcmp(e, "v1")) return kTileV1;
+  return kTileAuto;
+}
+
+// Tile choice: fewest rounds of resident tiles times the tile's work, with
+// the efficiency of smaller tiles discounted (they re-read more operand
+// bytes per MFMA from LDS).
+int choose_tile(int64_t Mc, int64_t Nc) {
+  const int cus = cu_count();
+  struct Cfg { int id, bm, bn, per_cu; double eff; };
+  const Cfg cfgs[3] = {{kTile256x256, 256, 256, 1, 1.0},
+                       {kTile256x128, 256, 128, 1, 0.9},
+                       {kTile128x128, 128, 128, 2, 0.7}};
+  int best = kTile256x256;
+  double best_cost = 1e300;
+  for (const Cfg& c : cfgs) {
+    const double tiles = (double)((Mc + c.bm - 1) / c.bm) * (double)((Nc + c.bn - 1) / c.bn);
+    const double rounds = ceil(tiles / (double)(cus * c.per_cu));
+    const double cost = rounds * c.bm * c.bn / c.eff;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = c.id;
+    }
+  }
+  return best;
+}
+
+template <int BM, int BN, int WGM, int WGN, int LA, int LB>
+void launch_gemm3_f(GemmArgs& g, int fa, int fb, hipStream_t st) {
+  if (fa == kE4M3 && fb == kE4M3) launch_gemm3_t<BM, BN, WGM, WGN, LA, LB, kE4M3, kE4M3>(g, st);
+  else if (fa == kE4M3 && fb == kE5M2) launch_gemm3_t<BM, BN, WGM, WGN, LA, LB, kE4M3, kE5M2>(g, st);
+  else if (fa == kE5M2 && fb == kE4M3) launch_gemm3_t<BM, BN, WGM, WGN, LA, LB, kE5M2, kE4M3>(g, st);
+  else launch_gemm3_t<BM, BN, WGM, WGN, LA, LB, kE5M2, kE5M2>(g, st);
+}
+
+// The fast kernel needs 16-byte chunks that never straddle a matrix edge and
+// byte offsets that fit a buffer descriptor.
+template <int LA, int LB>
+bool fast_path_ok(const GemmArgs& g) {
+  const int64_t a_rows = (LA == kKContig) ? g.Mc : g.Kc;
+  const int64_t b_rows = (LB == kKContig) ? g.Nc : g.Kc;
+  const int64_t a_inner = (LA == kKContig) ? g.Kc : g.Mc;
+  const int64_t b_inner = (LB == kKContig) ? g.Kc : g.Nc;
+  // a tile may hang up to 256 rows past the last one; its offsets must stay
+  // below 2^32 so they read as out of range instead of wrapping
+  return aligned16(g.a) && aligned16(g.b) && aligned16(g.c) && g.ldc % 8 == 0 && g.Nc % 8 == 0 &&
+         g.lda % 16 == 0 && g.ldb % 16 == 0 &&
+         a_inner % 16 == 0 && b_inner % 16 == 0 && (a_rows + 256) * g.lda < (1LL << 31) &&
+         (b_rows + 256) * g.ldb < (1LL << 31);
+}
+
 template <int LA, int LB>
 void launch_gemm_l(GemmArgs& g, int fa, int fb, hipStream_t st) {
+  int tile = forced_tile();
+  if (!fast_path_ok<LA, LB>(g)) tile = kTileV1;
+  if (tile == kTileAuto) tile = choose_tile(g.Mc, g.Nc);
+  switch (tile) {
+    case kTile256x256: launch_gemm3_f<256, 256, 2, 2, LA, LB>(g, fa, fb, st); return;
+    case kTile256x128: launch_gemm3_f<256, 128, 2, 2, LA, LB>(g, fa, fb, st); return;
+    case kTile128x128: launch_gemm3_f<128, 128, 2, 2, LA, LB>(g, fa, fb, st); return;
+    default: break;
+  }
   if (fa == kE4M3 && fb == kE4M3) launch_gemm_t<LA, LB, kE4M3, kE4M3>(g, st);
   else if (fa == kE4M3 && fb == kE5M2) launch_gemm_t<LA, LB, kE4M3, kE5M2>(g, st);
   else if (fa == kE5M2 && fb == kE4M3) launch_gemm_t<LA, LB, kE5M2, kE4M3>(g, st);

@@ -1,0 +1,501 @@
+// Pipelined FP8 GEMM for gfx950 (dimensions multiples of 16, matrices below
+// 2 GiB); same contract as gemm_kernel in fp8l_gemm.hpp:
+//
+//   C[i, j] = sum_k A(i, k) B(j, k) / (sa sb) (+ bias[j]), bf16 out.
+//
+// Why this shape of pipeline: on MI355X an operand fetch that misses L2
+// takes thousands of cycles, far more than one K step of MFMA work, so the
+// K loop must keep several steps of operands in flight.  Register staging
+// cannot (each step in flight costs a register set), so operands go from
+// HBM/L2 straight into LDS with buffer_load_dwordx4 ... lds (DMA: each lane
+// writes its 16 bytes at base + 16 * lane, and an offset past the buffer's
+// end writes zeros, which is how row and K tails become exact zeros).
+//
+//  * K advances 64 bytes per step (one v_mfma_f32_32x32x64_f8f6f4 depth).
+//    LDS holds 4 steps; the DMA for step k+4 is issued while step k is being
+//    multiplied, so each step's operands have 3 steps of MFMA time to land.
+//  * Fragments are double-buffered in registers: during step k the waves
+//    multiply step k's fragments while reading step k+1's from LDS.  One
+//    barrier per step (it also retires the LDS buffer step k+4 refills).
+//  * LDS reads are inline asm (ds_read_b128, ds_read_b64_tr_b8) that wait
+//    for their own results: the compiler cannot see them, so it does not
+//    drain the DMA queue before them; vmcnt is managed explicitly.
+//  * k-contiguous tiles sit in LDS as [rows][64 B]; crosswise tiles (dX's W,
+//    both operands of dW) as they lie in memory, [64 k][rows], read through
+//    the LDS transpose ds_read_b64_tr_b8.  16-byte chunks are XOR-swizzled
+//    against bank conflicts on both the DMA writes and the fragment reads.
+//  * Block tile BM x BN by a WGM x WGN grid of waves, each wave a grid of
+//    32x32 MFMA tiles; tiles renumbered XCD-major (see fp8l_gemm2.hpp).
+//  * Epilogue: (1/sa)(1/sb), bias in one fp32 fma, one RNE to bf16, staged
+//    through LDS and written back as whole rows.
+#pragma once
+
+#include <type_traits>
+
+#include "fp8l_gemm2.hpp"
+
+namespace fp8l {
+
+constexpr int kBK3 = 64;
+constexpr int kStages3 = 4;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+FP8L_DEV uint32_t lds_off(const uint8_t* p) { return (uint32_t)(uintptr_t)(const lds_u8*)p; }
+
+// k-contiguous rows of 64 B (4 chunks): 16 consecutive rows reading one
+// logical chunk hit 16 distinct 16-byte slots of a 256-byte bank row, and 8
+// consecutive rows 8 distinct slots of a 128-byte one.
+FP8L_DEV int swz64(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// ---- LDS fragment reads (inline asm; each block waits for its own data)
+
+FP8L_DEV void lds_read_kc2(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, v8i& f0, v8i& f1) {
+  v4i r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+  f0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  f1 = v8i{r2.x, r2.y, r2.z, r2.w, r3.x, r3.y, r3.z, r3.w};
+}
+
+FP8L_DEV void lds_read_x2(const uint32_t a[8], v8i& f0, v8i& f1) {
+  v2i r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %8\n\t"
+      "ds_read_b64_tr_b8 %1, %9\n\t"
+      "ds_read_b64_tr_b8 %2, %10\n\t"
+      "ds_read_b64_tr_b8 %3, %11\n\t"
+      "ds_read_b64_tr_b8 %4, %12\n\t"
+      "ds_read_b64_tr_b8 %5, %13\n\t"
+      "ds_read_b64_tr_b8 %6, %14\n\t"
+      "ds_read_b64_tr_b8 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+  f0 = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+  f1 = v8i{r4.x, r4.y, r5.x, r5.y, r6.x, r6.y, r7.x, r7.y};
+}
+
+// MFMAs of the current K step issued inside the same asm block as the LDS
+// reads of the next step's fragments, so the read latency overlaps MFMA
+// execution while the block still waits for its own data.  Operand roles as
+// in the builtin form: vdst/srcC = accumulator (AGPRs), srcA = fragment of B
+// (C columns, format FB via cbsz), srcB = fragment of A (C rows, FA via
+// blgp).  The compiler does not see these MFMAs, so the blocks carry their
+// own hazard padding and kernels drain before any VALU read of an
+// accumulator.  Mfma<NM> bundles the NM (1..4) accumulator updates a block
+// issues; unused slots alias slot 0 and are never named in the asm.
+struct MfmaSlot {
+  v16f* c;
+  const v8i* b;
+  const v8i* x;
+};
+
+#define FP8L_MF(i) \
+  "v_mfma_f32_32x32x64_f8f6f4 %[c" #i "], %[b" #i "], %[x" #i "], %[c" #i "] cbsz:%[fb] blgp:%[fa]\n\t"
+#define FP8L_MF1 FP8L_MF(0)
+#define FP8L_MF2 FP8L_MF1 FP8L_MF(1)
+#define FP8L_MF3 FP8L_MF2 FP8L_MF(2)
+#define FP8L_MF4 FP8L_MF3 FP8L_MF(3)
+#define FP8L_CO(i) [c##i] "+a"(*m[i].c)
+#define FP8L_CO1 FP8L_CO(0)
+#define FP8L_CO2 FP8L_CO1, FP8L_CO(1)
+#define FP8L_CO3 FP8L_CO2, FP8L_CO(2)
+#define FP8L_CO4 FP8L_CO3, FP8L_CO(3)
+#define FP8L_CI(i) [b##i] "v"(*m[i].b), [x##i] "v"(*m[i].x)
+#define FP8L_CI1 FP8L_CI(0)
+#define FP8L_CI2 FP8L_CI1, FP8L_CI(1)
+#define FP8L_CI3 FP8L_CI2, FP8L_CI(2)
+#define FP8L_CI4 FP8L_CI3, FP8L_CI(3)
+#define FP8L_FMT [fb] "n"(FB), [fa] "n"(FA)
+
+template <int FA, int FB, int NM>
+FP8L_DEV void mfma_only(const MfmaSlot (&m)[4]) {
+  // s_nop 1: operands may have just been written by VALU
+#define FP8L_ONLY(n) \
+  asm volatile("s_nop 1\n\t" FP8L_MF##n "" : FP8L_CO##n : FP8L_CI##n, FP8L_FMT)
+  if constexpr (NM == 1) FP8L_ONLY(1);
+  else if constexpr (NM == 2) FP8L_ONLY(2);
+  else if constexpr (NM == 3) FP8L_ONLY(3);
+  else FP8L_ONLY(4);
+#undef FP8L_ONLY
+}
+
+template <int FA, int FB, int NM>
+FP8L_DEV void fused_kc(const uint32_t ad[4], v8i& n0, v8i& n1, const MfmaSlot (&m)[4]) {
+  v4i r0, r1, r2, r3;
+#define FP8L_KC(n)                                                                        \
+  asm volatile("ds_read_b128 %[r0], %[a0]\n\t"                                            \
+               "ds_read_b128 %[r1], %[a1]\n\t"                                            \
+               "ds_read_b128 %[r2], %[a2]\n\t"                                            \
+               "ds_read_b128 %[r3], %[a3]\n\t" FP8L_MF##n "s_waitcnt lgkmcnt(0)"          \
+               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3), FP8L_CO##n \
+               : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]),      \
+                 FP8L_CI##n, FP8L_FMT                                                     \
+               : "memory")
+  if constexpr (NM == 1) FP8L_KC(1);
+  else if constexpr (NM == 2) FP8L_KC(2);
+  else if constexpr (NM == 3) FP8L_KC(3);
+  else FP8L_KC(4);
+#undef FP8L_KC
+  n0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  n1 = v8i{r2.x, r2.y, r2.z, r2.w, r3.x, r3.y, r3.z, r3.w};
+}
+
+template <int FA, int FB, int NM>
+FP8L_DEV void fused_x(const uint32_t ad[8], v8i& n0, v8i& n1, const MfmaSlot (&m)[4]) {
+  v2i r0, r1, r2, r3, r4, r5, r6, r7;
+#define FP8L_X(n)                                                                            \
+  asm volatile("ds_read_b64_tr_b8 %[r0], %[a0]\n\t"                                          \
+               "ds_read_b64_tr_b8 %[r1], %[a1]\n\t"                                          \
+               "ds_read_b64_tr_b8 %[r2], %[a2]\n\t"                                          \
+               "ds_read_b64_tr_b8 %[r3], %[a3]\n\t"                                          \
+               "ds_read_b64_tr_b8 %[r4], %[a4]\n\t"                                          \
+               "ds_read_b64_tr_b8 %[r5], %[a5]\n\t"                                          \
+               "ds_read_b64_tr_b8 %[r6], %[a6]\n\t"                                          \
+               "ds_read_b64_tr_b8 %[r7], %[a7]\n\t" FP8L_MF##n "s_waitcnt lgkmcnt(0)"        \
+               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3),             \
+                 [r4] "=&v"(r4), [r5] "=&v"(r5), [r6] "=&v"(r6), [r7] "=&v"(r7), FP8L_CO##n \
+               : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]),         \
+                 [a4] "v"(ad[4]), [a5] "v"(ad[5]), [a6] "v"(ad[6]), [a7] "v"(ad[7]),         \
+                 FP8L_CI##n, FP8L_FMT                                                        \
+               : "memory")
+  if constexpr (NM == 1) FP8L_X(1);
+  else if constexpr (NM == 2) FP8L_X(2);
+  else if constexpr (NM == 3) FP8L_X(3);
+  else FP8L_X(4);
+#undef FP8L_X
+  n0 = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+  n1 = v8i{r4.x, r4.y, r5.x, r5.y, r6.x, r6.y, r7.x, r7.y};
+}
+
+// VALU reads of MFMA results need wait states the compiler cannot insert
+// for asm MFMAs (a 16-pass MFMA needs 18); pad generously.
+FP8L_DEV void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
+
+// Calls f(integral_constant<int, i>) for i = 0 .. N-1 (compile-time indices,
+// so register arrays indexed by them stay in registers).
+template <int N, int I = 0, typename F>
+FP8L_DEV void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Explicit waits on the DMA queue (vmcnt) and the LDS barrier.
+template <int N>
+FP8L_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+FP8L_DEV void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// One operand of the pipelined kernel.  R: tile extent along C; NW: waves.
+template <int L, int R, int NW>
+struct Op3 {
+  static constexpr int kBytes = R * kBK3;          // one K step
+  static constexpr int kBlocks = kBytes / 1024;    // 1 KB DMA blocks per step
+  static constexpr int kPerWave = kBlocks / NW;    // DMA instructions per wave per step
+  static_assert(kPerWave >= 1 && kBlocks % NW == 0, "tile / wave split");
+  static constexpr int kCpr = (L == kKContig) ? 4 : R / 16;  // 16-byte chunks per LDS row
+
+  uint32_t base[kPerWave];  // byte offset of this lane's chunk at step 0
+  int32_t inner[kPerWave];  // position along the contiguous dimension (edge mask)
+  int64_t inlim;
+  uint32_t kstep;           // bytes per K step
+
+  FP8L_DEV static int swz(int row) {
+    if constexpr (L == kKContig) return swz64(row);
+    else return swz_cross<R>(row);
+  }
+
+  FP8L_DEV void init(int64_t ld, int64_t rbase, int64_t rlim, int64_t klim) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int blk = wave * kPerWave + i;
+      const int row = blk * (1024 / (kCpr * 16)) + lane / kCpr;  // LDS row of this lane
+      const int c = (lane % kCpr) ^ swz(row);                    // logical chunk it holds
+      if constexpr (L == kKContig) {
+        base[i] = (uint32_t)((rbase + row) * ld + 16 * c);
+        inner[i] = 16 * c;
+      } else {
+        base[i] = (uint32_t)((int64_t)row * ld + rbase + 16 * c);
+        inner[i] = (int32_t)(rbase + 16 * c);
+      }
+    }
+    inlim = (L == kKContig) ? klim : rlim;
+    kstep = (L == kKContig) ? (uint32_t)kBK3 : (uint32_t)(kBK3 * ld);
+  }
+
+  // DMA of K step kt into the step buffer at s (wave-uniform).
+  FP8L_DEV void issue(__amdgpu_buffer_rsrc_t rs, uint8_t* s, int kt) const {
+    const int wave = threadIdx.x >> 6;
+    const uint32_t koff = (uint32_t)kt * kstep;
+    const int64_t k0 = (int64_t)kt * kBK3;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int64_t in = (L == kKContig) ? k0 + inner[i] : (int64_t)inner[i];
+      const uint32_t off = in < inlim ? base[i] + koff : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(s + (wave * kPerWave + i) * 1024), 16, off,
+          0, 0, 0);
+    }
+  }
+
+  // LDS addresses of the reads that build two 32x32x64 fragments for tile
+  // indices f0 and f0 + 32 (lane l: index f0 + (l & 31), k bytes
+  // 32 (l >> 5) + [0, 32)).  k-contiguous: 2 reads per fragment; crosswise:
+  // 4 transpose reads per fragment (in each 16-lane group, lane 8h+i gets
+  // byte i of the 8-byte rows addressed by lanes 2j+h).
+  FP8L_DEV static void frag_addrs(const uint8_t* s, int f0, uint32_t a[8]) {
+    const int l = threadIdx.x & 63;
+    const uint32_t sb = lds_off(s);
+    if constexpr (L == kKContig) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int r = f0 + 32 * f + (l & 31);
+        const int c0 = 2 * (l >> 5);
+        a[2 * f + 0] = sb + r * 64 + ((c0 ^ swz64(r)) << 4);
+        a[2 * f + 1] = sb + r * 64 + (((c0 + 1) ^ swz64(r)) << 4);
+      }
+    } else {
+      const int q = l >> 4, sidx = l & 15;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int cc = ((f0 + 32 * f) >> 4) + (q & 1);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int kk = 32 * (q >> 1) + 8 * t + (sidx >> 1);
+          a[4 * f + t] = sb + kk * R + ((cc ^ swz_cross<R>(kk)) << 4) + ((sidx & 1) << 3);
+        }
+      }
+    }
+  }
+
+  // Reads of a fragment pair for the next step fused with NM MFMAs of the
+  // current one.
+  template <int FA, int FB, int NM>
+  FP8L_DEV static void read2_fused(const uint8_t* s, int f0, v8i& n0, v8i& n1,
+                                   const MfmaSlot (&m)[4]) {
+    uint32_t a[8];
+    frag_addrs(s, f0, a);
+    if constexpr (L == kKContig)
+      fused_kc<FA, FB, NM>(a, n0, n1, m);
+    else
+      fused_x<FA, FB, NM>(a, n0, n1, m);
+  }
+
+  FP8L_DEV static void read2(const uint8_t* s, int f0, v8i& x0, v8i& x1) {
+    uint32_t a[8];
+    frag_addrs(s, f0, a);
+    if constexpr (L == kKContig)
+      lds_read_kc2(a[0], a[1], a[2], a[3], x0, x1);
+    else
+      lds_read_x2(a, x0, x1);
+  }
+};
+
+template <int BM, int BN, int WGM, int WGN>
+constexpr int gemm3_lds_bytes() {
+  // operand ring, or the staged output tile if that is larger
+  return kStages3 * (BM + BN) * kBK3 > BM * (BN * 2 + 16) ? kStages3 * (BM + BN) * kBK3
+                                                         : BM * (BN * 2 + 16);
+}
+
+template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB>
+__global__ __launch_bounds__(64 * WGM * WGN, (BM * BN <= 128 * 128) ? 2 : 1)
+void gemm3_kernel(GemmArgs g) {
+  constexpr int NW = WGM * WGN;
+  using OA = Op3<LA, BM, NW>;
+  using OB = Op3<LB, BN, NW>;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
+  constexpr int FM = WTM / 32, FN = WTN / 32;    // 32x32 MFMA tiles per wave
+  static_assert(FM % 2 == 0 && FN % 2 == 0, "fragments are read in pairs");
+  constexpr int kStep = OA::kBytes + OB::kBytes;  // LDS bytes per K step
+  constexpr int kDma = OA::kPerWave + OB::kPerWave;  // DMA instructions per wave per step
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem3[];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int tm, tn;
+  tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
+
+  if (blockIdx.x == 0 && tid == 0) {
+    if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
+    if (g.aux_amax_dst0) *g.aux_amax_dst0 = 0.0f;
+    if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;
+    if (g.aux_amax_dst1) *g.aux_amax_dst1 = 0.0f;
+  }
+  if (g.db && tn == 0 && tid < BM) {
+    const int64_t i = i0 + tid;
+    if (i < g.Mc) {
+      float s = 0.0f;
+      for (int r = 0; r < g.db_R; ++r) s += g.db_ws[(int64_t)r * g.Mc + i];
+      if (g.db_scale) s *= 1.0f / *g.db_scale;
+      g.db[i] = (uint16_t)f32_to_bf16(s);
+    }
+  }
+  const float dq = (1.0f / *g.scale_a) * (1.0f / *g.scale_b);
+  const float inv_bs =
+      (g.bias_kind == kBiasE4M3 || g.bias_kind == kBiasE5M2) ? 1.0f / *g.bias_scale : 1.0f;
+  // nothing of the above may still count against vmcnt inside the loop
+  wait_vm<0>();
+
+  const int64_t a_rows = (LA == kKContig) ? g.Mc : g.Kc;
+  const int64_t b_rows = (LB == kKContig) ? g.Nc : g.Kc;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, (uint32_t)(a_rows * g.lda));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b, (uint32_t)(b_rows * g.ldb));
+  OA oa;
+  OB ob;
+  oa.init(g.lda, i0, g.Mc, g.Kc);
+  ob.init(g.ldb, j0, g.Nc, g.Kc);
+
+  const int wm = wave / WGN, wn = wave % WGN;
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int a = 0; a < FM; ++a)
+#pragma unroll
+    for (int b = 0; b < FN; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+
+  const int nk = (int)(((g.Kc + kBK3 - 1) / kBK3 + 1) & ~1);  // K steps, padded to even
+  auto step_buf = [&](int kt) { return smem3 + (kt % kStages3) * kStep; };
+
+  // prologue: DMA steps 0..3, then step 0's fragments
+  for (int s = 0; s < kStages3 && s < nk; ++s) {
+    oa.issue(ra, step_buf(s), s);
+    ob.issue(rb, step_buf(s) + OA::kBytes, s);
+  }
+  v8i fa[2][FM], fb[2][FN];
+  if (nk > 0) {
+    // step 0 landed: at most min(3, nk - 1) later steps still in flight
+    const int later = min(3, nk - 1);
+    if (later >= 3) wait_vm<3 * kDma>();
+    else if (later == 2) wait_vm<2 * kDma>();
+    else if (later == 1) wait_vm<kDma>();
+    else wait_vm<0>();
+    barrier_only();
+#pragma unroll
+    for (int f = 0; f < FM; f += 2) OA::read2(step_buf(0), wm * WTM + 32 * f, fa[0][f], fa[0][f + 1]);
+#pragma unroll
+    for (int f = 0; f < FN; f += 2)
+      OB::read2(step_buf(0) + OA::kBytes, wn * WTN + 32 * f, fb[0][f], fb[0][f + 1]);
+  }
+
+  // One K step.  CUR holds step kt's fragments; the other set receives
+  // step kt+1's.  Two MFMAs go ahead of the barrier; the rest are spread
+  // over the asm blocks that read the next fragments (one block per
+  // fragment pair), in row-major (a, b) order.
+  constexpr int kGroups = FM / 2 + FN / 2;
+  constexpr int kRest = FM * FN - 2;
+  static_assert(kRest >= kGroups && kRest <= 4 * kGroups, "MFMA split");
+  auto slot = [&](int CUR, int e) {
+    const int a = e / FN, b = e % FN;
+    return MfmaSlot{&acc[a][b], &fb[CUR][b], &fa[CUR][a]};
+  };
+  auto kstep_body = [&](int kt, auto cur_tag) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    constexpr int NXT = CUR ^ 1;
+    {
+      const MfmaSlot m[4] = {slot(CUR, 0), slot(CUR, 1), slot(CUR, 0), slot(CUR, 0)};
+      mfma_only<FA, FB, 2>(m);
+    }
+    {
+      // step kt+1 landed: at most min(2, nk-2-kt) later steps in flight
+      const int later = min(2, nk - 2 - kt);
+      if (later >= 2) wait_vm<2 * kDma>();
+      else if (later == 1) wait_vm<kDma>();
+      else wait_vm<0>();
+    }
+    barrier_only();  // step kt+1 visible to all; step kt's buffer is free
+    if (kt + kStages3 < nk) {
+      oa.issue(ra, step_buf(kt + kStages3), kt + kStages3);
+      ob.issue(rb, step_buf(kt + kStages3) + OA::kBytes, kt + kStages3);
+    }
+    static_for<kGroups>([&](auto gi_tag) {
+      constexpr int gi = decltype(gi_tag)::value;
+      // group gi issues entries [e0, e0 + n) of the MFMA list
+      constexpr int n = kRest / kGroups + (gi < kRest % kGroups ? 1 : 0);
+      constexpr int e0 = 2 + gi * (kRest / kGroups) + (gi < kRest % kGroups ? gi : kRest % kGroups);
+      const MfmaSlot m[4] = {slot(CUR, e0), slot(CUR, n > 1 ? e0 + 1 : e0),
+                             slot(CUR, n > 2 ? e0 + 2 : e0), slot(CUR, n > 3 ? e0 + 3 : e0)};
+      const uint8_t* sn = step_buf(kt + 1);
+      if constexpr (gi < FM / 2)
+        OA::template read2_fused<FA, FB, n>(sn, wm * WTM + 64 * gi, fa[NXT][2 * gi],
+                                            fa[NXT][2 * gi + 1], m);
+      else
+        OB::template read2_fused<FA, FB, n>(sn + OA::kBytes, wn * WTN + 64 * (gi - FM / 2),
+                                            fb[NXT][2 * (gi - FM / 2)],
+                                            fb[NXT][2 * (gi - FM / 2) + 1], m);
+    });
+  };
+
+  // The step count is padded to even so the loop body is one unrolled pair
+  // with a single register assignment: the padded step's DMA lies past K and
+  // lands as exact zeros (+0 products leave every sum unchanged), and the
+  // last step's reads of a successor fetch a stale buffer that is never used.
+  for (int kt = 0; kt < nk; kt += 2) {
+    kstep_body(kt, std::integral_constant<int, 0>{});
+    kstep_body(kt + 1, std::integral_constant<int, 1>{});
+  }
+
+  // Epilogue.  Each lane's accumulators hold 4 consecutive columns per
+  // register group, spread over 32 rows; storing them straight to global
+  // memory writes 16-byte pieces of many cache lines and ran at a fraction
+  // of HBM write bandwidth.  Instead the finished bf16 tile is staged in LDS
+  // (rows padded by 16 bytes, so the 32 rows of one store land on distinct
+  // banks) and written back as whole rows, 16 bytes per lane.
+  // lane holds, for reg e: row wm*WTM + 32a + (lane & 31),
+  //   column wn*WTN + 32b + 8(e>>2) + 4(lane>>5) + (e&3) of the block tile
+  constexpr int RS = BN * 2 + 16;  // LDS bytes per staged row
+  mfma_drain();                    // accumulators are read by VALU below
+  barrier_only();                  // every wave is done reading operand tiles
+#pragma unroll
+  for (int b = 0; b < FN; ++b) {
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const int jl = wn * WTN + 32 * b + 8 * grp + 4 * (lane >> 5);
+      const int64_t j = j0 + jl;
+      float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (g.bias_kind != kBiasNone) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (j + t < g.Nc) bias[t] = bias_at(g, j + t, inv_bs);
+      }
+#pragma unroll
+      for (int a = 0; a < FM; ++a) {
+        const int il = wm * WTM + 32 * a + (lane & 31);
+        uint32_t h[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          h[t] = f32_to_bf16(__builtin_fmaf(acc[a][b][4 * grp + t], dq, bias[t]));
+        *reinterpret_cast<uint2*>(smem3 + il * RS + jl * 2) =
+            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+      }
+    }
+  }
+  lds_barrier();
+  constexpr int kChunksPerRow = BN / 8;  // 16-byte chunks of bf16
+  const int64_t rows_left = g.Mc - i0, cols_left = g.Nc - j0;
+#pragma unroll 4
+  for (int q = tid; q < BM * kChunksPerRow; q += 64 * WGM * WGN) {
+    const int r = q / kChunksPerRow, ch = q % kChunksPerRow;
+    if (r < rows_left && 8 * ch < cols_left)
+      *reinterpret_cast<uint4*>(g.c + (i0 + r) * g.ldc + j0 + 8 * ch) =
+          *reinterpret_cast<const uint4*>(smem3 + r * RS + ch * 16);
+  }
+}
+
+}  // namespace fp8l

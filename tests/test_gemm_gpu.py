@@ -7,6 +7,8 @@ codes over the whole finite range, checked against the 2^-7 contract and
 the 2^-10 diagnostic bound.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,6 +18,24 @@ from oracle import fp8_oracle as O
 from tests.gpu_util import (DEV, bf16_bits, check_gemm, f32_scalar, scalar_dev, to_dev)
 
 pytestmark = pytest.mark.gpu
+
+TILES = ["auto", "256x256", "256x128", "128x128", "v1"]
+
+
+@pytest.fixture(params=TILES)
+def tile(request):
+    """Force one GEMM tile configuration (the library reads FP8L_TILE at each
+    launch); shapes the fast kernels cannot take fall back to v1 anyway."""
+    old = os.environ.get("FP8L_TILE")
+    if request.param == "auto":
+        os.environ.pop("FP8L_TILE", None)
+    else:
+        os.environ["FP8L_TILE"] = request.param
+    yield request.param
+    if old is None:
+        os.environ.pop("FP8L_TILE", None)
+    else:
+        os.environ["FP8L_TILE"] = old
 
 INT_CODES = {  # value -> code for 0, +-1, +-2
     O.E4M3: {0: 0x00, 1: 0x38, 2: 0x40, -1: 0xB8, -2: 0xC0},
@@ -71,11 +91,11 @@ def run_dw(g8, fg, x8, fx, sg, sx, with_db=False):
 
 
 SHAPES = [(128, 128, 128), (256, 384, 512), (200, 136, 300), (1, 1, 1), (33, 17, 129),
-          (130, 260, 1000)]
+          (130, 260, 1000), (272, 528, 400), (512, 256, 2064), (48, 80, 16)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
-def test_exact_small_integers_all_three(M, N, K):
+def test_exact_small_integers_all_three(M, N, K, tile):
     rng = np.random.default_rng(M * 7 + N * 3 + K)
     x8 = _int_codes((M, K), O.E4M3, rng)
     w8 = _int_codes((N, K), O.E4M3, rng)
@@ -91,7 +111,7 @@ def test_exact_small_integers_all_three(M, N, K):
 @pytest.mark.parametrize("M,N,K", SHAPES)
 @pytest.mark.parametrize("fa,fb", [(O.E4M3, O.E4M3), (O.E5M2, O.E4M3), (O.E5M2, O.E5M2),
                                    (O.E4M3, O.E5M2)])
-def test_random_codes_tolerance(M, N, K, fa, fb):
+def test_random_codes_tolerance(M, N, K, fa, fb, tile):
     rng = np.random.default_rng(M + N + K + 10 * fa + fb)
     sa, sb = np.float32(37.5), np.float32(0.0625)
     x8 = _rand_codes((M, K), fb, rng)
@@ -105,7 +125,7 @@ def test_random_codes_tolerance(M, N, K, fa, fb):
 
 @pytest.mark.parametrize("bias_kind", ["bf16", "e4m3", "e5m2"])
 @pytest.mark.parametrize("N", [256, 77])
-def test_fused_bias(bias_kind, N):
+def test_fused_bias(bias_kind, N, tile):
     rng = np.random.default_rng(N)
     M, K = 160, 384
     x8 = _rand_codes((M, K), O.E4M3, rng)
@@ -142,7 +162,7 @@ def test_identity_weight_special_case():
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 48, 0), (0, 48, 64), (48, 0, 64)])
-def test_degenerate_sizes(M, N, K):
+def test_degenerate_sizes(M, N, K, tile):
     rng = np.random.default_rng(0)
     x8 = _rand_codes((M, K), O.E4M3, rng)
     w8 = _rand_codes((N, K), O.E4M3, rng)
@@ -158,7 +178,7 @@ def test_degenerate_sizes(M, N, K):
 
 
 @pytest.mark.parametrize("M,N", [(2048, 1536), (100, 40), (37, 300)])
-def test_db_from_prequantized_gradient(M, N):
+def test_db_from_prequantized_gradient(M, N, tile):
     rng = np.random.default_rng(M)
     g8 = _rand_codes((M, N), O.E5M2, rng)
     x8 = _rand_codes((M, 64), O.E4M3, rng)
@@ -167,7 +187,7 @@ def test_db_from_prequantized_gradient(M, N):
     check_gemm(db, O.bias_grad(O.dequantized(g8, O.E5M2, sg)), "db")
 
 
-def test_full_size_sampled_rows():
+def test_full_size_sampled_rows(tile):
     """dim1536/ffn6912 shapes at M = 2048, full GPU outputs, oracle on a
     seeded sample of rows plus the first and last rows."""
     rng = np.random.default_rng(99)
