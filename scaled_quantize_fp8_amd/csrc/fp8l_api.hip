@@ -198,27 +198,15 @@ int forced_tile() {
   return kTileAuto;
 }
 
-// Tile choice: fewest rounds of resident tiles times the tile's work, with
-// the efficiency of smaller tiles discounted (they re-read more operand
-// bytes per MFMA from LDS).
+// Tile choice.  A 256x256 tile (one per CU, 4 waves) moves half the operand
+// bytes per MFMA of a 128x128 tile (two per CU) and runs its K loop closer
+// to the MFMA rate, but it leaves CUs idle when the output has few tiles and
+// it cannot overlap one tile's epilogue with another's loop.  Measured on
+// the layer shapes: 256x256 wins once its tiles fill three quarters of the
+// CUs; below that 128x128 does.
 int choose_tile(int64_t Mc, int64_t Nc) {
-  const int cus = cu_count();
-  struct Cfg { int id, bm, bn, per_cu; double eff; };
-  const Cfg cfgs[3] = {{kTile256x256, 256, 256, 1, 1.0},
-                       {kTile256x128, 256, 128, 1, 0.9},
-                       {kTile128x128, 128, 128, 2, 0.7}};
-  int best = kTile256x256;
-  double best_cost = 1e300;
-  for (const Cfg& c : cfgs) {
-    const double tiles = (double)((Mc + c.bm - 1) / c.bm) * (double)((Nc + c.bn - 1) / c.bn);
-    const double rounds = ceil(tiles / (double)(cus * c.per_cu));
-    const double cost = rounds * c.bm * c.bn / c.eff;
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = c.id;
-    }
-  }
-  return best;
+  const int64_t tiles256 = ((Mc + 255) / 256) * ((Nc + 255) / 256);
+  return 4 * tiles256 >= 3 * (int64_t)cu_count() ? kTile256x256 : kTile128x128;
 }
 
 template <int BM, int BN, int WGM, int WGN, int LA, int LB>

@@ -121,6 +121,17 @@ FP8L_DEV uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two floats to packed bf16 (a in the low half) with one v_cvt_pk_bf16_f32.
+// On gfx950, in the kernels' default FP mode, this instruction gives the
+// same bits as f32_to_bf16 above for every one of the 2^32 float inputs
+// (round to nearest even, NaN kept quiet, subnormals kept); checked
+// exhaustively on the device.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+FP8L_DEV uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // ---------------------------------------------------------------- reductions
 
 // Max of non-negative float bit patterns across a wave of 64 lanes: DPP row

@@ -238,6 +238,17 @@ struct Op3 {
     kstep = (L == kKContig) ? (uint32_t)kBK3 : (uint32_t)(kBK3 * ld);
   }
 
+  // DMA instruction i of K step kt into the step buffer at s.
+  template <int I>
+  FP8L_DEV void issue_one(__amdgpu_buffer_rsrc_t rs, uint8_t* s, int kt) const {
+    const int wave = threadIdx.x >> 6;
+    const int64_t in = (L == kKContig) ? (int64_t)kt * kBK3 + inner[I] : (int64_t)inner[I];
+    const uint32_t off = in < inlim ? base[I] + (uint32_t)kt * kstep : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(s + (wave * kPerWave + I) * 1024), 16, off, 0,
+        0, 0);
+  }
+
   // DMA of K step kt into the step buffer at s (wave-uniform).
   FP8L_DEV void issue(__amdgpu_buffer_rsrc_t rs, uint8_t* s, int kt) const {
     const int wave = threadIdx.x >> 6;
@@ -420,25 +431,54 @@ void gemm3_kernel(GemmArgs g) {
       else wait_vm<0>();
     }
     barrier_only();  // step kt+1 visible to all; step kt's buffer is free
-    if (kt + kStages3 < nk) {
-      oa.issue(ra, step_buf(kt + kStages3), kt + kStages3);
-      ob.issue(rb, step_buf(kt + kStages3) + OA::kBytes, kt + kStages3);
-    }
+    // The DMA of step kt+4 (into the buffer just freed) is spread over the
+    // groups: each load instruction occupies the wave until the load path
+    // accepts it, and issued between groups it overlaps the MFMAs already
+    // in flight instead of stalling them all at once.
+    const bool refill = kt + kStages3 < nk;
+    uint8_t* const sf = step_buf(kt + kStages3);
     static_for<kGroups>([&](auto gi_tag) {
       constexpr int gi = decltype(gi_tag)::value;
-      // group gi issues entries [e0, e0 + n) of the MFMA list
+      // group gi issues entries [e0, e0 + n) of the MFMA list and the DMA
+      // loads j with j * kGroups / kDma == gi
       constexpr int n = kRest / kGroups + (gi < kRest % kGroups ? 1 : 0);
       constexpr int e0 = 2 + gi * (kRest / kGroups) + (gi < kRest % kGroups ? gi : kRest % kGroups);
-      const MfmaSlot m[4] = {slot(CUR, e0), slot(CUR, n > 1 ? e0 + 1 : e0),
-                             slot(CUR, n > 2 ? e0 + 2 : e0), slot(CUR, n > 3 ? e0 + 3 : e0)};
-      const uint8_t* sn = step_buf(kt + 1);
-      if constexpr (gi < FM / 2)
-        OA::template read2_fused<FA, FB, n>(sn, wm * WTM + 64 * gi, fa[NXT][2 * gi],
-                                            fa[NXT][2 * gi + 1], m);
-      else
-        OB::template read2_fused<FA, FB, n>(sn + OA::kBytes, wn * WTN + 64 * (gi - FM / 2),
-                                            fb[NXT][2 * (gi - FM / 2)],
-                                            fb[NXT][2 * (gi - FM / 2) + 1], m);
+      constexpr int j0 = (gi * kDma + kGroups - 1) / kGroups;
+      constexpr int j1 = ((gi + 1) * kDma + kGroups - 1) / kGroups;
+      constexpr int nl = j1 - j0;                  // loads of this group
+      constexpr int nt = nl < n - 1 ? nl : n - 1;  // loads placed between MFMAs
+      auto load = [&](auto j_tag) {
+        constexpr int j = decltype(j_tag)::value;
+        if (refill) {
+          if constexpr (j < OA::kPerWave)
+            oa.template issue_one<j>(ra, sf, kt + kStages3);
+          else
+            ob.template issue_one<j - OA::kPerWave>(rb, sf + OA::kBytes, kt + kStages3);
+        }
+      };
+      // loads that find no MFMA to follow go first
+      static_for<nl - nt>([&](auto t) { load(std::integral_constant<int, j0 + decltype(t)::value>{}); });
+      {
+        constexpr int nf = n - nt;  // MFMAs inside the read block
+        const MfmaSlot m[4] = {slot(CUR, e0), slot(CUR, nf > 1 ? e0 + 1 : e0),
+                               slot(CUR, nf > 2 ? e0 + 2 : e0), slot(CUR, nf > 3 ? e0 + 3 : e0)};
+        const uint8_t* sn = step_buf(kt + 1);
+        if constexpr (gi < FM / 2)
+          OA::template read2_fused<FA, FB, nf>(sn, wm * WTM + 64 * gi, fa[NXT][2 * gi],
+                                               fa[NXT][2 * gi + 1], m);
+        else
+          OB::template read2_fused<FA, FB, nf>(sn + OA::kBytes, wn * WTN + 64 * (gi - FM / 2),
+                                               fb[NXT][2 * (gi - FM / 2)],
+                                               fb[NXT][2 * (gi - FM / 2) + 1], m);
+      }
+      // then each remaining load right after an MFMA issue, in its shadow
+      static_for<nt>([&](auto t) {
+        constexpr int tt = decltype(t)::value;
+        load(std::integral_constant<int, j0 + (nl - nt) + tt>{});
+        const MfmaSlot m1[4] = {slot(CUR, e0 + n - nt + tt), slot(CUR, 0), slot(CUR, 0),
+                                slot(CUR, 0)};
+        mfma_only<FA, FB, 1>(m1);
+      });
     });
   };
 
@@ -477,12 +517,11 @@ void gemm3_kernel(GemmArgs g) {
 #pragma unroll
       for (int a = 0; a < FM; ++a) {
         const int il = wm * WTM + 32 * a + (lane & 31);
-        uint32_t h[4];
+        float v[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          h[t] = f32_to_bf16(__builtin_fmaf(acc[a][b][4 * grp + t], dq, bias[t]));
+        for (int t = 0; t < 4; ++t) v[t] = __builtin_fmaf(acc[a][b][4 * grp + t], dq, bias[t]);
         *reinterpret_cast<uint2*>(smem3 + il * RS + jl * 2) =
-            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
       }
     }
   }
