@@ -42,9 +42,15 @@ def parse():
     p.add_argument("--workload", default="dim1536_m2048")
     p.add_argument("--kernel-reps", type=int, default=20, help="repeats of each isolated kernel timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=25.0,
+                   help="budget of the oracle sample (it stops after the linear that crosses it)")
     p.add_argument("--sweep-tiles", action="store_true",
                    help="time every GEMM of the step under each tile configuration and exit")
+    p.add_argument("--traffic-from", nargs=5, default=None,
+                   metavar=("KIND", "FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                   help="no GPU: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of "
+                        "'--only KIND' and '--only copy' runs into the HBM-traffic record that "
+                        "the roofline entry reads, and exit")
     p.add_argument("--only", default=None,
                    help="profiling aid: run only this kernel class (fwd, dx, dw, quant, copy) "
                         "for --steps iterations and exit")
@@ -126,10 +132,63 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+COPY_BYTES = 256 << 20            # the --only copy calibration moves this much each way
+GEMM_KERNEL_PREFIX = "fp8l::gemm3_kernel<"
+KIND_OPERANDS = {"fwd": ", 0, 0, 0, 0>", "dx": ", 0, 1, 1, 0>"}  # <.., LA, LB, FA, FB>
+
+
+def _pmc_per_dispatch(path, counter):
+    """{dispatch id: (kernel name, counter value in KiB)} from a rocprofv3
+    --pmc CSV (values of one dispatch summed over its rows)."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, v = out.get(d, (r["Kernel_Name"], 0.0))
+            out[d] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def traffic_record(kind, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload):
+    """HBM bytes per launch of the KIND GEMM kernel: FETCH_SIZE and WRITE_SIZE
+    averaged over its dispatches, each scaled by the factor that makes the
+    same counter read COPY_BYTES for the 256 MiB copy of the calibration run."""
+    def per_kernel(path, counter, match):
+        vals = [v for name, v in _pmc_per_dispatch(path, counter).values() if match(name)]
+        if not vals:
+            raise SystemExit(f"{path}: no dispatch of the kernel with {counter}")
+        return sum(vals) / len(vals), len(vals)
+
+    is_gemm = lambda n: n.split("(")[0].strip().replace("void ", "").startswith(
+        GEMM_KERNEL_PREFIX) and n.split("(")[0].rstrip().endswith(KIND_OPERANDS[kind])
+    # the copy: the largest dispatches of the calibration run (torch's copy_)
+    def copy_kib(path, counter):
+        vals = sorted(v for _, v in _pmc_per_dispatch(path, counter).values())
+        return vals[-1]
+    fetch_kib, n_f = per_kernel(fetch_csv, "FETCH_SIZE", is_gemm)
+    write_kib, n_w = per_kernel(write_csv, "WRITE_SIZE", is_gemm)
+    f_scale = COPY_BYTES / (copy_kib(copy_fetch_csv, "FETCH_SIZE") * 1024)
+    w_scale = COPY_BYTES / (copy_kib(copy_write_csv, "WRITE_SIZE") * 1024)
+    rd = fetch_kib * 1024 * f_scale
+    wr = write_kib * 1024 * w_scale
+    return {"kernel_kind": kind, "workload": workload, "kernel_source_hash": kernel_source_hash(),
+            "dispatches": [n_f, n_w], "fetch_kib_raw": fetch_kib, "write_kib_raw": write_kib,
+            "fetch_scale": f_scale, "write_scale": w_scale,
+            "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+            "hbm_bytes_per_launch": rd + wr}
+
+
+def traffic_path(kernel_key: str) -> str:
+    return os.path.join(PROFILE_DIR, f"traffic_{kernel_key}.txt")
+
+
 def load_traffic(kernel_key: str):
     """HBM bytes per launch from the committed PMC summary of this kernel, or
     None if absent or taken on different kernel sources."""
-    path = os.path.join(PROFILE_DIR, f"traffic_{kernel_key}.json")
+    path = traffic_path(kernel_key)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -147,7 +206,7 @@ def cpu_baseline(layers_cpu, budget_s):
 
     from oracle import fp8_oracle as O
 
-    rows = 512
+    rows = layers_cpu[0][0].shape[0]  # every row: one full layer step, if the budget allows
     flops = 0.0
     t0 = time.perf_counter()
     done = 0
@@ -178,6 +237,15 @@ def cpu_baseline(layers_cpu, budget_s):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        kind, *csvs = args.traffic_from
+        rec = traffic_record(kind, *csvs, workload=args.workload)
+        os.makedirs(PROFILE_DIR, exist_ok=True)
+        with open(traffic_path(f"gemm_{kind}_{args.workload}"), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is a design note, not a built path)", file=sys.stderr)

@@ -9,7 +9,13 @@
 // dW; [P3] entries on bf16 output and the forward scale reaching the
 // backward; [P1]/[P4] entries on the fused bias and bias_scale.)
 //
-// gfx950 design (the pages' ldmatrix/cp.async/PRMT kernel is prior art for
+// This file holds the shared GEMM definitions (GemmArgs, layouts, bias and
+// tile helpers) and gemm_kernel, the general-shape kernel: it accepts any
+// sizes, strides and alignments, and runs whenever the pipelined kernel of
+// fp8l_gemm3.hpp cannot (dimensions not multiples of 16, unaligned pointers
+// or leading dimensions, matrices of 2 GiB and more).
+//
+// gemm_kernel (the pages' ldmatrix/cp.async/PRMT kernel is prior art for
 // another machine): a 256-thread block owns a 128x128 C tile and walks K in
 // steps of 128 (one MFMA depth).  Both operands are staged in LDS through a
 // double buffer, one barrier per K step.  A k-contiguous operand tile is

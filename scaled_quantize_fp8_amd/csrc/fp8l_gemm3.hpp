@@ -25,16 +25,54 @@
 //    the LDS transpose ds_read_b64_tr_b8.  16-byte chunks are XOR-swizzled
 //    against bank conflicts on both the DMA writes and the fragment reads.
 //  * Block tile BM x BN by a WGM x WGN grid of waves, each wave a grid of
-//    32x32 MFMA tiles; tiles renumbered XCD-major (see fp8l_gemm2.hpp).
+//    32x32 MFMA tiles; tiles renumbered XCD-major (tile_coords_xcd).
 //  * Epilogue: (1/sa)(1/sb), bias in one fp32 fma, one RNE to bf16, staged
 //    through LDS and written back as whole rows.
 #pragma once
 
 #include <type_traits>
 
-#include "fp8l_gemm2.hpp"
+#include "fp8l_gemm.hpp"
 
 namespace fp8l {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Buffer resource over [p, p + bytes): raw buffer loads past the end return
+// zeros (flags 0x00020000: the gfx9-family resource word 3).
+FP8L_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// LDS write completion, then a workgroup barrier.  Loads still in flight are
+// not waited for; the memory clobber keeps the compiler from moving LDS
+// accesses across it.
+FP8L_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Chunk swizzle of crosswise tiles ([64 k][ROWB bytes]): the two 16-lane
+// groups serviced together by one ds_read_b64_tr_b8 read chunks cc and cc+1
+// (cc even) of the same 8 consecutive k rows; the swizzle keeps bit 0 of
+// the chunk index, so the two groups land on disjoint slots and each
+// group's 8 rows on distinct ones.
+template <int ROWB>
+FP8L_DEV int swz_cross(int kk) {
+  if constexpr (ROWB >= 256)
+    return (kk & 7) << 1;          // 8 rows of 256 B: 16 distinct 16-B slots
+  else
+    return ((kk >> 1) & 3) << 1;   // 128-B rows pair up within a 256-B bank row
+}
+
+// Workgroups are dealt round-robin over the 8 XCDs (block b runs on XCD
+// b % 8).  Renumber so that each XCD gets a contiguous range of tile indices,
+// then walk them in groups of tile rows (tile_coords), so that tiles sharing
+// operand rows or columns share one XCD's L2.
+FP8L_DEV void tile_coords_xcd(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int nb = tiles_m * tiles_n;
+  const int q = nb / 8, r = nb % 8;
+  const int x = b % 8, i = b / 8;
+  const int pid = x * q + min(x, r) + i;
+  tile_coords(pid, tiles_m, tiles_n, tm, tn);
+}
 
 constexpr int kBK3 = 64;
 constexpr int kStages3 = 4;
