@@ -133,8 +133,21 @@ def kernel_source_hash() -> str:
 
 
 COPY_BYTES = 256 << 20            # the --only copy calibration moves this much each way
-GEMM_KERNEL_PREFIX = "fp8l::gemm3_kernel<"
-KIND_OPERANDS = {"fwd": ", 0, 0, 0, 0>", "dx": ", 0, 1, 1, 0>"}  # <.., LA, LB, FA, FB>
+# GEMM kinds by the last four template arguments <.., LA, LB, FA, FB> of the
+# pipelined kernels (gemm3_kernel<BM, BN, WGM, WGN, ...>, gemm4_kernel<...>)
+KIND_OPERANDS = {"fwd": (0, 0, 0, 0), "dx": (0, 1, 1, 0), "dw": (1, 1, 1, 0)}
+
+
+def gemm_kind_of(kernel_name: str):
+    """'fwd' / 'dx' / 'dw' for a pipelined GEMM kernel name, else None."""
+    head = kernel_name.split("(")[0].replace("void ", "").strip()
+    if not (head.startswith("fp8l::gemm3_kernel<") or head.startswith("fp8l::gemm4_kernel<")):
+        return None
+    args = tuple(int(a) for a in head[head.index("<") + 1:head.rindex(">")].split(","))[-4:]
+    for kind, ops in KIND_OPERANDS.items():
+        if args == ops:
+            return kind
+    return None
 
 
 def _pmc_per_dispatch(path, counter):
@@ -162,8 +175,7 @@ def traffic_record(kind, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, w
             raise SystemExit(f"{path}: no dispatch of the kernel with {counter}")
         return sum(vals) / len(vals), len(vals)
 
-    is_gemm = lambda n: n.split("(")[0].strip().replace("void ", "").startswith(
-        GEMM_KERNEL_PREFIX) and n.split("(")[0].rstrip().endswith(KIND_OPERANDS[kind])
+    is_gemm = lambda n: gemm_kind_of(n) == kind
     # the copy: the largest dispatches of the calibration run (torch's copy_)
     def copy_kib(path, counter):
         vals = sorted(v for _, v in _pmc_per_dispatch(path, counter).values())
@@ -277,7 +289,7 @@ def main():
         step()  # seed the rings and fill the quantized operands
         torch.cuda.synchronize()
         res = {}
-        for tile in ("256x256", "256x128", "128x128", "v1"):
+        for tile in ("256x256w8", "256x256", "256x128", "128x128", "v1"):
             os.environ["FP8L_TILE"] = tile
             for L in layers:
                 for gname, fn in (("fwd", L.gemm_fwd), ("dx", L.bwd_dx), ("dw", L.gemm_dw)):
@@ -408,8 +420,10 @@ def main():
     # the roofline entry covers the GEMM kernel with the largest live total
     dom = max(live, key=lambda k: live[k]["total_ms"])
     kernel_names = {
-        "fwd": "gemm3_kernel<.., kKContig, kKContig, E4M3, E4M3> (Y = X8 W8^T, both k-contiguous)",
-        "dx": "gemm3_kernel<.., kKContig, kCross, E5M2, E4M3> (dX = G8 W8, W8 read crosswise)",
+        "fwd": "gemm4_kernel / gemm3_kernel <.., kKContig, kKContig, E4M3, E4M3> "
+               "(Y = X8 W8^T, both operands k-contiguous; tile chosen per shape)",
+        "dx": "gemm4_kernel / gemm3_kernel <.., kKContig, kCross, E5M2, E4M3> "
+              "(dX = G8 W8, W8 read crosswise; tile chosen per shape)",
     }
     achieved = live[dom]["flops"] / (live[dom]["avg_ms"] * 1e-3) / 1e12
     traffic = load_traffic(f"gemm_{dom}_" + args.workload)

@@ -246,6 +246,7 @@ struct Op3 {
   static constexpr int kPerWave = kBlocks / NW;    // DMA instructions per wave per step
   static_assert(kPerWave >= 1 && kBlocks % NW == 0, "tile / wave split");
   static constexpr int kCpr = (L == kKContig) ? 4 : R / 16;  // 16-byte chunks per LDS row
+  static constexpr int kLayout = L;
 
   uint32_t base[kPerWave];  // byte offset of this lane's chunk at step 0
   int32_t inner[kPerWave];  // position along the contiguous dimension (edge mask)

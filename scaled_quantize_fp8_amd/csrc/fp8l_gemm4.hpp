@@ -1,0 +1,264 @@
+// 256x256 FP8 GEMM with two waves per SIMD; same contract and operand
+// layouts as gemm3_kernel (fp8l_gemm3.hpp), whose staging it shares.
+//
+// Why a second 256x256 kernel: on gfx950 an MFMA issue holds its wave until
+// the matrix pipe accepts it, so a wave can queue at most one MFMA ahead.
+// With one wave per SIMD (gemm3's 256x256 tile, 128x128 per wave) every
+// barrier, DMA issue and LDS wait of that wave drains the pipe.  Here 8 waves
+// (2 per SIMD) each own a 128x64 quarter-column, so one wave's MFMAs cover
+// the other's memory work.  That needs at most 256 registers per wave: the
+// 128 accumulators live in AGPRs, and the fragments take 64 VGPRs by
+// single-buffering A (each A fragment is refilled with the next step's data
+// right after the last MFMA that reads it) and double-buffering only B.
+//
+// Per K step (64 bytes) each wave issues 8 MFMAs (4 A fragments x 2 B
+// fragments) and 4 DMA loads; the LDS ring is the 4-deep ring of gemm3.
+// The next step's first two MFMAs are issued in the step's last read block,
+// ahead of the barrier.  For the last step that means one step past K: its
+// DMA is issued like any other and lands as zeros (every offset lies past K),
+// so those MFMAs add exact zeros.
+#pragma once
+
+#include "fp8l_gemm3.hpp"
+
+namespace fp8l {
+
+// One fragment (32 rows x 64 k) read fused with NM MFMAs; k-contiguous tiles
+// take two ds_read_b128, crosswise tiles four ds_read_b64_tr_b8.
+template <int FA, int FB, int NM>
+FP8L_DEV void fused_kc1(const uint32_t ad[2], v8i& n0, const MfmaSlot (&m)[4]) {
+  v4i r0, r1;
+#define FP8L_KC1(n)                                                                  \
+  asm volatile("ds_read_b128 %[r0], %[a0]\n\t"                                       \
+               "ds_read_b128 %[r1], %[a1]\n\t" FP8L_MF##n "s_waitcnt lgkmcnt(0)"     \
+               : [r0] "=&v"(r0), [r1] "=&v"(r1), FP8L_CO##n                          \
+               : [a0] "v"(ad[0]), [a1] "v"(ad[1]), FP8L_CI##n, FP8L_FMT              \
+               : "memory")
+  if constexpr (NM == 1) FP8L_KC1(1);
+  else if constexpr (NM == 2) FP8L_KC1(2);
+  else if constexpr (NM == 3) FP8L_KC1(3);
+  else FP8L_KC1(4);
+#undef FP8L_KC1
+  n0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+}
+
+template <int FA, int FB, int NM>
+FP8L_DEV void fused_x1(const uint32_t ad[4], v8i& n0, const MfmaSlot (&m)[4]) {
+  v2i r0, r1, r2, r3;
+#define FP8L_X1(n)                                                                        \
+  asm volatile("ds_read_b64_tr_b8 %[r0], %[a0]\n\t"                                       \
+               "ds_read_b64_tr_b8 %[r1], %[a1]\n\t"                                       \
+               "ds_read_b64_tr_b8 %[r2], %[a2]\n\t"                                       \
+               "ds_read_b64_tr_b8 %[r3], %[a3]\n\t" FP8L_MF##n "s_waitcnt lgkmcnt(0)"     \
+               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3),          \
+                 FP8L_CO##n                                                               \
+               : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]),      \
+                 FP8L_CI##n, FP8L_FMT                                                     \
+               : "memory")
+  if constexpr (NM == 1) FP8L_X1(1);
+  else if constexpr (NM == 2) FP8L_X1(2);
+  else if constexpr (NM == 3) FP8L_X1(3);
+  else FP8L_X1(4);
+#undef FP8L_X1
+  n0 = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+}
+
+// Read one fragment of operand Op (tile index f) fused with NM MFMAs.
+template <typename Op, int FA, int FB, int NM>
+FP8L_DEV void read1_fused(const uint8_t* s, int f, v8i& n0, const MfmaSlot (&m)[4]) {
+  uint32_t a[8];
+  Op::frag_addrs(s, f, a);  // the first fragment of the pair at f
+  if constexpr (Op::kLayout == kKContig)
+    fused_kc1<FA, FB, NM>(a, n0, m);
+  else
+    fused_x1<FA, FB, NM>(a, n0, m);
+}
+
+template <int LA, int LB, int FA, int FB>
+__global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
+  constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4, NW = WGM * WGN;
+  using OA = Op3<LA, BM, NW>;
+  using OB = Op3<LB, BN, NW>;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;  // 128 x 64 per wave
+  constexpr int FM = WTM / 32, FN = WTN / 32;    // 4 x 2 MFMA tiles
+  static_assert(FM == 4 && FN == 2, "schedule below is written for 4 x 2");
+  constexpr int kStep = OA::kBytes + OB::kBytes;
+  constexpr int kDma = OA::kPerWave + OB::kPerWave;  // 2 + 2
+  static_assert(kDma == 4, "one DMA load after each of the four read groups");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem4[];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int tm, tn;
+  tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
+
+  if (blockIdx.x == 0 && tid == 0) {
+    if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
+    if (g.aux_amax_dst0) *g.aux_amax_dst0 = 0.0f;
+    if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;
+    if (g.aux_amax_dst1) *g.aux_amax_dst1 = 0.0f;
+  }
+  if (g.db && tn == 0 && tid < BM) {
+    const int64_t i = i0 + tid;
+    if (i < g.Mc) {
+      float s = 0.0f;
+      for (int r = 0; r < g.db_R; ++r) s += g.db_ws[(int64_t)r * g.Mc + i];
+      if (g.db_scale) s *= 1.0f / *g.db_scale;
+      g.db[i] = (uint16_t)f32_to_bf16(s);
+    }
+  }
+  const float dq = (1.0f / *g.scale_a) * (1.0f / *g.scale_b);
+  const float inv_bs =
+      (g.bias_kind == kBiasE4M3 || g.bias_kind == kBiasE5M2) ? 1.0f / *g.bias_scale : 1.0f;
+  wait_vm<0>();  // nothing above may count against vmcnt in the loop
+
+  const int64_t a_rows = (LA == kKContig) ? g.Mc : g.Kc;
+  const int64_t b_rows = (LB == kKContig) ? g.Nc : g.Kc;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, (uint32_t)(a_rows * g.lda));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b, (uint32_t)(b_rows * g.ldb));
+  OA oa;
+  OB ob;
+  oa.init(g.lda, i0, g.Mc, g.Kc);
+  ob.init(g.ldb, j0, g.Nc, g.Kc);
+
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int ra0 = wm * WTM, rb0 = wn * WTN;  // this wave's first A row / B column in the tile
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int a = 0; a < FM; ++a)
+#pragma unroll
+    for (int b = 0; b < FN; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+
+  // nk K steps (padded to even); steps 0 .. nk are loaded, step nk being
+  // all zeros (see the header comment)
+  const int nk = (int)(((g.Kc + kBK3 - 1) / kBK3 + 1) & ~1);
+  auto step_buf = [&](int kt) { return smem4 + (kt % kStages3) * kStep; };
+  auto issue_step = [&](int kt) {
+    static_for<OA::kPerWave>([&](auto i) { oa.template issue_one<decltype(i)::value>(ra, step_buf(kt), kt); });
+    static_for<OB::kPerWave>([&](auto i) {
+      ob.template issue_one<decltype(i)::value>(rb, step_buf(kt) + OA::kBytes, kt);
+    });
+  };
+
+  v8i fa[FM], fb[2][FN];
+  auto slot = [&](int a, int b, int buf) { return MfmaSlot{&acc[a][b], &fb[buf][b], &fa[a]}; };
+
+  // prologue: DMA steps 0..3, read step 0, issue its first two MFMAs
+  for (int s = 0; s < kStages3 && s <= nk; ++s) issue_step(s);
+  if (nk > 0) {
+    const int later = min(3, nk);  // steps 1..min(3, nk) may still be in flight
+    if (later >= 3) wait_vm<3 * kDma>();
+    else if (later == 2) wait_vm<2 * kDma>();
+    else wait_vm<kDma>();
+    barrier_only();
+#pragma unroll
+    for (int f = 0; f < FM; f += 2) OA::read2(step_buf(0), ra0 + 32 * f, fa[f], fa[f + 1]);
+    OB::read2(step_buf(0) + OA::kBytes, rb0, fb[0][0], fb[0][1]);
+    const MfmaSlot m[4] = {slot(0, 0, 0), slot(0, 1, 0), slot(0, 0, 0), slot(0, 0, 0)};
+    mfma_only<FA, FB, 2>(m);
+  }
+
+  // Step kt: on entry MFMAs (a0, *) of step kt are issued; fa holds step kt's
+  // A fragments, fb[CUR] its B fragments.
+  auto kstep_body = [&](int kt, auto cur_tag) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    constexpr int NXT = CUR ^ 1;
+    {
+      // step kt+1 landed: later steps kt+2 .. min(kt+3, nk) may be in flight
+      const int later = min(2, nk - kt - 1);
+      if (later >= 2) wait_vm<2 * kDma>();
+      else if (later == 1) wait_vm<kDma>();
+      else wait_vm<0>();
+    }
+    barrier_only();  // step kt+1 visible to all; step kt's buffer is free
+    const bool refill = kt + kStages3 <= nk;
+    uint8_t* const sf = step_buf(kt + kStages3);
+    const uint8_t* const sa = step_buf(kt + 1);
+    const uint8_t* const sb = sa + OA::kBytes;
+    auto load = [&](auto j_tag) {
+      constexpr int j = decltype(j_tag)::value;
+      if (refill) {
+        if constexpr (j < OA::kPerWave)
+          oa.template issue_one<j>(ra, sf, kt + kStages3);
+        else
+          ob.template issue_one<j - OA::kPerWave>(rb, sf + OA::kBytes, kt + kStages3);
+      }
+    };
+    {  // fa[0] <- step kt+1; MFMAs (a1, *)
+      const MfmaSlot m[4] = {slot(1, 0, CUR), slot(1, 1, CUR), slot(1, 0, CUR), slot(1, 0, CUR)};
+      read1_fused<OA, FA, FB, 2>(sa, ra0 + 0, fa[0], m);
+    }
+    load(std::integral_constant<int, 0>{});
+    {  // fa[1] <- step kt+1; MFMAs (a2, *)
+      const MfmaSlot m[4] = {slot(2, 0, CUR), slot(2, 1, CUR), slot(2, 0, CUR), slot(2, 0, CUR)};
+      read1_fused<OA, FA, FB, 2>(sa, ra0 + 32, fa[1], m);
+    }
+    load(std::integral_constant<int, 1>{});
+    {  // fa[2] <- step kt+1; MFMA (a3, b0)
+      const MfmaSlot m[4] = {slot(3, 0, CUR), slot(3, 0, CUR), slot(3, 0, CUR), slot(3, 0, CUR)};
+      read1_fused<OA, FA, FB, 1>(sa, ra0 + 64, fa[2], m);
+    }
+    load(std::integral_constant<int, 2>{});
+    {  // fb[NXT] <- step kt+1; MFMA (a3, b1)
+      const MfmaSlot m[4] = {slot(3, 1, CUR), slot(3, 1, CUR), slot(3, 1, CUR), slot(3, 1, CUR)};
+      OB::template read2_fused<FA, FB, 1>(sb, rb0, fb[NXT][0], fb[NXT][1], m);
+    }
+    load(std::integral_constant<int, 3>{});
+    {  // fa[3] <- step kt+1; MFMAs (a0, *) of step kt+1
+      const MfmaSlot m[4] = {slot(0, 0, NXT), slot(0, 1, NXT), slot(0, 0, NXT), slot(0, 0, NXT)};
+      read1_fused<OA, FA, FB, 2>(sa, ra0 + 96, fa[3], m);
+    }
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    kstep_body(kt, std::integral_constant<int, 0>{});
+    kstep_body(kt + 1, std::integral_constant<int, 1>{});
+  }
+  wait_vm<0>();  // the DMA of step nk (zeros) must not land in the staging area
+
+  // Epilogue as in gemm3_kernel: scale, bias, one packed RNE to bf16, staged
+  // through LDS (rows padded by 16 bytes) and stored as whole rows.
+  constexpr int RS = BN * 2 + 16;
+  mfma_drain();
+  barrier_only();
+#pragma unroll
+  for (int b = 0; b < FN; ++b) {
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const int jl = rb0 + 32 * b + 8 * grp + 4 * (lane >> 5);
+      const int64_t j = j0 + jl;
+      float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (g.bias_kind != kBiasNone) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (j + t < g.Nc) bias[t] = bias_at(g, j + t, inv_bs);
+      }
+#pragma unroll
+      for (int a = 0; a < FM; ++a) {
+        const int il = ra0 + 32 * a + (lane & 31);
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = __builtin_fmaf(acc[a][b][4 * grp + t], dq, bias[t]);
+        *reinterpret_cast<uint2*>(smem4 + il * RS + jl * 2) =
+            make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
+      }
+    }
+  }
+  lds_barrier();
+  constexpr int kChunksPerRow = BN / 8;
+  const int64_t rows_left = g.Mc - i0, cols_left = g.Nc - j0;
+#pragma unroll 4
+  for (int q = tid; q < BM * kChunksPerRow; q += 64 * NW) {
+    const int r = q / kChunksPerRow, ch = q % kChunksPerRow;
+    if (r < rows_left && 8 * ch < cols_left)
+      *reinterpret_cast<uint4*>(g.c + (i0 + r) * g.ldc + j0 + 8 * ch) =
+          *reinterpret_cast<const uint4*>(smem4 + r * RS + ch * 16);
+  }
+}
+
+constexpr int gemm4_lds_bytes() {
+  return kStages3 * 512 * kBK3 > 256 * (256 * 2 + 16) ? kStages3 * 512 * kBK3 : 256 * (256 * 2 + 16);
+}
+
+}  // namespace fp8l
