@@ -138,6 +138,46 @@ void enqueue_quant_t(const void* x, int64_t n, uint8_t* q, fp8_ring_t* ring, flo
   }
 }
 
+// X and W of a forward in one launch (same input type, both rings seeded).
+template <int IN, int FMT>
+void enqueue_quant2_t(const void* x0, int64_t n0, uint8_t* q0, fp8_ring_t* r0, float* su0,
+                      float* am0, const void* x1, int64_t n1, uint8_t* q1, fp8_ring_t* r1,
+                      float* su1, float* am1, hipStream_t st) {
+  auto args = [](const void* x, int64_t n, uint8_t* q, fp8_ring_t* r, float* su, float* am) {
+    QArgs a = {};
+    a.x = x;
+    a.q = q;
+    a.n = n;
+    a.scale_used = su;
+    a.amax_out = am;
+    a.vec_ok = aligned16(x) && aligned16(q);
+    a.ring = reinterpret_cast<RingHdr*>(r->dev);
+    a.hist = reinterpret_cast<float*>(reinterpret_cast<char*>(r->dev) + sizeof(RingHdr));
+    a.hist_len = r->hist_len;
+    return a;
+  };
+  const QArgs a0 = args(x0, n0, q0, r0, su0, am0), a1 = args(x1, n1, q1, r1, su1, am1);
+  const int64_t cap = (int64_t)cu_count() * 8;
+  int64_t b0 = flat_blocks(n0, cap), b1 = flat_blocks(n1, cap);
+  if (b0 + b1 > cap) {  // share the cap in proportion to the sizes
+    b0 = (int64_t)((double)cap * (double)n0 / (double)(n0 + n1));
+    b0 = b0 < 1 ? 1 : (b0 > cap - 1 ? cap - 1 : b0);
+    b1 = cap - b0;
+  }
+  hipLaunchKernelGGL((quantize_flat2_kernel<IN, FMT>), dim3((unsigned)(b0 + b1)), dim3(kQThreads),
+                     0, st, a0, a1, (uint32_t)b0);
+}
+
+template <int IN>
+void enqueue_quant2_in(int32_t fmt, const void* x0, int64_t n0, uint8_t* q0, fp8_ring_t* r0,
+                       float* su0, float* am0, const void* x1, int64_t n1, uint8_t* q1,
+                       fp8_ring_t* r1, float* su1, float* am1, hipStream_t st) {
+  if (fmt == FP8_E4M3)
+    enqueue_quant2_t<IN, kE4M3>(x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st);
+  else
+    enqueue_quant2_t<IN, kE5M2>(x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st);
+}
+
 template <int IN>
 void enqueue_quant_in(const void* x, int64_t n, int32_t fmt, uint8_t* q, fp8_ring_t* ring,
                       float* scale_used, float* amax_out, const ColsumSpec* cs, hipStream_t st) {
@@ -385,8 +425,23 @@ int fp8_linear_fwd(int64_t M, int64_t N, int64_t K, fp8_operand_t x, fp8_operand
   if (M * N > 0 && !y) return FP8_ERR_NULL;
 
   GemmArgs g = {};
+  // steady state of a delayed-scaling forward: X and W in one quantize launch
+  const bool dual = is_hp(x.dtype) && x.dtype == w.dtype && ring_x && ring_w && ring_x->seeded &&
+                    ring_w->seeded && M * K > 0 && N * K > 0;
+  if (dual) {
+    if (x.dtype == FP8_DT_F32)
+      enqueue_quant2_in<kInF32>(fmt, x.data, M * K, x8_out, ring_x, sx_used, amax_x, w.data, N * K,
+                                w8_out, ring_w, sw_used, amax_w, stream);
+    else if (x.dtype == FP8_DT_F16)
+      enqueue_quant2_in<kInF16>(fmt, x.data, M * K, x8_out, ring_x, sx_used, amax_x, w.data, N * K,
+                                w8_out, ring_w, sw_used, amax_w, stream);
+    else
+      enqueue_quant2_in<kInBF16>(fmt, x.data, M * K, x8_out, ring_x, sx_used, amax_x, w.data,
+                                 N * K, w8_out, ring_w, sw_used, amax_w, stream);
+  }
   if (is_hp(x.dtype)) {
-    enqueue_quant(x.data, x.dtype, M * K, fmt, x8_out, ring_x, sx_used, amax_x, nullptr, stream);
+    if (!dual)
+      enqueue_quant(x.data, x.dtype, M * K, fmt, x8_out, ring_x, sx_used, amax_x, nullptr, stream);
     g.a = x8_out;
     g.scale_a = sx_used;
   } else {
@@ -397,7 +452,8 @@ int fp8_linear_fwd(int64_t M, int64_t N, int64_t K, fp8_operand_t x, fp8_operand
     g.aux_amax_dst0 = amax_x;
   }
   if (is_hp(w.dtype)) {
-    enqueue_quant(w.data, w.dtype, N * K, fmt, w8_out, ring_w, sw_used, amax_w, nullptr, stream);
+    if (!dual)
+      enqueue_quant(w.data, w.dtype, N * K, fmt, w8_out, ring_w, sw_used, amax_w, nullptr, stream);
     g.b = w8_out;
     g.scale_b = sw_used;
   } else {

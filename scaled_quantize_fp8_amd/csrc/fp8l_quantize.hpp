@@ -25,6 +25,7 @@
 #pragma once
 
 #include "fp8l_device.hpp"
+#include "fp8linear.h"
 
 namespace fp8l {
 
@@ -141,12 +142,12 @@ FP8L_DEV uint32_t block_max_u32(uint32_t v, uint32_t* sh4) {
   return r;
 }
 
-// Two-level last-block election (thread 0 only).  bm: this block's max |x|
-// bits.  Returns true in the one block that completes last; *amax receives
-// the launch's max.  consume: clear the header max (the last block folds
-// it) or leave it for the next launch (the amax pass of a seeding quantize).
-FP8L_DEV bool elect_last(RingHdr* h, uint32_t bid, uint32_t total, uint32_t bm, bool consume,
-                         uint32_t* amax) {
+// Two-level last-block election (thread 0 only), in two halves so that a
+// block that wins its group can prefetch the window between them.
+// Group level: fold bm (this block's max |x| bits) into the block's group;
+// true in the group's last block, which receives the group max in *gm and
+// leaves the group's counter and max at zero.
+FP8L_DEV bool elect_group(RingHdr* h, uint32_t bid, uint32_t total, uint32_t bm, uint32_t* gm) {
   const uint32_t G = total < (uint32_t)kGroups ? total : (uint32_t)kGroups;
   const uint32_t g = bid % G;
   const uint32_t gsize = (total - g + G - 1) / G;
@@ -155,14 +156,30 @@ FP8L_DEV bool elect_last(RingHdr* h, uint32_t bid, uint32_t total, uint32_t bm, 
   wait_vmem();  // the max is performed before the ticket is taken
   if (atom_add(&grp->count, 1u) != gsize - 1) return false;
   // last block of its group: every block of the group has folded its max
-  const uint32_t gm = atom_xchg(&grp->amax, 0u);
+  *gm = atom_xchg(&grp->amax, 0u);
   atom_xchg(&grp->count, 0u);
+  return true;
+}
+
+// Top level, for group winners: true in the launch's last block, which gets
+// the launch max in *amax.  consume: clear the header max (the last block
+// folds it) or leave it for the next launch (the amax pass of a seeding
+// quantize).
+FP8L_DEV bool elect_top(RingHdr* h, uint32_t total, uint32_t gm, bool consume, uint32_t* amax) {
+  const uint32_t G = total < (uint32_t)kGroups ? total : (uint32_t)kGroups;
   if (gm) atom_max(&h->top_amax, gm);
   wait_vmem();
   if (atom_add(&h->top_count, 1u) != G - 1) return false;
   atom_xchg(&h->top_count, 0u);
   *amax = consume ? atom_xchg(&h->top_amax, 0u) : atom_read(&h->top_amax);
   return true;
+}
+
+FP8L_DEV bool elect_last(RingHdr* h, uint32_t bid, uint32_t total, uint32_t bm, bool consume,
+                         uint32_t* amax) {
+  uint32_t gm = 0;
+  if (!elect_group(h, bid, total, bm, &gm)) return false;
+  return elect_top(h, total, gm, consume, amax);
 }
 
 // Scale the launch quantizes with.
@@ -189,25 +206,46 @@ FP8L_DEV float launch_scale(const QArgs& a) {
 template <int FMT, int SMODE>
 FP8L_DEV void finish_launch(const QArgs& a, uint32_t mx, float s, uint32_t bid, uint32_t total) {
   __shared__ uint32_t sh4[4];
-  __shared__ uint32_t sh_last, sh_amax;
+  __shared__ uint32_t sh_flag, sh_gm, sh_amax;
   if constexpr (SMODE == kScaleDyn) {
     if (bid == 0 && threadIdx.x == 0) *a.scale_used = s;
     return;
   } else {
     const uint32_t bm = block_max_u32(mx, sh4);
     if (threadIdx.x == 0) {
+      uint32_t gm = 0;
+      sh_flag = elect_group(a.ring, bid, total, bm, &gm) ? 1u : 0u;
+      sh_gm = gm;
+    }
+    __syncthreads();
+    if (!sh_flag) return;
+    // A group winner may be the launch's last block: load the window and its
+    // index now, in parallel with the top-level election.  Only the last
+    // block writes them, and only after it has won, so what a winner reads
+    // here is the state the previous launch left.
+    const int H = a.hist_len;
+    uint32_t hv[FP8_RING_MAX_HIST / kQThreads];
+#pragma unroll
+    for (int k = 0; k < FP8_RING_MAX_HIST / kQThreads; ++k) {
+      const int j = threadIdx.x + k * kQThreads;
+      hv[k] = j < H ? __float_as_uint(a.hist[j]) : 0u;
+    }
+    const uint32_t idx = a.ring->idx % (uint32_t)H;  // in range even for a corrupted header
+    __syncthreads();  // every thread has read sh_flag before it is reused
+    if (threadIdx.x == 0) {
       uint32_t am = 0;
-      sh_last = elect_last(a.ring, bid, total, bm, true, &am) ? 1u : 0u;
+      sh_flag = elect_top(a.ring, total, sh_gm, true, &am) ? 1u : 0u;
       sh_amax = am;
     }
     __syncthreads();
-    if (!sh_last) return;
+    if (!sh_flag) return;
     const uint32_t amax_bits = sh_amax;
-    const int H = a.hist_len;
-    const uint32_t idx = a.ring->idx % (uint32_t)H;  // in range even for a corrupted header
     uint32_t m = 0;
-    for (int j = threadIdx.x; j < H; j += kQThreads)
-      m = max(m, (uint32_t)j == idx ? amax_bits : __float_as_uint(a.hist[j]));
+#pragma unroll
+    for (int k = 0; k < FP8_RING_MAX_HIST / kQThreads; ++k) {
+      const int j = threadIdx.x + k * kQThreads;
+      if (j < H) m = max(m, (uint32_t)j == idx ? amax_bits : hv[k]);
+    }
     m = block_max_u32(m, sh4);
     if (threadIdx.x == 0) {
       a.hist[idx] = __uint_as_float(amax_bits);
@@ -221,14 +259,15 @@ FP8L_DEV void finish_launch(const QArgs& a, uint32_t mx, float s, uint32_t bid, 
 }
 
 // Flat quantize.  Lane l of a wave handles elements [c + 8l, +8) and
-// [c + 512 + 8l, +8) of each 1024-element wave chunk c.
+// [c + 512 + 8l, +8) of each 1024-element wave chunk c.  bid / nblk: this
+// block's index among the nblk blocks working on the tensor.
 template <int IN, int FMT, int SMODE>
-__global__ __launch_bounds__(kQThreads) void quantize_flat_kernel(QArgs a) {
+FP8L_DEV void quantize_flat_body(const QArgs& a, uint32_t bid, uint32_t nblk) {
   const float s = launch_scale<FMT, SMODE>(a);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t mx = 0;
-  for (int64_t base = (int64_t)blockIdx.x * kBlockChunk + wave * kWaveChunk; base < a.n;
-       base += (int64_t)gridDim.x * kBlockChunk) {
+  for (int64_t base = (int64_t)bid * kBlockChunk + wave * kWaveChunk; base < a.n;
+       base += (int64_t)nblk * kBlockChunk) {
     const int64_t e0 = base + 8 * lane, e1 = base + 512 + 8 * lane;
     if (a.vec_ok && base + kWaveChunk <= a.n) {
       float v0[8], v1[8];
@@ -251,7 +290,25 @@ __global__ __launch_bounds__(kQThreads) void quantize_flat_kernel(QArgs a) {
         mx = max(mx, quant_scalar8<IN, FMT>(a.x, a.q, e1, (int)min<int64_t>(8, a.n - e1), s, v));
     }
   }
-  finish_launch<FMT, SMODE>(a, mx, s, blockIdx.x, gridDim.x);
+  finish_launch<FMT, SMODE>(a, mx, s, bid, nblk);
+}
+
+template <int IN, int FMT, int SMODE>
+__global__ __launch_bounds__(kQThreads) void quantize_flat_kernel(QArgs a) {
+  quantize_flat_body<IN, FMT, SMODE>(a, blockIdx.x, gridDim.x);
+}
+
+// Two tensors of one input type and format, each with its own seeded ring,
+// in one launch: blocks [0, nblk0) quantize a0, the rest a1.  The forward of
+// a linear layer quantizes X and W this way, so that one tensor's fixed
+// latency (first loads, the election chain) overlaps the other's.
+template <int IN, int FMT>
+__global__ __launch_bounds__(kQThreads) void quantize_flat2_kernel(QArgs a0, QArgs a1,
+                                                                   uint32_t nblk0) {
+  if (blockIdx.x < nblk0)
+    quantize_flat_body<IN, FMT, kScaleRing>(a0, blockIdx.x, nblk0);
+  else
+    quantize_flat_body<IN, FMT, kScaleRing>(a1, blockIdx.x - nblk0, gridDim.x - nblk0);
 }
 
 // Column-sum quantize over x [rows, cols]: block (bx, by) covers columns
