@@ -288,7 +288,7 @@ def main():
         step()  # seed the rings and fill the quantized operands
         torch.cuda.synchronize()
         res = {}
-        for tile in ("256x256w8", "256x256", "256x128", "128x128", "v1"):
+        for tile in ("256x256w8", "128x128w8", "256x256", "256x128", "128x128", "v1"):
             os.environ["FP8L_TILE"] = tile
             for L in layers:
                 for gname, fn in (("fwd", L.gemm_fwd), ("dx", L.bwd_dx), ("dw", L.gemm_dw)):

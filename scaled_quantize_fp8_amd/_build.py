@@ -13,7 +13,7 @@ LIB_NAME = "libfp8linear.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "fp8l_api.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("fp8l_device.hpp", "fp8l_quantize.hpp", "fp8l_gemm.hpp",
-                                                     "fp8l_gemm3.hpp", "fp8l_gemm4.hpp")] + [
+                                                     "fp8l_gemm3.hpp", "fp8l_gemm4.hpp", "fp8l_gemm5.hpp")] + [
     os.path.join(ROOT, "include", "fp8linear.h")
 ]
 

@@ -15,7 +15,7 @@
 #include "../../include/fp8linear.h"
 #include "fp8l_device.hpp"
 #include "fp8l_gemm.hpp"
-#include "fp8l_gemm4.hpp"
+#include "fp8l_gemm5.hpp"
 #include "fp8l_quantize.hpp"
 
 namespace fp8l {
@@ -223,7 +223,7 @@ void launch_gemm3_t(GemmArgs& g, hipStream_t st) {
                      dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(64 * WGM * WGN), lds, st, g);
 }
 
-enum { kTileAuto = 0, kTile256x256, kTile256x128, kTile128x128, kTileV1, kTile256x256w8 };
+enum { kTileAuto = 0, kTile256x256, kTile256x128, kTile128x128, kTileV1, kTile256x256w8, kTile128x128w8 };
 
 // FP8L_TILE forces a tile configuration (for sweeps and tests): 256x256,
 // 256x128, 128x128 or v1 (the general register-staged kernel).  Read at
@@ -236,18 +236,23 @@ int forced_tile() {
   if (!strcmp(e, "128x128")) return kTile128x128;
   if (!strcmp(e, "v1")) return kTileV1;
   if (!strcmp(e, "256x256w8")) return kTile256x256w8;
+  if (!strcmp(e, "128x128w8")) return kTile128x128w8;
   return kTileAuto;
 }
 
-// Tile choice.  A 256x256 tile (one per CU, 8 waves of 128x64, gemm4)
-// moves half the operand bytes per MFMA of a 128x128 tile (4 waves of 64x64,
-// two per CU, gemm3), but leaves CUs idle when the output has few tiles and
-// cannot overlap one tile's epilogue with another's loop.  Measured on the
-// layer shapes: 256x256 wins once its tiles fill half the CUs; below that
-// 128x128 does.
+// Tile choice (measured crossovers on the layer shapes).  Larger tiles move
+// fewer operand bytes per MFMA but leave CUs idle when the output has few
+// tiles, and one tile per CU cannot overlap its epilogue with another loop.
+//  * 256x256, 8 waves (gemm4): when its tiles fill at least half the CUs.
+//  * 128x128, 8 waves (gemm5): when the 128x128 tiles fit one per CU; the
+//    block's 8 waves give each SIMD two waves.
+//  * 128x128, 4 waves, two blocks per CU (gemm3): otherwise.
 int choose_tile(int64_t Mc, int64_t Nc) {
+  const int64_t cus = cu_count();
   const int64_t tiles256 = ((Mc + 255) / 256) * ((Nc + 255) / 256);
-  return 2 * tiles256 >= (int64_t)cu_count() ? kTile256x256w8 : kTile128x128;
+  const int64_t tiles128 = ((Mc + 127) / 128) * ((Nc + 127) / 128);
+  if (2 * tiles256 >= cus) return kTile256x256w8;
+  return tiles128 <= cus ? kTile128x128w8 : kTile128x128;
 }
 
 template <int BM, int BN, int WGM, int WGN, int LA, int LB>
@@ -285,6 +290,33 @@ void launch_gemm4_f(GemmArgs& g, int fa, int fb, hipStream_t st) {
   else launch_gemm4_t<LA, LB, kE5M2, kE5M2>(g, st);
 }
 
+template <int LA, int LB, int FA, int FB>
+void launch_gemm5_t(GemmArgs& g, hipStream_t st) {
+  constexpr int lds = gemm5_lds_bytes();
+  static bool attr_set[64] = {false};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+    (void)hipFuncSetAttribute((const void*)gemm5_kernel<LA, LB, FA, FB>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr_set[dev] = true;
+  }
+  g.tiles_m = (int32_t)((g.Mc + 127) / 128);
+  g.tiles_n = (int32_t)((g.Nc + 127) / 128);
+  if (g.tiles_m < 1) g.tiles_m = 1;
+  if (g.tiles_n < 1) g.tiles_n = 1;
+  hipLaunchKernelGGL((gemm5_kernel<LA, LB, FA, FB>), dim3((unsigned)(g.tiles_m * g.tiles_n)),
+                     dim3(512), lds, st, g);
+}
+
+template <int LA, int LB>
+void launch_gemm5_f(GemmArgs& g, int fa, int fb, hipStream_t st) {
+  if (fa == kE4M3 && fb == kE4M3) launch_gemm5_t<LA, LB, kE4M3, kE4M3>(g, st);
+  else if (fa == kE4M3 && fb == kE5M2) launch_gemm5_t<LA, LB, kE4M3, kE5M2>(g, st);
+  else if (fa == kE5M2 && fb == kE4M3) launch_gemm5_t<LA, LB, kE5M2, kE4M3>(g, st);
+  else launch_gemm5_t<LA, LB, kE5M2, kE5M2>(g, st);
+}
+
 // The fast kernel needs 16-byte chunks that never straddle a matrix edge and
 // byte offsets that fit a buffer descriptor.
 template <int LA, int LB>
@@ -311,6 +343,7 @@ void launch_gemm_l(GemmArgs& g, int fa, int fb, hipStream_t st) {
     case kTile256x128: launch_gemm3_f<256, 128, 2, 2, LA, LB>(g, fa, fb, st); return;
     case kTile128x128: launch_gemm3_f<128, 128, 2, 2, LA, LB>(g, fa, fb, st); return;
     case kTile256x256w8: launch_gemm4_f<LA, LB>(g, fa, fb, st); return;
+    case kTile128x128w8: launch_gemm5_f<LA, LB>(g, fa, fb, st); return;
     default: break;
   }
   if (fa == kE4M3 && fb == kE4M3) launch_gemm_t<LA, LB, kE4M3, kE4M3>(g, st);

@@ -19,7 +19,7 @@ from tests.gpu_util import (DEV, bf16_bits, check_gemm, f32_scalar, scalar_dev, 
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["auto", "256x256w8", "256x256", "256x128", "128x128", "v1"]
+TILES = ["auto", "256x256w8", "128x128w8", "256x256", "256x128", "128x128", "v1"]
 
 
 @pytest.fixture(params=TILES)
