@@ -163,6 +163,27 @@ int fp8_quantize(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, uint8_
                  fp8_ring_t* ring, float* scale_used, float* amax_out, hipStream_t stream);
 
 /*
+ * Two per-tensor quantizes in one call, each exactly as fp8_quantize with
+ * its own input, output, ring, scale_used and amax_out, in one format.  When
+ * both inputs have the same dtype and both rings are seeded, the two are one
+ * kernel launch (a linear layer's X and W: the fixed latency of one tensor's
+ * loads and ring finalize overlaps the other's); otherwise they are enqueued
+ * one after the other.  fp8_linear_fwd uses the same path for a high-precision
+ * X and W ([P1] entry on finalizing scale rings inside the quantize kernels
+ * with no extra launches per linear layer).
+ *
+ *   x0, dtype0, n0, q0, ring0, scale_used0, amax_out0   first tensor
+ *   x1, dtype1, n1, q1, ring1, scale_used1, amax_out1   second tensor
+ *   fmt                                                 format of both
+ * Errors: as fp8_quantize for either tensor; FP8_ERR_RING if both rings are
+ * the same ring.  Nothing is enqueued on error.
+ */
+int fp8_quantize_pair(const void* x0, int32_t dtype0, int64_t n0, uint8_t* q0, fp8_ring_t* ring0,
+                      float* scale_used0, float* amax_out0, const void* x1, int32_t dtype1,
+                      int64_t n1, uint8_t* q1, fp8_ring_t* ring1, float* scale_used1,
+                      float* amax_out1, int32_t fmt, hipStream_t stream);
+
+/*
  * Forward of one FP8 linear layer ([P1] entries on optional ring arguments,
  * pre-quantized w8 with amax_w = 0, and the bias fused into the epilogue
  * with bias_scale; [P4] entry on the bias added in fp32 before the single

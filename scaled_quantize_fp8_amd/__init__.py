@@ -29,7 +29,7 @@ _FMT_DT = {FP8_E4M3: FP8_DT_E4M3, FP8_E5M2: FP8_DT_E5M2}
 
 C_SYMBOLS = (
     "fp8_abi_version", "fp8_status_str", "fp8_ring_bytes", "fp8_ring_init", "fp8_quantize",
-    "fp8_linear_fwd", "fp8_linear_bwd_dx", "fp8_db_workspace_bytes", "fp8_linear_bwd_dw",
+    "fp8_quantize_pair", "fp8_linear_fwd", "fp8_linear_bwd_dx", "fp8_db_workspace_bytes", "fp8_linear_bwd_dw",
 )
 
 
@@ -68,11 +68,14 @@ def lib() -> ctypes.CDLL:
         L.fp8_db_workspace_bytes.argtypes = [i64, i64]
         L.fp8_ring_init.argtypes = [rp, vp, i32, vp]
         L.fp8_quantize.argtypes = [vp, i32, i64, i32, vp, rp, vp, vp, vp]
+        L.fp8_quantize_pair.argtypes = [vp, i32, i64, vp, rp, vp, vp, vp, i32, i64, vp, rp, vp, vp,
+                                        i32, vp]
         L.fp8_linear_fwd.argtypes = [i64, i64, i64, op, op, op, i32, rp, rp, vp, vp, vp, vp, vp, vp,
                                      vp, vp]
         L.fp8_linear_bwd_dx.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp]
         L.fp8_linear_bwd_dw.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp, vp, vp]
-        for name in ("fp8_ring_init", "fp8_quantize", "fp8_linear_fwd", "fp8_linear_bwd_dx",
+        for name in ("fp8_ring_init", "fp8_quantize", "fp8_quantize_pair", "fp8_linear_fwd",
+                     "fp8_linear_bwd_dx",
                      "fp8_linear_bwd_dw"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -168,6 +171,13 @@ def _quantize_args(x, fmt, q, ring, scale_used, amax_out, stream):
             ctypes.c_void_p(_stream(stream)))
 
 
+def _quantize_pair_args(x0, q0, ring0, su0, am0, x1, q1, ring1, su1, am1, fmt, stream):
+    return (_vp(x0), ctypes.c_int32(_TORCH_DT[x0.dtype]), ctypes.c_int64(x0.numel()), _vp(q0),
+            _ring(ring0), _vp(su0), _vp(am0), _vp(x1), ctypes.c_int32(_TORCH_DT[x1.dtype]),
+            ctypes.c_int64(x1.numel()), _vp(q1), _ring(ring1), _vp(su1), _vp(am1),
+            ctypes.c_int32(fmt), ctypes.c_void_p(_stream(stream)))
+
+
 def _fwd_args(x, w, bias, fmt, y, ring_x, ring_w, x8_out, w8_out, sx_used, sw_used, amax_x,
               amax_w, stream):
     xd = x.codes if isinstance(x, Quantized) else x
@@ -215,6 +225,18 @@ def fp8_quantize(x, fmt, q, ring=None, scale_used=None, amax_out=None, stream=No
 
 def bind_fp8_quantize(x, fmt, q, ring=None, scale_used=None, amax_out=None, stream=None):
     return _bind("fp8_quantize", _quantize_args(x, fmt, q, ring, scale_used, amax_out, stream))
+
+
+def fp8_quantize_pair(x0, q0, ring0, su0, am0, x1, q1, ring1, su1, am1, fmt, stream=None):
+    """Two quantizes (x0 -> q0 with ring0, x1 -> q1 with ring1) in one call."""
+    _check(lib().fp8_quantize_pair(*_quantize_pair_args(x0, q0, ring0, su0, am0, x1, q1, ring1,
+                                                        su1, am1, fmt, stream)),
+           "fp8_quantize_pair")
+
+
+def bind_fp8_quantize_pair(x0, q0, ring0, su0, am0, x1, q1, ring1, su1, am1, fmt, stream=None):
+    return _bind("fp8_quantize_pair", _quantize_pair_args(x0, q0, ring0, su0, am0, x1, q1, ring1,
+                                                          su1, am1, fmt, stream))
 
 
 def fp8_linear_fwd(x, w, bias, fmt, y, ring_x=None, ring_w=None, x8_out=None, w8_out=None,

@@ -198,6 +198,25 @@ void enqueue_quant(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, uint
     enqueue_quant_in<kInBF16>(x, n, fmt, q, ring, scale_used, amax_out, cs, st);
 }
 
+// Two quantizes: one launch when the input types match and both rings are
+// seeded (the steady state of delayed scaling), else one after the other.
+void enqueue_quant_pair(const void* x0, int32_t dt0, int64_t n0, uint8_t* q0, fp8_ring_t* r0,
+                        float* su0, float* am0, const void* x1, int32_t dt1, int64_t n1,
+                        uint8_t* q1, fp8_ring_t* r1, float* su1, float* am1, int32_t fmt,
+                        hipStream_t st) {
+  const bool one = dt0 == dt1 && r0 && r1 && r0->seeded && r1->seeded && n0 > 0 && n1 > 0;
+  if (!one) {
+    enqueue_quant(x0, dt0, n0, fmt, q0, r0, su0, am0, nullptr, st);
+    enqueue_quant(x1, dt1, n1, fmt, q1, r1, su1, am1, nullptr, st);
+  } else if (dt0 == FP8_DT_F32) {
+    enqueue_quant2_in<kInF32>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st);
+  } else if (dt0 == FP8_DT_F16) {
+    enqueue_quant2_in<kInF16>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st);
+  } else {
+    enqueue_quant2_in<kInBF16>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st);
+  }
+}
+
 template <int LA, int LB, int FA, int FB>
 void launch_gemm_t(GemmArgs& g, hipStream_t st) {
   hipLaunchKernelGGL((gemm_kernel<LA, LB, FA, FB>), dim3((unsigned)(g.tiles_m * g.tiles_n)),
@@ -409,6 +428,21 @@ int fp8_ring_init(fp8_ring_t* ring, void* dev, int32_t hist_len, hipStream_t str
   return FP8_OK;
 }
 
+int fp8_quantize_pair(const void* x0, int32_t dtype0, int64_t n0, uint8_t* q0, fp8_ring_t* ring0,
+                      float* scale_used0, float* amax_out0, const void* x1, int32_t dtype1,
+                      int64_t n1, uint8_t* q1, fp8_ring_t* ring1, float* scale_used1,
+                      float* amax_out1, int32_t fmt, hipStream_t stream) {
+  int st = check_quant(x0, dtype0, n0, fmt, q0, ring0, scale_used0, amax_out0);
+  if (st) return st;
+  st = check_quant(x1, dtype1, n1, fmt, q1, ring1, scale_used1, amax_out1);
+  if (st) return st;
+  if (!mul_ok(n0, 4) || !mul_ok(n1, 4)) return FP8_ERR_SHAPE;
+  if (ring0 && ring0 == ring1) return FP8_ERR_RING;
+  enqueue_quant_pair(x0, dtype0, n0, q0, ring0, scale_used0, amax_out0, x1, dtype1, n1, q1, ring1,
+                     scale_used1, amax_out1, fmt, stream);
+  return hip_status();
+}
+
 int fp8_quantize(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, uint8_t* q,
                  fp8_ring_t* ring, float* scale_used, float* amax_out, hipStream_t stream) {
   int st = check_quant(x, in_dtype, n, fmt, q, ring, scale_used, amax_out);
@@ -458,22 +492,12 @@ int fp8_linear_fwd(int64_t M, int64_t N, int64_t K, fp8_operand_t x, fp8_operand
   if (M * N > 0 && !y) return FP8_ERR_NULL;
 
   GemmArgs g = {};
-  // steady state of a delayed-scaling forward: X and W in one quantize launch
-  const bool dual = is_hp(x.dtype) && x.dtype == w.dtype && ring_x && ring_w && ring_x->seeded &&
-                    ring_w->seeded && M * K > 0 && N * K > 0;
-  if (dual) {
-    if (x.dtype == FP8_DT_F32)
-      enqueue_quant2_in<kInF32>(fmt, x.data, M * K, x8_out, ring_x, sx_used, amax_x, w.data, N * K,
-                                w8_out, ring_w, sw_used, amax_w, stream);
-    else if (x.dtype == FP8_DT_F16)
-      enqueue_quant2_in<kInF16>(fmt, x.data, M * K, x8_out, ring_x, sx_used, amax_x, w.data, N * K,
-                                w8_out, ring_w, sw_used, amax_w, stream);
-    else
-      enqueue_quant2_in<kInBF16>(fmt, x.data, M * K, x8_out, ring_x, sx_used, amax_x, w.data,
-                                 N * K, w8_out, ring_w, sw_used, amax_w, stream);
-  }
+  if (is_hp(x.dtype) && is_hp(w.dtype))
+    enqueue_quant_pair(x.data, x.dtype, M * K, x8_out, ring_x, sx_used, amax_x, w.data, w.dtype,
+                       N * K, w8_out, ring_w, sw_used, amax_w, fmt, stream);
+  const bool pair = is_hp(x.dtype) && is_hp(w.dtype);
   if (is_hp(x.dtype)) {
-    if (!dual)
+    if (!pair)
       enqueue_quant(x.data, x.dtype, M * K, fmt, x8_out, ring_x, sx_used, amax_x, nullptr, stream);
     g.a = x8_out;
     g.scale_a = sx_used;
@@ -485,7 +509,7 @@ int fp8_linear_fwd(int64_t M, int64_t N, int64_t K, fp8_operand_t x, fp8_operand
     g.aux_amax_dst0 = amax_x;
   }
   if (is_hp(w.dtype)) {
-    if (!dual)
+    if (!pair)
       enqueue_quant(w.data, w.dtype, N * K, fmt, w8_out, ring_w, sw_used, amax_w, nullptr, stream);
     g.b = w8_out;
     g.scale_b = sw_used;

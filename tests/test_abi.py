@@ -30,9 +30,10 @@ def lib():
     return F.lib()
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_every_entry_point():
     names = set(_declared_functions())
-    for must in ("fp8_quantize", "fp8_linear_fwd", "fp8_linear_bwd_dx", "fp8_linear_bwd_dw"):
+    for must in ("fp8_quantize", "fp8_quantize_pair", "fp8_linear_fwd", "fp8_linear_bwd_dx",
+                 "fp8_linear_bwd_dw"):
         assert must in names
     assert names == set(F.C_SYMBOLS)
 
@@ -83,6 +84,24 @@ def test_quantize_validation(lib):
     ring = F._Ring(ctypes.c_void_p(0x100000), 16, 1)
     assert q(P, F.FP8_DT_BF16, 16, F.FP8_E4M3, P, ctypes.byref(ring), P, None, None) == F.FP8_ERR_RING
     assert ring.seeded == 1
+
+
+def test_quantize_pair_validation(lib):
+    qp = lib.fp8_quantize_pair
+    P2 = ctypes.c_void_p(0x200000)
+    bf, e4 = F.FP8_DT_BF16, F.FP8_E4M3
+    ring = F._Ring(ctypes.c_void_p(0x100000), 16, 1)
+    r = ctypes.byref(ring)
+    # one ring for both tensors
+    assert qp(P, bf, 16, P, r, P2, None, P, bf, 16, P, r, P2, None, e4, None) == F.FP8_ERR_RING
+    # second tensor: fp8 input type, NULL scale_used, dynamic without amax_out
+    assert qp(P, bf, 16, P, None, P2, P, P, F.FP8_DT_E5M2, 16, P, None, P2, P, e4,
+              None) == F.FP8_ERR_DTYPE
+    assert qp(P, bf, 16, P, None, P2, P, P, bf, 16, P, None, None, P, e4, None) == F.FP8_ERR_NULL
+    assert qp(P, bf, 16, P, None, P2, P, P, bf, 16, P, None, P2, None, e4, None) == F.FP8_ERR_NULL
+    # bad format, negative size
+    assert qp(P, bf, 16, P, None, P2, P, P, bf, 16, P, None, P2, P, 5, None) == F.FP8_ERR_DTYPE
+    assert qp(P, bf, -3, P, None, P2, P, P, bf, 16, P, None, P2, P, e4, None) == F.FP8_ERR_SHAPE
 
 
 def test_linear_validation(lib):

@@ -203,3 +203,43 @@ def test_full_size_layer_tensors(wl_name):
                 assert s == os_ and a == oa, (wl_name, li, name, step)
                 assert np.array_equal(q, oq.reshape(-1)), (wl_name, li, name, step)
             del xd
+
+
+@pytest.mark.parametrize("dtypes", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.bfloat16)])
+def test_quantize_pair_matches_two_rings(dtypes):
+    """fp8_quantize_pair over several delayed steps: step 0 seeds both rings
+    (two launches); later steps with matching input types run as one launch.
+    Every step matches the oracle for both tensors: bytes, scale_used, amax
+    and ring state."""
+    shapes = ((2048, 1536), (6912, 1536)) if dtypes[0] == dtypes[1] else ((333, 77), (4097, 3))
+    x0 = WL.normal_bf16(shapes[0], 1.0, 21).float()
+    x1 = WL.normal_bf16(shapes[1], 0.02, 22).float()
+    rings = [F.ScaleRing(16), F.ScaleRing(16)]
+    orings = [O.ScaleRing(16), O.ScaleRing(16)]
+    for t, (c0, c1) in enumerate(((1.0, 1.0), (4.0, 0.5), (0.25, 2.0), (1.0, 1.0))):
+        xs = [(x0 * c0).to(dtypes[0]), (x1 * c1).to(dtypes[1])]
+        q = [torch.empty(x.numel(), dtype=torch.uint8, device=DEV) for x in xs]
+        su = [torch.empty(1, dtype=torch.float32, device=DEV) for _ in xs]
+        am = [torch.empty(1, dtype=torch.float32, device=DEV) for _ in xs]
+        xd = [x.to(DEV) for x in xs]
+        F.fp8_quantize_pair(xd[0], q[0], rings[0], su[0], am[0], xd[1], q[1], rings[1], su[1],
+                            am[1], O.E4M3)
+        torch.cuda.synchronize()
+        for i in range(2):
+            oq, os_, oa = O.quantize_step(f32(xs[i]), O.E4M3, orings[i])
+            assert np.array_equal(u8(q[i]), oq.reshape(-1)), (t, i)
+            assert f32_scalar(su[i]).tobytes() == np.float32(os_).tobytes(), (t, i)
+            assert f32_scalar(am[i]).tobytes() == np.float32(oa).tobytes(), (t, i)
+            assert_ring_matches(rings[i], orings[i])
+
+
+def test_quantize_pair_rejects_one_ring_twice():
+    ring = F.ScaleRing(16)
+    x = torch.zeros(64, dtype=torch.bfloat16, device=DEV)
+    q = [torch.empty(64, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    su = [torch.empty(1, dtype=torch.float32, device=DEV) for _ in range(2)]
+    before = ring.buf.clone()
+    with pytest.raises(F.Fp8Error):
+        F.fp8_quantize_pair(x, q[0], ring, su[0], None, x, q[1], ring, su[1], None, O.E4M3)
+    torch.cuda.synchronize()
+    assert torch.equal(ring.buf, before)
