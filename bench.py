@@ -137,14 +137,15 @@ def kernel_source_hash() -> str:
 
 COPY_BYTES = 256 << 20            # the --only copy calibration moves this much each way
 # GEMM kinds by the last four template arguments <.., LA, LB, FA, FB> of the
-# pipelined kernels (gemm3_kernel<BM, BN, WGM, WGN, ...>, gemm4_kernel<...>)
+# pipelined kernels (gemm3_kernel<BM, BN, WGM, WGN, ...>, gemm4_kernel<...>,
+# gemm5_kernel<...>)
 KIND_OPERANDS = {"fwd": (0, 0, 0, 0), "dx": (0, 1, 1, 0), "dw": (1, 1, 1, 0)}
 
 
 def gemm_kind_of(kernel_name: str):
     """'fwd' / 'dx' / 'dw' for a pipelined GEMM kernel name, else None."""
     head = kernel_name.split("(")[0].replace("void ", "").strip()
-    if not (head.startswith("fp8l::gemm3_kernel<") or head.startswith("fp8l::gemm4_kernel<")):
+    if not any(head.startswith(f"fp8l::gemm{v}_kernel<") for v in (3, 4, 5)):
         return None
     args = tuple(int(a) for a in head[head.index("<") + 1:head.rindex(">")].split(","))[-4:]
     for kind, ops in KIND_OPERANDS.items():
@@ -213,7 +214,7 @@ def load_traffic(kernel_key: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(layers_cpu, budget_s):
+def cpu_baseline(layers_cpu, budget_s, min_s=10.0):
     """The oracle (untuned) on a bounded row sample of the same layer: the
     quantizes of X/W/G and the three GEMMs per linear.  Rate in TFLOP/s."""
     import numpy as np
@@ -221,11 +222,12 @@ def cpu_baseline(layers_cpu, budget_s):
 
     from oracle import fp8_oracle as O
 
-    rows = layers_cpu[0][0].shape[0]  # every row: one full layer step, if the budget allows
+    rows = layers_cpu[0][0].shape[0]  # every row: full layer steps, repeated to >= min_s
     flops = 0.0
     t0 = time.perf_counter()
     done = 0
-    for (X, W, b, G) in layers_cpu:
+    order = [layers_cpu[i % len(layers_cpu)] for i in range(64 * len(layers_cpu))]
+    for (X, W, b, G) in order:
         xs = X[:rows].float().numpy()
         gs = G[:rows].float().numpy()
         ws = W.float().numpy()
@@ -240,13 +242,15 @@ def cpu_baseline(layers_cpu, budget_s):
         K, N = X.shape[1], W.shape[0]
         flops += 3 * 2.0 * rows * N * K
         done += 1
-        if time.perf_counter() - t0 > budget_s:
+        el = time.perf_counter() - t0
+        if el > budget_s or (el >= min_s and done % len(layers_cpu) == 0):
             break
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {layers_cpu[0][0].shape[0]} rows of X and G, full W, for "
-                      f"{done} of {len(layers_cpu)} linears: quantize X/W/G (dynamic) + fwd/dX/dW "
+            "sample": f"{rows} of {layers_cpu[0][0].shape[0]} rows of X and G, full W; "
+                      f"{done} linear passes over the layer's {len(layers_cpu)} linears: "
+                      f"quantize X/W/G (dynamic) + fwd/dX/dW "
                       f"GEMMs + db, fp64 accumulation; {dt:.1f} s on {os.cpu_count()} host cpus"}
 
 
