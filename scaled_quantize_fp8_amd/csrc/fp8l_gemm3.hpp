@@ -288,6 +288,38 @@ struct Op3 {
         0, 0);
   }
 
+  // DMA instruction I of K step kt through a buffer resource advanced to
+  // the step (rs_kt: base moved by kt * kstep bytes, record count reduced by
+  // as much and clamped at zero; see step_rsrc), so the per-lane offset is
+  // loop-invariant and the range check still sees every byte.  Only a K step
+  // that reaches past the end of a k-contiguous operand needs per-lane
+  // selects (those bytes lie inside the buffer, in the next row).  wave: this
+  // wave's index, uniform, so the LDS address stays scalar.
+  template <int I>
+  FP8L_DEV void issue_step(__amdgpu_buffer_rsrc_t rs_kt, uint8_t* s, int kt, int wave) const {
+    uint32_t voff;
+    if constexpr (L == kKContig) {
+      // K < 2^31 on this path (the resource's byte count is 32-bit)
+      const int k0 = kt * kBK3, klim = (int)inlim;
+      const int full = __builtin_amdgcn_readfirstlane(k0 + kBK3 <= klim ? 1 : 0);
+      voff = (full || k0 + inner[I] < klim) ? base[I] : 0x80000000u;
+    } else {
+      voff = (int64_t)inner[I] < inlim ? base[I] : 0x80000000u;  // columns past the edge
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs_kt, (__attribute__((address_space(3))) void*)(s + (wave * kPerWave + I) * 1024), 16, voff,
+        0, 0, 0);
+  }
+
+  // Resource over the operand advanced to K step kt (uniform arithmetic).
+  // (readfirstlane: the values are uniform, and saying so keeps the resource
+  // in scalar registers instead of a per-lane loop around each load)
+  FP8L_DEV __amdgpu_buffer_rsrc_t step_rsrc(const uint8_t* p, uint32_t bytes, int kt) const {
+    const uint32_t adv = __builtin_amdgcn_readfirstlane((uint32_t)kt * kstep);
+    const uint32_t n = __builtin_amdgcn_readfirstlane(adv < bytes ? bytes - adv : 0u);
+    return make_rsrc(p + adv, n);
+  }
+
   // DMA of K step kt into the step buffer at s (wave-uniform).
   FP8L_DEV void issue(__amdgpu_buffer_rsrc_t rs, uint8_t* s, int kt) const {
     const int wave = threadIdx.x >> 6;

@@ -74,6 +74,114 @@ FP8L_DEV void read1_fused(const uint8_t* s, int f, v8i& n0, const MfmaSlot (&m)[
     fused_x1<FA, FB, NM>(a, n0, m);
 }
 
+// Fragment reads addressed with the instruction's immediate offset, so a
+// step needs one or two address registers per operand.  A k-contiguous
+// fragment 32 rows further lies exactly 2048 bytes further (the chunk
+// swizzle repeats every 4 rows); the four 8-row reads of a crosswise
+// fragment lie 8 R bytes apart (the swizzle repeats every 8 k rows).
+#define FP8L_RKC(r, a, o) "ds_read_b128 %[" #r "], %[" #a "] offset:%[" #o "]\n\t"
+#define FP8L_RX(r, a, o) "ds_read_b64_tr_b8 %[" #r "], %[" #a "] offset:%[" #o "]\n\t"
+
+// k-contiguous fragment at offset OFF from the lane addresses a0, a1
+template <int FA, int FB, int NM, int OFF>
+FP8L_DEV void kc1o(uint32_t a0, uint32_t a1, v8i& n0, const MfmaSlot (&m)[4]) {
+  v4i r0, r1;
+#define FP8L_KC1O(n)                                                                      \
+  asm volatile(FP8L_RKC(r0, a0, o0) FP8L_RKC(r1, a1, o0) FP8L_MF##n "s_waitcnt lgkmcnt(0)" \
+               : [r0] "=&v"(r0), [r1] "=&v"(r1), FP8L_CO##n                                \
+               : [a0] "v"(a0), [a1] "v"(a1), [o0] "n"(OFF), FP8L_CI##n, FP8L_FMT           \
+               : "memory")
+  if constexpr (NM == 1) FP8L_KC1O(1);
+  else if constexpr (NM == 2) FP8L_KC1O(2);
+  else if constexpr (NM == 3) FP8L_KC1O(3);
+  else FP8L_KC1O(4);
+#undef FP8L_KC1O
+  n0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+}
+
+// k-contiguous fragment pair at offsets 0 and 2048
+template <int FA, int FB, int NM>
+FP8L_DEV void kc2o(uint32_t a0, uint32_t a1, v8i& n0, v8i& n1, const MfmaSlot (&m)[4]) {
+  v4i r0, r1, r2, r3;
+#define FP8L_KC2O(n)                                                                           \
+  asm volatile(FP8L_RKC(r0, a0, o0) FP8L_RKC(r1, a1, o0) FP8L_RKC(r2, a0, o1)                  \
+                   FP8L_RKC(r3, a1, o1) FP8L_MF##n "s_waitcnt lgkmcnt(0)"                      \
+               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3), FP8L_CO##n     \
+               : [a0] "v"(a0), [a1] "v"(a1), [o0] "n"(0), [o1] "n"(2048), FP8L_CI##n, FP8L_FMT \
+               : "memory")
+  if constexpr (NM == 1) FP8L_KC2O(1);
+  else if constexpr (NM == 2) FP8L_KC2O(2);
+  else if constexpr (NM == 3) FP8L_KC2O(3);
+  else FP8L_KC2O(4);
+#undef FP8L_KC2O
+  n0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  n1 = v8i{r2.x, r2.y, r2.z, r2.w, r3.x, r3.y, r3.z, r3.w};
+}
+
+// crosswise fragment from base b: reads at b + t * DT, t = 0..3
+template <int FA, int FB, int NM, int DT>
+FP8L_DEV void x1o(uint32_t b, v8i& n0, const MfmaSlot (&m)[4]) {
+  v2i r0, r1, r2, r3;
+#define FP8L_X1O(n)                                                                            \
+  asm volatile(FP8L_RX(r0, p0, o0) FP8L_RX(r1, p0, o1) FP8L_RX(r2, p0, o2) FP8L_RX(r3, p0, o3) \
+                   FP8L_MF##n "s_waitcnt lgkmcnt(0)"                                           \
+               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3), FP8L_CO##n     \
+               : [p0] "v"(b), [o0] "n"(0), [o1] "n"(DT), [o2] "n"(2 * DT), [o3] "n"(3 * DT),     \
+                 FP8L_CI##n, FP8L_FMT                                                          \
+               : "memory")
+  if constexpr (NM == 1) FP8L_X1O(1);
+  else if constexpr (NM == 2) FP8L_X1O(2);
+  else if constexpr (NM == 3) FP8L_X1O(3);
+  else FP8L_X1O(4);
+#undef FP8L_X1O
+  n0 = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+}
+
+// crosswise fragment pair from bases b0, b1
+template <int FA, int FB, int NM, int DT>
+FP8L_DEV void x2o(uint32_t b0, uint32_t b1, v8i& n0, v8i& n1, const MfmaSlot (&m)[4]) {
+  v2i r0, r1, r2, r3, r4, r5, r6, r7;
+#define FP8L_X2O(n)                                                                             \
+  asm volatile(FP8L_RX(r0, p0, o0) FP8L_RX(r1, p0, o1) FP8L_RX(r2, p0, o2) FP8L_RX(r3, p0, o3)  \
+                   FP8L_RX(r4, p1, o0) FP8L_RX(r5, p1, o1) FP8L_RX(r6, p1, o2)                  \
+                       FP8L_RX(r7, p1, o3) FP8L_MF##n "s_waitcnt lgkmcnt(0)"                    \
+               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3), [r4] "=&v"(r4), \
+                 [r5] "=&v"(r5), [r6] "=&v"(r6), [r7] "=&v"(r7), FP8L_CO##n                     \
+               : [p0] "v"(b0), [p1] "v"(b1), [o0] "n"(0), [o1] "n"(DT), [o2] "n"(2 * DT),        \
+                 [o3] "n"(3 * DT), FP8L_CI##n, FP8L_FMT                                         \
+               : "memory")
+  if constexpr (NM == 1) FP8L_X2O(1);
+  else if constexpr (NM == 2) FP8L_X2O(2);
+  else if constexpr (NM == 3) FP8L_X2O(3);
+  else FP8L_X2O(4);
+#undef FP8L_X2O
+  n0 = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+  n1 = v8i{r4.x, r4.y, r5.x, r5.y, r6.x, r6.y, r7.x, r7.y};
+}
+
+// Lane address registers of one operand's fragments in the stage-0 buffer
+// (add a stage's byte offset to use them for that stage).  k-contiguous:
+// the two chunk addresses of fragment f0 (fragment f0 + 32 i is at offset
+// 2048 i).  Crosswise: one base per fragment f0 + 32 i, i < NF.
+template <typename Op, int NF>
+struct FragBase {
+  uint32_t a[(Op::kLayout == kKContig) ? 2 : NF];
+  FP8L_DEV void init(const uint8_t* s0, int f0) {
+    uint32_t t[8];
+    if constexpr (Op::kLayout == kKContig) {
+      Op::frag_addrs(s0, f0, t);
+      a[0] = t[0];
+      a[1] = t[1];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        Op::frag_addrs(s0, f0 + 32 * i, t);
+        a[i] = t[0];
+      }
+    }
+  }
+};
+
 template <int LA, int LB, int FA, int FB>
 __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4, NW = WGM * WGN;
@@ -114,15 +222,19 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
 
   const int64_t a_rows = (LA == kKContig) ? g.Mc : g.Kc;
   const int64_t b_rows = (LB == kKContig) ? g.Nc : g.Kc;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, (uint32_t)(a_rows * g.lda));
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(g.b, (uint32_t)(b_rows * g.ldb));
+  const uint32_t a_bytes = (uint32_t)(a_rows * g.lda), b_bytes = (uint32_t)(b_rows * g.ldb);
   OA oa;
   OB ob;
   oa.init(g.lda, i0, g.Mc, g.Kc);
   ob.init(g.ldb, j0, g.Nc, g.Kc);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // uniform wave index
 
   const int wm = wave / WGN, wn = wave % WGN;
   const int ra0 = wm * WTM, rb0 = wn * WTN;  // this wave's first A row / B column in the tile
+  FragBase<OA, FM> fra;
+  FragBase<OB, FN> frb;
+  fra.init(smem4, ra0);
+  frb.init(smem4 + OA::kBytes, rb0);
   v16f acc[FM][FN];
 #pragma unroll
   for (int a = 0; a < FM; ++a)
@@ -136,9 +248,13 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   const int nk = (int)(((g.Kc + kBK3 - 1) / kBK3 + 1) & ~1);
   auto step_buf = [&](int kt) { return smem4 + (kt % kStages3) * kStep; };
   auto issue_step = [&](int kt) {
-    static_for<OA::kPerWave>([&](auto i) { oa.template issue_one<decltype(i)::value>(ra, step_buf(kt), kt); });
+    const __amdgpu_buffer_rsrc_t ra_k = oa.step_rsrc(g.a, a_bytes, kt);
+    const __amdgpu_buffer_rsrc_t rb_k = ob.step_rsrc(g.b, b_bytes, kt);
+    static_for<OA::kPerWave>([&](auto i) {
+      oa.template issue_step<decltype(i)::value>(ra_k, step_buf(kt), kt, wv);
+    });
     static_for<OB::kPerWave>([&](auto i) {
-      ob.template issue_one<decltype(i)::value>(rb, step_buf(kt) + OA::kBytes, kt);
+      ob.template issue_step<decltype(i)::value>(rb_k, step_buf(kt) + OA::kBytes, kt, wv);
     });
   };
 
@@ -174,41 +290,59 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
     }
     barrier_only();  // step kt+1 visible to all; step kt's buffer is free
     const bool refill = kt + kStages3 <= nk;
-    uint8_t* const sf = step_buf(kt + kStages3);
-    const uint8_t* const sa = step_buf(kt + 1);
-    const uint8_t* const sb = sa + OA::kBytes;
+    const int kf = kt + kStages3;
+    uint8_t* const sf = step_buf(kf);
+    const __amdgpu_buffer_rsrc_t ra_k = oa.step_rsrc(g.a, a_bytes, kf);
+    const __amdgpu_buffer_rsrc_t rb_k = ob.step_rsrc(g.b, b_bytes, kf);
     auto load = [&](auto j_tag) {
       constexpr int j = decltype(j_tag)::value;
       if (refill) {
         if constexpr (j < OA::kPerWave)
-          oa.template issue_one<j>(ra, sf, kt + kStages3);
+          oa.template issue_step<j>(ra_k, sf, kf, wv);
         else
-          ob.template issue_one<j - OA::kPerWave>(rb, sf + OA::kBytes, kt + kStages3);
+          ob.template issue_step<j - OA::kPerWave>(rb_k, sf + OA::kBytes, kf, wv);
       }
     };
+    // this step's fragment addresses: the stage-0 lane addresses plus the
+    // byte offset of step kt+1's stage
+    const uint32_t d = (uint32_t)(((kt + 1) % kStages3) * kStep);
+    auto readA = [&](auto i_tag, v8i& dst, const MfmaSlot (&m)[4], auto nm_tag) {
+      constexpr int i = decltype(i_tag)::value, NM = decltype(nm_tag)::value;
+      if constexpr (LA == kKContig)
+        kc1o<FA, FB, NM, 2048 * i>(fra.a[0] + d, fra.a[1] + d, dst, m);
+      else
+        x1o<FA, FB, NM, 8 * BM>(fra.a[i] + d, dst, m);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
     {  // fa[0] <- step kt+1; MFMAs (a1, *)
       const MfmaSlot m[4] = {slot(1, 0, CUR), slot(1, 1, CUR), slot(1, 0, CUR), slot(1, 0, CUR)};
-      read1_fused<OA, FA, FB, 2>(sa, ra0 + 0, fa[0], m);
+      readA(I0{}, fa[0], m, I2{});
     }
-    load(std::integral_constant<int, 0>{});
+    load(I0{});
     {  // fa[1] <- step kt+1; MFMAs (a2, *)
       const MfmaSlot m[4] = {slot(2, 0, CUR), slot(2, 1, CUR), slot(2, 0, CUR), slot(2, 0, CUR)};
-      read1_fused<OA, FA, FB, 2>(sa, ra0 + 32, fa[1], m);
+      readA(I1{}, fa[1], m, I2{});
     }
-    load(std::integral_constant<int, 1>{});
+    load(I1{});
     {  // fa[2] <- step kt+1; MFMA (a3, b0)
       const MfmaSlot m[4] = {slot(3, 0, CUR), slot(3, 0, CUR), slot(3, 0, CUR), slot(3, 0, CUR)};
-      read1_fused<OA, FA, FB, 1>(sa, ra0 + 64, fa[2], m);
+      readA(I2{}, fa[2], m, I1{});
     }
-    load(std::integral_constant<int, 2>{});
+    load(I2{});
     {  // fb[NXT] <- step kt+1; MFMA (a3, b1)
       const MfmaSlot m[4] = {slot(3, 1, CUR), slot(3, 1, CUR), slot(3, 1, CUR), slot(3, 1, CUR)};
-      OB::template read2_fused<FA, FB, 1>(sb, rb0, fb[NXT][0], fb[NXT][1], m);
+      if constexpr (LB == kKContig)
+        kc2o<FA, FB, 1>(frb.a[0] + d, frb.a[1] + d, fb[NXT][0], fb[NXT][1], m);
+      else
+        x2o<FA, FB, 1, 8 * BN>(frb.a[0] + d, frb.a[1] + d, fb[NXT][0], fb[NXT][1], m);
     }
-    load(std::integral_constant<int, 3>{});
+    load(I3{});
     {  // fa[3] <- step kt+1; MFMAs (a0, *) of step kt+1
       const MfmaSlot m[4] = {slot(0, 0, NXT), slot(0, 1, NXT), slot(0, 0, NXT), slot(0, 0, NXT)};
-      read1_fused<OA, FA, FB, 2>(sa, ra0 + 96, fa[3], m);
+      readA(I3{}, fa[3], m, I2{});
     }
   };
   for (int kt = 0; kt < nk; kt += 2) {
