@@ -37,6 +37,7 @@
 namespace fp8l {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // Buffer resource over [p, p + bytes): raw buffer loads past the end return
 // zeros (flags 0x00020000: the gfx9-family resource word 3).
@@ -603,8 +604,8 @@ void gemm3_kernel(GemmArgs g) {
   for (int q = tid; q < BM * kChunksPerRow; q += 64 * WGM * WGN) {
     const int r = q / kChunksPerRow, ch = q % kChunksPerRow;
     if (r < rows_left && 8 * ch < cols_left)
-      *reinterpret_cast<uint4*>(g.c + (i0 + r) * g.ldc + j0 + 8 * ch) =
-          *reinterpret_cast<const uint4*>(smem3 + r * RS + ch * 16);
+      __builtin_nontemporal_store(*reinterpret_cast<const v4u*>(smem3 + r * RS + ch * 16),
+                                  reinterpret_cast<v4u*>(g.c + (i0 + r) * g.ldc + j0 + 8 * ch));
   }
 }
 

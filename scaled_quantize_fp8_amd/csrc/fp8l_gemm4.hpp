@@ -386,8 +386,8 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   for (int q = tid; q < BM * kChunksPerRow; q += 64 * NW) {
     const int r = q / kChunksPerRow, ch = q % kChunksPerRow;
     if (r < rows_left && 8 * ch < cols_left)
-      *reinterpret_cast<uint4*>(g.c + (i0 + r) * g.ldc + j0 + 8 * ch) =
-          *reinterpret_cast<const uint4*>(smem4 + r * RS + ch * 16);
+      __builtin_nontemporal_store(*reinterpret_cast<const v4u*>(smem4 + r * RS + ch * 16),
+                                  reinterpret_cast<v4u*>(g.c + (i0 + r) * g.ldc + j0 + 8 * ch));
   }
 }
 
