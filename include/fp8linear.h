@@ -258,6 +258,44 @@ int fp8_linear_bwd_dw(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t 
                       fp8_ring_t* ring_g, fp8_operand_t x8, void* dw, void* db, float* db_ws,
                       uint8_t* g8_out, float* sg_used, float* amax_g, hipStream_t stream);
 
+/* Storage of a GEMM operand, with its contraction index k ([P4] entry on 3D
+ * operands and transposed views folding into the layout tag):
+ *   FP8_K_CONTIG   element (r, k) at p[r * ld + k]  (rows of k-contiguous codes)
+ *   FP8_K_STRIDED  element (r, k) at p[k * ld + r]  (the transposed view of such
+ *                  rows; read through the LDS transpose, no copy) */
+typedef enum { FP8_K_CONTIG = 0, FP8_K_STRIDED = 1 } fp8_layout_t;
+
+/*
+ * Batched FP8 GEMM on pre-quantized operands ([P4] entry on the fp8 matmul
+ * accepting 3D operands: batch slices by stride, size-1 batches broadcast
+ * with stride 0, transposed views as a layout tag; [P4] entry on the bias
+ * added in fp32 before the single bf16 rounding).  For z < batch:
+ *
+ *   C_z[i, j] = RNE_bf16( sum_k A_z(i, k) B_z(j, k) / (sa sb) + bias[j] ),
+ *
+ * fp32 accumulation, i < M, j < N, k < K.
+ *
+ *   a         fp8 codes (E4M3 or E5M2) with their device scale sa; A_z is the
+ *             M x K operand at a.data + z * stride_a in layout layout_a with
+ *             leading dimension lda (>= K for FP8_K_CONTIG, >= M otherwise).
+ *   b         likewise, N x K, with layout_b, ldb, stride_b and scale sb.
+ *   stride_a, stride_b   elements between batch slices; 0 broadcasts one
+ *             slice to every z.
+ *   bias      [N]: data NULL = none; BF16; or fp8 codes with scale =
+ *             bias_scale (dec(b8)/bias_scale).  The same for every slice.
+ *   c         bf16 out: C_z at c + z * stride_c, leading dimension ldc >= N;
+ *             when batch > 1, stride_c >= (M - 1) * ldc + N (slices must not
+ *             overlap).
+ * Errors: FP8_ERR_SHAPE (a negative size, a leading dimension or stride too
+ * small, a byte count overflowing int64, batch > 65535), FP8_ERR_DTYPE (a
+ * non-fp8 operand, an unknown layout, a bad bias dtype), FP8_ERR_NULL (a
+ * missing pointer or scale).  Nothing is enqueued on error.
+ */
+int fp8_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, fp8_operand_t a, int32_t layout_a,
+             int64_t lda, int64_t stride_a, fp8_operand_t b, int32_t layout_b, int64_t ldb,
+             int64_t stride_b, fp8_operand_t bias, void* c, int64_t ldc, int64_t stride_c,
+             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

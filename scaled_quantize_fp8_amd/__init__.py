@@ -23,13 +23,15 @@ from ._build import LIB_PATH
 FP8_E4M3, FP8_E5M2 = 0, 1
 FP8_DT_F32, FP8_DT_F16, FP8_DT_BF16, FP8_DT_E4M3, FP8_DT_E5M2 = 0, 1, 2, 3, 4
 FP8_OK, FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_DTYPE, FP8_ERR_RING, FP8_ERR_HIP = range(6)
+FP8_K_CONTIG, FP8_K_STRIDED = 0, 1
 
 _TORCH_DT = {torch.float32: FP8_DT_F32, torch.float16: FP8_DT_F16, torch.bfloat16: FP8_DT_BF16}
 _FMT_DT = {FP8_E4M3: FP8_DT_E4M3, FP8_E5M2: FP8_DT_E5M2}
 
 C_SYMBOLS = (
     "fp8_abi_version", "fp8_status_str", "fp8_ring_bytes", "fp8_ring_init", "fp8_quantize",
-    "fp8_quantize_pair", "fp8_linear_fwd", "fp8_linear_bwd_dx", "fp8_db_workspace_bytes", "fp8_linear_bwd_dw",
+    "fp8_quantize_pair", "fp8_linear_fwd", "fp8_linear_bwd_dx", "fp8_db_workspace_bytes",
+    "fp8_linear_bwd_dw", "fp8_gemm",
 )
 
 
@@ -74,8 +76,10 @@ def lib() -> ctypes.CDLL:
                                      vp, vp]
         L.fp8_linear_bwd_dx.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp]
         L.fp8_linear_bwd_dw.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp, vp, vp]
+        L.fp8_gemm.argtypes = [i64, i64, i64, i64, op, i32, i64, i64, op, i32, i64, i64, op, vp,
+                               i64, i64, vp]
         for name in ("fp8_ring_init", "fp8_quantize", "fp8_quantize_pair", "fp8_linear_fwd",
-                     "fp8_linear_bwd_dx",
+                     "fp8_gemm", "fp8_linear_bwd_dx",
                      "fp8_linear_bwd_dw"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -276,3 +280,53 @@ def bind_fp8_linear_bwd_dw(g, fmt_g, x8, dw, db=None, db_ws=None, ring_g=None, g
                            sg_used=None, amax_g=None, stream=None):
     return _bind("fp8_linear_bwd_dw", _dw_args(g, fmt_g, x8, dw, db, db_ws, ring_g, g8_out,
                                                sg_used, amax_g, stream))
+
+
+def _matrix_view(t, what):
+    """(batch, rows, cols, batch_stride, layout, ld) of a 2-D or 3-D tensor
+    whose last two dims are (rows, k): k-contiguous rows, or the transposed
+    view of such rows (k strided).  A batch dim of size 1 or stride 0 is
+    broadcast."""
+    if t.dim() == 2:
+        t3, bstride = t.unsqueeze(0), 0
+    elif t.dim() == 3:
+        t3, bstride = t, (0 if t.shape[0] == 1 else t.stride(0))
+    else:
+        raise ValueError(f"{what}: expected a 2-D or 3-D tensor")
+    B, R, Kd = t3.shape
+    if t3.stride(2) == 1 or Kd <= 1:
+        return B, R, Kd, bstride, FP8_K_CONTIG, max(t3.stride(1), Kd, 1)
+    if t3.stride(1) == 1 or R <= 1:
+        return B, R, Kd, bstride, FP8_K_STRIDED, max(t3.stride(2), R, 1)
+    raise ValueError(f"{what}: neither dim of the matrix is contiguous")
+
+
+def _gemm_args(a, b, c, bias, stream):
+    Ba, M, K, sa, la, lda = _matrix_view(a.codes, "a")
+    Bb, N, Kb, sb, lb, ldb = _matrix_view(b.codes, "b")
+    if K != Kb:
+        raise ValueError("a and b disagree on K")
+    batch = max(Ba, Bb)
+    if Ba not in (1, batch) or Bb not in (1, batch):
+        raise ValueError("batch sizes do not broadcast")
+    c3 = c if c.dim() == 3 else c.unsqueeze(0)
+    if tuple(c3.shape) != (batch, M, N) or c3.stride(2) != 1:
+        raise ValueError("c must be [batch, M, N] (or [M, N]) with contiguous rows")
+    return (ctypes.c_int64(batch), ctypes.c_int64(M), ctypes.c_int64(N), ctypes.c_int64(K),
+            _operand(a), ctypes.c_int32(la), ctypes.c_int64(lda), ctypes.c_int64(sa),
+            _operand(b), ctypes.c_int32(lb), ctypes.c_int64(ldb), ctypes.c_int64(sb),
+            _operand(bias), _vp(c), ctypes.c_int64(max(c3.stride(1), N)),
+            ctypes.c_int64(c3.stride(0) if batch > 1 else 0), ctypes.c_void_p(_stream(stream)))
+
+
+def fp8_gemm(a, b, c, bias=None, stream=None):
+    """c[z] = a[z] b[z]^T / (sa sb) (+ bias), bf16.  a: Quantized with codes
+    [.., M, K]; b: Quantized with codes [.., N, K]; either may be a transposed
+    view (.mT of a [.., K, M] buffer) and either may be 2-D or have batch 1
+    (broadcast).  c: bf16 [.., M, N]."""
+    _check(lib().fp8_gemm(*_gemm_args(a, b, c, bias, stream)), "fp8_gemm")
+
+
+def bind_fp8_gemm(a, b, c, bias=None, stream=None):
+    return _bind("fp8_gemm", _gemm_args(a, b, c, bias, stream))
+

@@ -41,6 +41,7 @@ bool is_f8(int32_t dt) { return dt == FP8_DT_E4M3 || dt == FP8_DT_E5M2; }
 bool valid_fmt(int32_t f) { return f == FP8_E4M3 || f == FP8_E5M2; }
 int32_t fmt_dtype(int32_t f) { return f == FP8_E4M3 ? FP8_DT_E4M3 : FP8_DT_E5M2; }
 int dtype_fmt(int32_t dt) { return dt == FP8_DT_E4M3 ? kE4M3 : kE5M2; }
+bool is_fp8_dtype(int32_t dt) { return dt == FP8_DT_E4M3 || dt == FP8_DT_E5M2; }
 
 // a * b fits in int64 (a, b >= 0)
 bool mul_ok(int64_t a, int64_t b) { return a == 0 || b <= INT64_MAX / 4 / a; }
@@ -219,8 +220,9 @@ void enqueue_quant_pair(const void* x0, int32_t dt0, int64_t n0, uint8_t* q0, fp
 
 template <int LA, int LB, int FA, int FB>
 void launch_gemm_t(GemmArgs& g, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<LA, LB, FA, FB>), dim3((unsigned)(g.tiles_m * g.tiles_n)),
-                     dim3(kGThreads), 0, st, g);
+  hipLaunchKernelGGL((gemm_kernel<LA, LB, FA, FB>),
+                     dim3((unsigned)(g.tiles_m * g.tiles_n), (unsigned)g.batch), dim3(kGThreads), 0,
+                     st, g);
 }
 
 template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB>
@@ -239,7 +241,8 @@ void launch_gemm3_t(GemmArgs& g, hipStream_t st) {
   if (g.tiles_m < 1) g.tiles_m = 1;
   if (g.tiles_n < 1) g.tiles_n = 1;
   hipLaunchKernelGGL((gemm3_kernel<BM, BN, WGM, WGN, LA, LB, FA, FB>),
-                     dim3((unsigned)(g.tiles_m * g.tiles_n)), dim3(64 * WGM * WGN), lds, st, g);
+                     dim3((unsigned)(g.tiles_m * g.tiles_n), (unsigned)g.batch), dim3(64 * WGM * WGN),
+                     lds, st, g);
 }
 
 enum { kTileAuto = 0, kTile256x256, kTile256x128, kTile128x128, kTileV1, kTile256x256w8, kTile128x128w8 };
@@ -259,17 +262,18 @@ int forced_tile() {
   return kTileAuto;
 }
 
-// Tile choice (measured crossovers on the layer shapes).  Larger tiles move
+// Tile choice (measured crossovers on the layer shapes; tiles counted over
+// all batch slices).  Larger tiles move
 // fewer operand bytes per MFMA but leave CUs idle when the output has few
 // tiles, and one tile per CU cannot overlap its epilogue with another loop.
 //  * 256x256, 8 waves (gemm4): when its tiles fill at least half the CUs.
 //  * 128x128, 8 waves (gemm5): when the 128x128 tiles fit one per CU; the
 //    block's 8 waves give each SIMD two waves.
 //  * 128x128, 4 waves, two blocks per CU (gemm3): otherwise.
-int choose_tile(int64_t Mc, int64_t Nc) {
+int choose_tile(int64_t Mc, int64_t Nc, int64_t batch) {
   const int64_t cus = cu_count();
-  const int64_t tiles256 = ((Mc + 255) / 256) * ((Nc + 255) / 256);
-  const int64_t tiles128 = ((Mc + 127) / 128) * ((Nc + 127) / 128);
+  const int64_t tiles256 = batch * ((Mc + 255) / 256) * ((Nc + 255) / 256);
+  const int64_t tiles128 = batch * ((Mc + 127) / 128) * ((Nc + 127) / 128);
   if (2 * tiles256 >= cus) return kTile256x256w8;
   return tiles128 <= cus ? kTile128x128w8 : kTile128x128;
 }
@@ -297,8 +301,9 @@ void launch_gemm4_t(GemmArgs& g, hipStream_t st) {
   g.tiles_n = (int32_t)((g.Nc + 255) / 256);
   if (g.tiles_m < 1) g.tiles_m = 1;
   if (g.tiles_n < 1) g.tiles_n = 1;
-  hipLaunchKernelGGL((gemm4_kernel<LA, LB, FA, FB>), dim3((unsigned)(g.tiles_m * g.tiles_n)),
-                     dim3(512), lds, st, g);
+  hipLaunchKernelGGL((gemm4_kernel<LA, LB, FA, FB>),
+                     dim3((unsigned)(g.tiles_m * g.tiles_n), (unsigned)g.batch), dim3(512), lds, st,
+                     g);
 }
 
 template <int LA, int LB>
@@ -324,8 +329,9 @@ void launch_gemm5_t(GemmArgs& g, hipStream_t st) {
   g.tiles_n = (int32_t)((g.Nc + 127) / 128);
   if (g.tiles_m < 1) g.tiles_m = 1;
   if (g.tiles_n < 1) g.tiles_n = 1;
-  hipLaunchKernelGGL((gemm5_kernel<LA, LB, FA, FB>), dim3((unsigned)(g.tiles_m * g.tiles_n)),
-                     dim3(512), lds, st, g);
+  hipLaunchKernelGGL((gemm5_kernel<LA, LB, FA, FB>),
+                     dim3((unsigned)(g.tiles_m * g.tiles_n), (unsigned)g.batch), dim3(512), lds, st,
+                     g);
 }
 
 template <int LA, int LB>
@@ -347,6 +353,7 @@ bool fast_path_ok(const GemmArgs& g) {
   // a tile may hang up to 256 rows past the last one; its offsets must stay
   // below 2^32 so they read as out of range instead of wrapping
   return aligned16(g.a) && aligned16(g.b) && aligned16(g.c) && g.ldc % 8 == 0 && g.Nc % 8 == 0 &&
+         g.bsa % 16 == 0 && g.bsb % 16 == 0 && g.bsc % 8 == 0 &&
          g.lda % 16 == 0 && g.ldb % 16 == 0 &&
          a_inner % 16 == 0 && b_inner % 16 == 0 && (a_rows + 256) * g.lda < (1LL << 31) &&
          (b_rows + 256) * g.ldb < (1LL << 31);
@@ -356,7 +363,7 @@ template <int LA, int LB>
 void launch_gemm_l(GemmArgs& g, int fa, int fb, hipStream_t st) {
   int tile = forced_tile();
   if (!fast_path_ok<LA, LB>(g)) tile = kTileV1;
-  if (tile == kTileAuto) tile = choose_tile(g.Mc, g.Nc);
+  if (tile == kTileAuto) tile = choose_tile(g.Mc, g.Nc, g.batch);
   switch (tile) {
     case kTile256x256: launch_gemm3_f<256, 256, 2, 2, LA, LB>(g, fa, fb, st); return;
     case kTile256x128: launch_gemm3_f<256, 128, 2, 2, LA, LB>(g, fa, fb, st); return;
@@ -375,9 +382,10 @@ void finish_gemm_args(GemmArgs& g) {
   const int64_t tm = (g.Mc + kBM - 1) / kBM, tn = (g.Nc + kBN - 1) / kBN;
   g.tiles_m = (int32_t)(tm < 1 ? 1 : tm);
   g.tiles_n = (int32_t)(tn < 1 ? 1 : tn);
-  g.a_vec = aligned16(g.a) && g.lda % 16 == 0;
-  g.b_vec = aligned16(g.b) && g.ldb % 16 == 0;
-  g.c_vec = ((uintptr_t)g.c & 7u) == 0 && g.ldc % 4 == 0;
+  if (g.batch < 1) g.batch = 1;
+  g.a_vec = aligned16(g.a) && g.lda % 16 == 0 && g.bsa % 16 == 0;
+  g.b_vec = aligned16(g.b) && g.ldb % 16 == 0 && g.bsb % 16 == 0;
+  g.c_vec = ((uintptr_t)g.c & 7u) == 0 && g.ldc % 4 == 0 && g.bsc % 4 == 0;
 }
 
 int hip_status() { return hipGetLastError() == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
@@ -657,3 +665,67 @@ int fp8_linear_bwd_dw(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t 
 }
 
 }  // extern "C"
+
+int fp8_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, fp8_operand_t a, int32_t layout_a,
+             int64_t lda, int64_t stride_a, fp8_operand_t b, int32_t layout_b, int64_t ldb,
+             int64_t stride_b, fp8_operand_t bias, void* c, int64_t ldc, int64_t stride_c,
+             hipStream_t stream) {
+  if (batch < 0 || M < 0 || N < 0 || K < 0 || stride_a < 0 || stride_b < 0 || stride_c < 0)
+    return FP8_ERR_SHAPE;
+  if (batch > 65535) return FP8_ERR_SHAPE;
+  if (!is_fp8_dtype(a.dtype) || !is_fp8_dtype(b.dtype)) return FP8_ERR_DTYPE;
+  if ((layout_a != FP8_K_CONTIG && layout_a != FP8_K_STRIDED) ||
+      (layout_b != FP8_K_CONTIG && layout_b != FP8_K_STRIDED))
+    return FP8_ERR_DTYPE;
+  int bias_kind = kBiasNone;
+  if (bias.data) {
+    if (bias.dtype == FP8_DT_BF16) bias_kind = kBiasBF16;
+    else if (bias.dtype == FP8_DT_E4M3) bias_kind = kBiasE4M3;
+    else if (bias.dtype == FP8_DT_E5M2) bias_kind = kBiasE5M2;
+    else return FP8_ERR_DTYPE;
+    if (bias_kind != kBiasBF16 && !bias.scale) return FP8_ERR_NULL;
+  }
+  if (!a.scale || !b.scale) return FP8_ERR_NULL;
+  if (batch == 0 || M == 0 || N == 0) return FP8_OK;
+  // leading dimensions, slice extents and non-overlapping output slices
+  const int64_t a_rows = layout_a == FP8_K_CONTIG ? M : K, a_inner = layout_a == FP8_K_CONTIG ? K : M;
+  const int64_t b_rows = layout_b == FP8_K_CONTIG ? N : K, b_inner = layout_b == FP8_K_CONTIG ? K : N;
+  if (lda < a_inner || ldb < b_inner || ldc < N) return FP8_ERR_SHAPE;
+  if (!mul_ok(a_rows, lda) || !mul_ok(b_rows, ldb) || !mul_ok(M, ldc) || !mul_ok(batch, stride_a) ||
+      !mul_ok(batch, stride_b) || !mul_ok(batch, stride_c))
+    return FP8_ERR_SHAPE;
+  if (batch > 1 && stride_c < (M - 1) * ldc + N) return FP8_ERR_SHAPE;
+  if (K > 0 && (!a.data || !b.data)) return FP8_ERR_NULL;
+  if (!c) return FP8_ERR_NULL;
+
+  GemmArgs g = {};
+  g.a = reinterpret_cast<const uint8_t*>(a.data);
+  g.lda = lda;
+  g.b = reinterpret_cast<const uint8_t*>(b.data);
+  g.ldb = ldb;
+  g.Mc = M;
+  g.Nc = N;
+  g.Kc = K;
+  g.c = reinterpret_cast<uint16_t*>(c);
+  g.ldc = ldc;
+  g.scale_a = a.scale;
+  g.scale_b = b.scale;
+  g.bias = bias.data;
+  g.bias_kind = bias_kind;
+  g.bias_scale = bias.scale;
+  g.bsa = stride_a;
+  g.bsb = stride_b;
+  g.bsc = stride_c;
+  g.batch = (int32_t)batch;
+  finish_gemm_args(g);
+  const int fa = dtype_fmt(a.dtype), fb = dtype_fmt(b.dtype);
+  if (layout_a == FP8_K_CONTIG && layout_b == FP8_K_CONTIG)
+    launch_gemm_l<kKContig, kKContig>(g, fa, fb, stream);
+  else if (layout_a == FP8_K_CONTIG)
+    launch_gemm_l<kKContig, kCross>(g, fa, fb, stream);
+  else if (layout_b == FP8_K_CONTIG)
+    launch_gemm_l<kCross, kKContig>(g, fa, fb, stream);
+  else
+    launch_gemm_l<kCross, kCross>(g, fa, fb, stream);
+  return hip_status();
+}

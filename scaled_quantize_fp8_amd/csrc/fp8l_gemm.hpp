@@ -70,7 +70,19 @@ struct GemmArgs {
   float* aux_amax_dst1;
   int32_t a_vec, b_vec, c_vec;
   int32_t tiles_m, tiles_n;
+  // batched operands (grid.y = batch): slice z starts at a + z bsa, b + z bsb
+  // (bytes) and c + z bsc (elements); a stride of 0 broadcasts the slice
+  int64_t bsa, bsb, bsc;
+  int32_t batch;  // >= 1
 };
+
+// Move the operand pointers to this block's batch slice (blockIdx.y).
+FP8L_DEV void batch_slice(GemmArgs& g) {
+  const int64_t z = blockIdx.y;
+  g.a += z * g.bsa;
+  g.b += z * g.bsb;
+  g.c += z * g.bsc;
+}
 
 // Swizzle of the 16-byte chunk index within a 128-byte LDS row.
 // k-contiguous tiles (row = C row): 16 consecutive rows read the same logical
@@ -179,6 +191,7 @@ FP8L_DEV void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
 
 template <int LA, int LB, int FA, int FB>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_kernel(GemmArgs g) {
+  batch_slice(g);
   __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][kTileBytes];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -188,7 +201,7 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_kernel(GemmArgs g) {
   const int64_t i0 = (int64_t)tm * kBM;
   const int64_t j0 = (int64_t)tn * kBN;
 
-  if (blockIdx.x == 0 && tid == 0) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
     if (g.aux_amax_dst0) *g.aux_amax_dst0 = 0.0f;
     if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;

@@ -399,6 +399,7 @@ constexpr int gemm3_lds_bytes() {
 template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB>
 __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN <= 128 * 128) ? 2 : 1)
 void gemm3_kernel(GemmArgs g) {
+  batch_slice(g);
   constexpr int NW = WGM * WGN;
   using OA = Op3<LA, BM, NW>;
   using OB = Op3<LB, BN, NW>;
@@ -414,7 +415,7 @@ void gemm3_kernel(GemmArgs g) {
   tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
 
-  if (blockIdx.x == 0 && tid == 0) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
     if (g.aux_amax_dst0) *g.aux_amax_dst0 = 0.0f;
     if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;

@@ -184,6 +184,7 @@ struct FragBase {
 
 template <int LA, int LB, int FA, int FB>
 __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
+  batch_slice(g);
   constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4, NW = WGM * WGN;
   using OA = Op3<LA, BM, NW>;
   using OB = Op3<LB, BN, NW>;
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
 
-  if (blockIdx.x == 0 && tid == 0) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
     if (g.aux_amax_dst0) *g.aux_amax_dst0 = 0.0f;
     if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;

@@ -53,6 +53,7 @@ FP8L_DEV void read1(const uint8_t* s, int f, v8i& n0) {
 
 template <int LA, int LB, int FA, int FB>
 __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
+  batch_slice(g);
   constexpr int BM = 128, BN = 128, WGM = 2, WGN = 4, NW = WGM * WGN;
   using OA = Op3<LA, BM, NW>;  // one 64-byte sub-step: 8 KB, one DMA load per wave
   using OB = Op3<LB, BN, NW>;
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
   tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
 
-  if (blockIdx.x == 0 && tid == 0) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
     if (g.aux_amax_dst0) *g.aux_amax_dst0 = 0.0f;
     if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;

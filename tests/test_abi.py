@@ -138,3 +138,32 @@ def test_ring_init_validation(lib):
     assert lib.fp8_ring_init(ctypes.byref(r), None, 16, None) == F.FP8_ERR_NULL
     assert lib.fp8_ring_init(ctypes.byref(r), P, 0, None) == F.FP8_ERR_RING
     assert lib.fp8_ring_init(ctypes.byref(r), ctypes.c_void_p(0x100040), 16, None) == F.FP8_ERR_RING
+
+
+def test_gemm_validation(lib):
+    gm = lib.fp8_gemm
+    f8 = F._Operand(P, F.FP8_DT_E4M3, P)
+    f8b = F._Operand(P, F.FP8_DT_E5M2, P)
+    none = F._Operand(None, F.FP8_DT_BF16, None)
+    KC, KS = F.FP8_K_CONTIG, F.FP8_K_STRIDED
+
+    def call(batch=2, M=8, N=16, K=32, a=f8, la=KC, lda=32, sa=256, b=f8b, lb=KC, ldb=32, sb=512,
+             bias=none, c=P, ldc=16, sc=128):
+        return gm(batch, M, N, K, a, la, lda, sa, b, lb, ldb, sb, bias, c, ldc, sc, None)
+
+    assert call(a=F._Operand(P, F.FP8_DT_BF16, None)) == F.FP8_ERR_DTYPE  # not fp8
+    assert call(la=2) == F.FP8_ERR_DTYPE
+    assert call(a=F._Operand(P, F.FP8_DT_E4M3, None)) == F.FP8_ERR_NULL  # no scale
+    assert call(bias=F._Operand(P, F.FP8_DT_F16, None)) == F.FP8_ERR_DTYPE
+    assert call(bias=F._Operand(P, F.FP8_DT_E5M2, None)) == F.FP8_ERR_NULL
+    assert call(lda=31) == F.FP8_ERR_SHAPE                 # k-contiguous A needs lda >= K
+    assert call(la=KS, lda=7) == F.FP8_ERR_SHAPE           # strided A needs lda >= M
+    assert call(lb=KS, ldb=15) == F.FP8_ERR_SHAPE          # strided B needs ldb >= N
+    assert call(ldc=15) == F.FP8_ERR_SHAPE
+    assert call(sc=16 * 7 + 15) == F.FP8_ERR_SHAPE         # output slices would overlap
+    assert call(batch=-1) == F.FP8_ERR_SHAPE and call(sa=-1) == F.FP8_ERR_SHAPE
+    assert call(batch=65536) == F.FP8_ERR_SHAPE
+    assert call(c=None) == F.FP8_ERR_NULL
+    # empty problems enqueue nothing and succeed
+    assert call(batch=0) == F.FP8_OK and call(M=0) == F.FP8_OK
+

@@ -206,3 +206,71 @@ def test_full_size_sampled_rows(tile):
         nrows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 48, replace=False)]))
         check_gemm(dw[nrows], O.linear_bwd_dw(g8[:, nrows], O.E5M2, x8, O.E4M3, 7.0e3, 100.0),
                    f"dw {K}x{N}")
+
+
+# ---------------------------------------------------------------- fp8_gemm
+# The general entry point: batch slices by stride, size-1 batches broadcast,
+# and transposed views passed as a layout (no copy).  Each slice is compared
+# with the oracle on the same codes arranged as [M, K] and [N, K].
+
+def _stored(codes_rk, layout):
+    """Device tensor holding [.., R, K] codes in the given layout: k-contiguous
+    rows, or a [.., K, R] buffer seen through .mT."""
+    if layout == F.FP8_K_CONTIG:
+        return to_dev(np.ascontiguousarray(codes_rk))
+    buf = to_dev(np.ascontiguousarray(np.swapaxes(codes_rk, -1, -2)))
+    return buf.mT
+
+
+@pytest.mark.parametrize("la", [F.FP8_K_CONTIG, F.FP8_K_STRIDED])
+@pytest.mark.parametrize("lb", [F.FP8_K_CONTIG, F.FP8_K_STRIDED])
+@pytest.mark.parametrize("shape", [(3, 256, 384, 512), (2, 200, 136, 300), (3, 208, 96, 64)])
+def test_gemm_batched_layouts(tile, la, lb, shape):
+    B, M, N, K = shape
+    rng = np.random.default_rng(B * M + N + 7 * K + 2 * la + lb)
+    a = _rand_codes((B, M, K), O.E4M3, rng)
+    b = _rand_codes((B, N, K), O.E4M3, rng)
+    bias = (rng.standard_normal(N) * 0.5).astype(np.float32)
+    bias_t = torch.from_numpy(bias).to(torch.bfloat16)
+    sa, sb = np.float32(3.0), np.float32(0.125)
+    c = torch.empty(B, M, N, dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm(F.Quantized(_stored(a, la), O.E4M3, scalar_dev(sa)),
+               F.Quantized(_stored(b, lb), O.E4M3, scalar_dev(sb)), c, bias=bias_t.to(DEV))
+    torch.cuda.synchronize()
+    beta = O.bias_values(bias_t.view(torch.int16).numpy().view(np.uint16), "bf16")
+    got = bf16_bits(c)
+    for z in range(B):
+        check_gemm(got[z], O.linear_fwd(a[z], b[z], O.E4M3, sa, sb, beta), f"slice {z}")
+
+
+@pytest.mark.parametrize("lb", [F.FP8_K_CONTIG, F.FP8_K_STRIDED])
+def test_gemm_broadcast_and_mixed_formats_exact(tile, lb):
+    """b given once (2-D) for 4 slices of a; e5m2 x e4m3 small integers, so
+    every slice must equal the oracle bit for bit."""
+    B, M, N, K = 4, 160, 272, 384
+    rng = np.random.default_rng(11 + lb)
+    a = _int_codes((B, M, K), O.E5M2, rng)
+    b = _int_codes((N, K), O.E4M3, rng)
+    c = torch.empty(B, M, N, dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm(F.Quantized(_stored(a, F.FP8_K_CONTIG), O.E5M2, scalar_dev(1.0)),
+               F.Quantized(_stored(b, lb), O.E4M3, scalar_dev(2.0)), c)
+    torch.cuda.synchronize()
+    got = bf16_bits(c)
+    for z in range(B):
+        ref = O.linear_bwd_dx(a[z], O.E5M2, np.ascontiguousarray(b.T), O.E4M3, 1.0, 2.0)
+        assert np.array_equal(got[z], ref.y_bits), f"slice {z}"
+
+
+def test_gemm_batch_one_of_a_broadcasts(tile):
+    """a with batch 1 against b with batch 3: a's slice is shared."""
+    M, N, K = 128, 256, 192
+    rng = np.random.default_rng(5)
+    a = _rand_codes((1, M, K), O.E4M3, rng)
+    b = _rand_codes((3, N, K), O.E4M3, rng)
+    c = torch.empty(3, M, N, dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm(F.Quantized(to_dev(a), O.E4M3, scalar_dev(1.0)),
+               F.Quantized(to_dev(b), O.E4M3, scalar_dev(1.0)), c)
+    torch.cuda.synchronize()
+    got = bf16_bits(c)
+    for z in range(3):
+        check_gemm(got[z], O.linear_fwd(a[0], b[z], O.E4M3, 1.0, 1.0), f"slice {z}")
