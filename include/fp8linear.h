@@ -162,6 +162,33 @@ int fp8_ring_init(fp8_ring_t* ring, void* dev, int32_t hist_len, hipStream_t str
 int fp8_quantize(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, uint8_t* q,
                  fp8_ring_t* ring, float* scale_used, float* amax_out, hipStream_t stream);
 
+/* Output orientation of fp8_quantize_2d ([P4] entry on splitting the quantize
+ * into transposed and dual variants with a layout enum). */
+typedef enum {
+  FP8_QUANT_ROWS = 0,        /* q [rows, cols] only (as fp8_quantize) */
+  FP8_QUANT_TRANSPOSED = 1,  /* qt [cols, rows] only */
+  FP8_QUANT_DUAL = 2         /* both */
+} fp8_quant_layout_t;
+
+/*
+ * Per-tensor quantize of a row-major x [rows, cols] with transposed and dual
+ * outputs ([P4] entry on the quantize bindings split into transposed and
+ * dual variants, tested for byte equality between orientations): the codes,
+ * scale, amax and ring update are exactly those of fp8_quantize on the same
+ * rows * cols elements; q receives them row-major, qt transposed,
+ * qt[c * rows + r] = q[r * cols + c].  A transposed copy of X8 or G8 lets
+ * fp8_gemm run the weight gradient with both operands k-contiguous.
+ *
+ *   layout   FP8_QUANT_ROWS, FP8_QUANT_TRANSPOSED or FP8_QUANT_DUAL.
+ *   q        device [rows, cols] bytes out; required unless TRANSPOSED.
+ *   qt       device [cols, rows] bytes out; required unless ROWS.
+ *   x, in_dtype, fmt, ring, scale_used, amax_out: as fp8_quantize.
+ * Errors: as fp8_quantize; FP8_ERR_DTYPE for an unknown layout.
+ */
+int fp8_quantize_2d(const void* x, int32_t in_dtype, int64_t rows, int64_t cols, int32_t fmt,
+                    int32_t layout, uint8_t* q, uint8_t* qt, fp8_ring_t* ring, float* scale_used,
+                    float* amax_out, hipStream_t stream);
+
 /*
  * Two per-tensor quantizes in one call, each exactly as fp8_quantize with
  * its own input, output, ring, scale_used and amax_out, in one format.  When

@@ -24,6 +24,7 @@ FP8_E4M3, FP8_E5M2 = 0, 1
 FP8_DT_F32, FP8_DT_F16, FP8_DT_BF16, FP8_DT_E4M3, FP8_DT_E5M2 = 0, 1, 2, 3, 4
 FP8_OK, FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_DTYPE, FP8_ERR_RING, FP8_ERR_HIP = range(6)
 FP8_K_CONTIG, FP8_K_STRIDED = 0, 1
+FP8_QUANT_ROWS, FP8_QUANT_TRANSPOSED, FP8_QUANT_DUAL = 0, 1, 2
 
 _TORCH_DT = {torch.float32: FP8_DT_F32, torch.float16: FP8_DT_F16, torch.bfloat16: FP8_DT_BF16}
 _FMT_DT = {FP8_E4M3: FP8_DT_E4M3, FP8_E5M2: FP8_DT_E5M2}
@@ -31,7 +32,7 @@ _FMT_DT = {FP8_E4M3: FP8_DT_E4M3, FP8_E5M2: FP8_DT_E5M2}
 C_SYMBOLS = (
     "fp8_abi_version", "fp8_status_str", "fp8_ring_bytes", "fp8_ring_init", "fp8_quantize",
     "fp8_quantize_pair", "fp8_linear_fwd", "fp8_linear_bwd_dx", "fp8_db_workspace_bytes",
-    "fp8_linear_bwd_dw", "fp8_gemm",
+    "fp8_linear_bwd_dw", "fp8_gemm", "fp8_quantize_2d",
 )
 
 
@@ -76,10 +77,11 @@ def lib() -> ctypes.CDLL:
                                      vp, vp]
         L.fp8_linear_bwd_dx.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp]
         L.fp8_linear_bwd_dw.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp, vp, vp]
+        L.fp8_quantize_2d.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, rp, vp, vp, vp]
         L.fp8_gemm.argtypes = [i64, i64, i64, i64, op, i32, i64, i64, op, i32, i64, i64, op, vp,
                                i64, i64, vp]
-        for name in ("fp8_ring_init", "fp8_quantize", "fp8_quantize_pair", "fp8_linear_fwd",
-                     "fp8_gemm", "fp8_linear_bwd_dx",
+        for name in ("fp8_ring_init", "fp8_quantize", "fp8_quantize_pair", "fp8_quantize_2d",
+                     "fp8_linear_fwd", "fp8_gemm", "fp8_linear_bwd_dx",
                      "fp8_linear_bwd_dw"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -229,6 +231,27 @@ def fp8_quantize(x, fmt, q, ring=None, scale_used=None, amax_out=None, stream=No
 
 def bind_fp8_quantize(x, fmt, q, ring=None, scale_used=None, amax_out=None, stream=None):
     return _bind("fp8_quantize", _quantize_args(x, fmt, q, ring, scale_used, amax_out, stream))
+
+
+def _quantize_2d_args(x, fmt, layout, q, qt, ring, scale_used, amax_out, stream):
+    rows, cols = x.shape
+    return (_vp(x), ctypes.c_int32(_TORCH_DT[x.dtype]), ctypes.c_int64(rows), ctypes.c_int64(cols),
+            ctypes.c_int32(fmt), ctypes.c_int32(layout), _vp(q), _vp(qt), _ring(ring),
+            _vp(scale_used), _vp(amax_out), ctypes.c_void_p(_stream(stream)))
+
+
+def fp8_quantize_2d(x, fmt, layout, q=None, qt=None, ring=None, scale_used=None, amax_out=None,
+                    stream=None):
+    """x [rows, cols] -> q [rows, cols] and/or qt [cols, rows] (layout:
+    FP8_QUANT_ROWS / _TRANSPOSED / _DUAL)."""
+    _check(lib().fp8_quantize_2d(*_quantize_2d_args(x, fmt, layout, q, qt, ring, scale_used,
+                                                    amax_out, stream)), "fp8_quantize_2d")
+
+
+def bind_fp8_quantize_2d(x, fmt, layout, q=None, qt=None, ring=None, scale_used=None,
+                         amax_out=None, stream=None):
+    return _bind("fp8_quantize_2d", _quantize_2d_args(x, fmt, layout, q, qt, ring, scale_used,
+                                                      amax_out, stream))
 
 
 def fp8_quantize_pair(x0, q0, ring0, su0, am0, x1, q1, ring1, su1, am1, fmt, stream=None):

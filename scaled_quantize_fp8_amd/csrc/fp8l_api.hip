@@ -75,9 +75,13 @@ int check_quant(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, const u
   return check_alias(ring, scale_used);
 }
 
+// 2-D shape of a quantize: the column-sum variant (ws != null) or the
+// transposed/dual variant (tkernel: q and/or qt).
 struct ColsumSpec {
   int64_t rows, cols;
   float* ws;
+  uint8_t* qt = nullptr;
+  bool tkernel = false;
 };
 
 int64_t flat_blocks(int64_t n, int64_t cap) {
@@ -87,7 +91,13 @@ int64_t flat_blocks(int64_t n, int64_t cap) {
 
 template <int IN, int FMT, int SMODE>
 void launch_convert(const QArgs& a, const ColsumSpec* cs, hipStream_t st) {
-  if (cs && cs->rows > 0 && cs->cols > 0) {
+  if (cs && cs->tkernel) {
+    const int64_t tiles = ((cs->rows + kTT - 1) / kTT) * ((cs->cols + kTT - 1) / kTT);
+    const int64_t cap = (int64_t)cu_count() * 8;
+    const int64_t blocks = tiles < 1 ? 1 : (tiles > cap ? cap : tiles);
+    hipLaunchKernelGGL((quantize_t_kernel<IN, FMT, SMODE>), dim3((unsigned)blocks), dim3(kQThreads),
+                       0, st, a);
+  } else if (cs && cs->rows > 0 && cs->cols > 0) {
     dim3 grid((unsigned)((cs->cols + kColStrip - 1) / kColStrip),
               (unsigned)((cs->rows + kColRowsPerChunk - 1) / kColRowsPerChunk));
     hipLaunchKernelGGL((quantize_colsum_kernel<IN, FMT, SMODE>), grid, dim3(kQThreads), 0, st, a);
@@ -113,6 +123,8 @@ void enqueue_quant_t(const void* x, int64_t n, uint8_t* q, fp8_ring_t* ring, flo
     a.cols = cs->cols;
     a.colsum = cs->ws;
     a.vec_ok = a.vec_ok && (cs->cols % 8 == 0);
+    a.qt = cs->qt;
+    a.qt_vec = cs->qt && aligned16(cs->qt) && cs->rows % 16 == 0;
   }
   const int vec_x = aligned16(x);
   if (ring) {
@@ -448,6 +460,34 @@ int fp8_quantize_pair(const void* x0, int32_t dtype0, int64_t n0, uint8_t* q0, f
   if (ring0 && ring0 == ring1) return FP8_ERR_RING;
   enqueue_quant_pair(x0, dtype0, n0, q0, ring0, scale_used0, amax_out0, x1, dtype1, n1, q1, ring1,
                      scale_used1, amax_out1, fmt, stream);
+  return hip_status();
+}
+
+int fp8_quantize_2d(const void* x, int32_t in_dtype, int64_t rows, int64_t cols, int32_t fmt,
+                    int32_t layout, uint8_t* q, uint8_t* qt, fp8_ring_t* ring, float* scale_used,
+                    float* amax_out, hipStream_t stream) {
+  if (rows < 0 || cols < 0 || !mul_ok(rows, cols)) return FP8_ERR_SHAPE;
+  if (layout != FP8_QUANT_ROWS && layout != FP8_QUANT_TRANSPOSED && layout != FP8_QUANT_DUAL)
+    return FP8_ERR_DTYPE;
+  const int64_t n = rows * cols;
+  if (!mul_ok(n, 4)) return FP8_ERR_SHAPE;
+  const bool want_q = layout != FP8_QUANT_TRANSPOSED, want_qt = layout != FP8_QUANT_ROWS;
+  if (n > 0 && ((want_q && !q) || (want_qt && !qt))) return FP8_ERR_NULL;
+  // the rest as fp8_quantize (q stands for whichever output is given)
+  int st = check_quant(x, in_dtype, n, fmt, want_q ? q : qt, ring, scale_used, amax_out);
+  if (st) return st;
+  if (layout == FP8_QUANT_ROWS) {
+    enqueue_quant(x, in_dtype, n, fmt, q, ring, scale_used, amax_out, nullptr, stream);
+  } else {
+    ColsumSpec cs;
+    cs.rows = rows;
+    cs.cols = cols;
+    cs.ws = nullptr;
+    cs.qt = qt;
+    cs.tkernel = true;
+    enqueue_quant(x, in_dtype, n, fmt, want_q ? q : nullptr, ring, scale_used, amax_out, &cs,
+                  stream);
+  }
   return hip_status();
 }
 

@@ -49,6 +49,8 @@ struct QArgs {
   float* amax_out;    // dynamic: complete amax from the amax pass; ring: optional output
   float* colsum;      // [ceil(rows / kColRowsPerChunk)][cols] partial sums or null
   int32_t vec_ok;     // x, q 16-byte aligned (and cols % 8 == 0 for the column variant)
+  uint8_t* qt;        // transposed variant: [cols, rows] codes or null (q may be null)
+  int32_t qt_vec;     // qt 16-byte aligned and rows % 16 == 0
 };
 
 template <int IN>
@@ -309,6 +311,78 @@ __global__ __launch_bounds__(kQThreads) void quantize_flat2_kernel(QArgs a0, QAr
     quantize_flat_body<IN, FMT, kScaleRing>(a0, blockIdx.x, nblk0);
   else
     quantize_flat_body<IN, FMT, kScaleRing>(a1, blockIdx.x - nblk0, gridDim.x - nblk0);
+}
+
+// Quantize x [rows, cols] into q [rows, cols] and/or its transpose
+// qt [cols, rows] ([P4] entry on the transposed and dual quantize layouts):
+// qt[c][r] = q[r][c], same codes, same amax and ring finalize as the flat
+// kernel.  Tiles of 64 x 64: each thread converts 16 consecutive elements of
+// one row (stored to q directly), the tile's codes pass through LDS, and each
+// thread then writes 16 consecutive codes of one qt row.
+constexpr int kTT = 64;
+
+template <int IN, int FMT, int SMODE>
+__global__ __launch_bounds__(kQThreads) void quantize_t_kernel(QArgs a) {
+  __shared__ uint8_t tile[kTT][kTT + 4];  // rows 68 bytes apart
+  const float s = launch_scale<FMT, SMODE>(a);
+  const int t = threadIdx.x;
+  const int lr = t >> 2, lc = (t & 3) * 16;  // load: row lr, columns lc .. lc + 15
+  const int tc = t >> 2, tr = (t & 3) * 16;  // store: qt row tc, rows tr .. tr + 15
+  const int64_t tiles_c = (a.cols + kTT - 1) / kTT;
+  const int64_t ntiles = ((a.rows + kTT - 1) / kTT) * tiles_c;
+  uint32_t mx = 0;
+  for (int64_t ti = blockIdx.x; ti < ntiles; ti += gridDim.x) {
+    const int64_t r0 = (ti / tiles_c) * kTT, c0 = (ti % tiles_c) * kTT;
+    const int64_t r = r0 + lr, c = c0 + lc;
+    float v[16];
+    uint32_t m0 = 0, m1 = 0;
+    const bool full = a.vec_ok && r < a.rows && c + 16 <= a.cols;
+    if (full) {
+      load8<IN>(a.x, r * a.cols + c, v);
+      load8<IN>(a.x, r * a.cols + c + 8, v + 8);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        v[i] = (r < a.rows && c + i < a.cols) ? load1<IN>(a.x, r * a.cols + c + i) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      m0 = max(m0, absbits(v[i]));
+      m1 = max(m1, absbits(v[8 + i]));
+    }
+    const uint2 w0 = quant8<FMT>(v, s, m0), w1 = quant8<FMT>(v + 8, s, m1);
+    mx = max(mx, max(m0, m1));
+    const uint32_t w[4] = {w0.x, w0.y, w1.x, w1.y};
+    if (a.q) {
+      if (full) {
+        *reinterpret_cast<uint2*>(a.q + r * a.cols + c) = w0;
+        *reinterpret_cast<uint2*>(a.q + r * a.cols + c + 8) = w1;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (r < a.rows && c + i < a.cols)
+            a.q[r * a.cols + c + i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(&tile[lr][lc + 4 * j]) = w[j];
+    __syncthreads();
+    if (a.qt && c0 + tc < a.cols) {
+      uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[i >> 2] |= (uint32_t)tile[tr + i][tc] << (8 * (i & 3));
+      uint8_t* dst = a.qt + (c0 + tc) * a.rows + r0 + tr;
+      if (a.qt_vec && r0 + tr + 16 <= a.rows) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (r0 + tr + i < a.rows) dst[i] = (uint8_t)(o[i >> 2] >> (8 * (i & 3)));
+      }
+    }
+    __syncthreads();  // the next tile reuses the LDS tile
+  }
+  finish_launch<FMT, SMODE>(a, mx, s, blockIdx.x, gridDim.x);
 }
 
 // Column-sum quantize over x [rows, cols]: block (bx, by) covers columns

@@ -167,3 +167,16 @@ def test_gemm_validation(lib):
     # empty problems enqueue nothing and succeed
     assert call(batch=0) == F.FP8_OK and call(M=0) == F.FP8_OK
 
+
+
+def test_quantize_2d_validation(lib):
+    q2 = lib.fp8_quantize_2d
+    bf, e4 = F.FP8_DT_BF16, F.FP8_E4M3
+    P2 = ctypes.c_void_p(0x200000)
+    assert q2(P, bf, 8, 8, e4, 3, P, P, None, P2, P, None) == F.FP8_ERR_DTYPE   # layout
+    assert q2(P, bf, 8, 8, e4, F.FP8_QUANT_ROWS, None, P, None, P2, P, None) == F.FP8_ERR_NULL
+    assert q2(P, bf, 8, 8, e4, F.FP8_QUANT_TRANSPOSED, P, None, None, P2, P, None) == F.FP8_ERR_NULL
+    assert q2(P, bf, 8, 8, e4, F.FP8_QUANT_DUAL, P, None, None, P2, P, None) == F.FP8_ERR_NULL
+    assert q2(P, bf, -1, 8, e4, F.FP8_QUANT_DUAL, P, P, None, P2, P, None) == F.FP8_ERR_SHAPE
+    assert q2(P, F.FP8_DT_E5M2, 8, 8, e4, F.FP8_QUANT_DUAL, P, P, None, P2, P, None) == F.FP8_ERR_DTYPE
+    assert q2(P, bf, 8, 8, e4, F.FP8_QUANT_DUAL, P, P, None, None, P, None) == F.FP8_ERR_NULL

@@ -243,3 +243,85 @@ def test_quantize_pair_rejects_one_ring_twice():
         F.fp8_quantize_pair(x, q[0], ring, su[0], None, x, q[1], ring, su[1], None, O.E4M3)
     torch.cuda.synchronize()
     assert torch.equal(ring.buf, before)
+
+
+# ---------------------------------------------------------------- fp8_quantize_2d
+SHAPES_2D = [(2048, 1536), (333, 77), (64, 64), (1, 1000), (1000, 1), (130, 24), (96, 4104)]
+
+
+@pytest.mark.parametrize("shape", SHAPES_2D)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quantize_2d_dual_matches_oracle(shape, dtype):
+    """Dual orientation over three delayed steps: q is the oracle's codes,
+    qt their transpose, and scale, amax and ring match every step."""
+    rows, cols = shape
+    x0 = WL.normal_bf16(shape, 1.0, 31).float()
+    ring, oring = F.ScaleRing(16), O.ScaleRing(16)
+    for t, c in enumerate((1.0, 8.0, 0.5)):
+        x = (x0 * c).to(dtype)
+        q = torch.empty(rows, cols, dtype=torch.uint8, device=DEV)
+        qt = torch.empty(cols, rows, dtype=torch.uint8, device=DEV)
+        su = torch.empty(1, dtype=torch.float32, device=DEV)
+        am = torch.empty(1, dtype=torch.float32, device=DEV)
+        F.fp8_quantize_2d(x.to(DEV), O.E4M3, F.FP8_QUANT_DUAL, q, qt, ring, su, am)
+        torch.cuda.synchronize()
+        oq, os_, oa = O.quantize_step(f32(x), O.E4M3, oring)
+        oq = oq.reshape(rows, cols)
+        assert np.array_equal(u8(q), oq), t
+        assert np.array_equal(u8(qt), oq.T), t
+        assert f32_scalar(su).tobytes() == np.float32(os_).tobytes(), t
+        assert f32_scalar(am).tobytes() == np.float32(oa).tobytes(), t
+        assert_ring_matches(ring, oring)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_2d_transposed_only_dynamic(fmt):
+    rows, cols = 517, 264
+    x = (torch.randn(rows, cols, generator=torch.Generator().manual_seed(4)) * 3).to(torch.bfloat16)
+    qt = torch.empty(cols, rows, dtype=torch.uint8, device=DEV)
+    su = torch.empty(1, dtype=torch.float32, device=DEV)
+    am = torch.empty(1, dtype=torch.float32, device=DEV)
+    F.fp8_quantize_2d(x.to(DEV), fmt, F.FP8_QUANT_TRANSPOSED, None, qt, None, su, am)
+    torch.cuda.synchronize()
+    oq, os_, oa = O.quantize_step(f32(x), fmt, None)
+    assert np.array_equal(u8(qt), oq.reshape(rows, cols).T)
+    assert f32_scalar(su) == np.float32(os_) and f32_scalar(am) == np.float32(oa)
+
+
+def test_quantize_2d_rows_equals_quantize():
+    x = WL.normal_bf16((300, 200), 1.0, 41).to(DEV)
+    q1, s1, a1 = _quant_gpu(x.reshape(-1), O.E5M2)
+    q2 = torch.empty(300, 200, dtype=torch.uint8, device=DEV)
+    su = torch.empty(1, dtype=torch.float32, device=DEV)
+    am = torch.empty(1, dtype=torch.float32, device=DEV)
+    F.fp8_quantize_2d(x, O.E5M2, F.FP8_QUANT_ROWS, q2, None, None, su, am)
+    torch.cuda.synchronize()
+    assert np.array_equal(u8(q2).reshape(-1), q1) and f32_scalar(su) == s1
+
+
+def test_weight_gradient_from_transposed_operands():
+    """dW = G8^T X8 run k-contiguous: quantize G and X transposed, then
+    fp8_gemm with G8^T [N, M] and X8^T [K, M]; checked against the oracle
+    and against the crosswise dW of fp8_linear_bwd_dw on the same codes."""
+    from tests.gpu_util import check_gemm, bf16_bits
+    M, N, K = 2048, 1536, 6912
+    G = WL.normal_bf16((M, N), 1e-3, 51)
+    X = WL.normal_bf16((M, K), 1.0, 52)
+    g8t = torch.empty(N, M, dtype=torch.uint8, device=DEV)
+    x8t = torch.empty(K, M, dtype=torch.uint8, device=DEV)
+    sg, sx = (torch.empty(1, dtype=torch.float32, device=DEV) for _ in range(2))
+    ag, ax = (torch.empty(1, dtype=torch.float32, device=DEV) for _ in range(2))
+    F.fp8_quantize_2d(G.to(DEV), O.E5M2, F.FP8_QUANT_TRANSPOSED, None, g8t, None, sg, ag)
+    F.fp8_quantize_2d(X.to(DEV), O.E4M3, F.FP8_QUANT_TRANSPOSED, None, x8t, None, sx, ax)
+    dw = torch.empty(N, K, dtype=torch.bfloat16, device=DEV)
+    F.fp8_gemm(F.Quantized(g8t, O.E5M2, sg), F.Quantized(x8t, O.E4M3, sx), dw)
+    # the crosswise path on the same codes (transposed back)
+    g8 = g8t.t().contiguous()
+    x8 = x8t.t().contiguous()
+    dw2 = torch.empty(N, K, dtype=torch.bfloat16, device=DEV)
+    F.fp8_linear_bwd_dw(F.Quantized(g8, O.E5M2, sg), O.E5M2, F.Quantized(x8, O.E4M3, sx), dw2)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(3).choice(N, 48, replace=False)
+    ref = O.linear_bwd_dw(u8(g8)[:, rows], O.E5M2, u8(x8), O.E4M3, f32_scalar(sg), f32_scalar(sx))
+    check_gemm(bf16_bits(dw)[rows], ref, "k-contiguous dW")
+    check_gemm(bf16_bits(dw2)[rows], ref, "crosswise dW")
