@@ -254,6 +254,58 @@ def cpu_baseline(layers_cpu, budget_s, min_s=10.0):
                       f"GEMMs + db, fp64 accumulation; {dt:.1f} s on {os.cpu_count()} host cpus"}
 
 
+def widened_rows(torch, F, WL, wl, layers, stream, reps):
+    """Isolated timings of the entry points beyond the layer step (not part of
+    the step or its value): the transposed and dual quantize, the weight
+    gradient run k-contiguous from transposed operands next to the crosswise
+    one, and a batched fp8_gemm."""
+    dev = "cuda:0"
+    up = next(L for L in layers if L.name == "up")
+    M, N, K = up.M, up.N, up.K
+    res = {}
+    g8t = torch.empty(N, M, dtype=torch.uint8, device=dev)
+    x8t = torch.empty(K, M, dtype=torch.uint8, device=dev)
+    g8 = torch.empty(M, N, dtype=torch.uint8, device=dev)
+    s1, a1, s2, a2 = (torch.zeros(1, dtype=torch.float32, device=dev) for _ in range(4))
+    dual = F.bind_fp8_quantize_2d(up.G, F.FP8_E5M2, F.FP8_QUANT_DUAL, g8, g8t, None, s1, a1,
+                                  stream=stream)
+    tq = F.bind_fp8_quantize_2d(up.G, F.FP8_E5M2, F.FP8_QUANT_TRANSPOSED, None, g8t, None, s1, a1,
+                                stream=stream)
+    tx = F.bind_fp8_quantize_2d(up.X, F.FP8_E4M3, F.FP8_QUANT_TRANSPOSED, None, x8t, None, s2, a2,
+                                stream=stream)
+    for fn in (dual, tq, tx):
+        fn()
+    n = M * N
+    us = 1e3 * event_time_ms(torch, dual, reps, stream)
+    res["quantize_2d_dual_G_up_us"] = round(us, 2)
+    res["quantize_2d_dual_G_up_GBps"] = round(4.0 * n / (us * 1e-6) / 1e9, 1)  # 2 B in, 1 + 1 out
+    us = 1e3 * event_time_ms(torch, tq, reps, stream)
+    res["quantize_2d_transposed_G_up_GBps"] = round(3.0 * n / (us * 1e-6) / 1e9, 1)
+    dw = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+    kc = F.bind_fp8_gemm(F.Quantized(g8t, F.FP8_E5M2, s1), F.Quantized(x8t, F.FP8_E4M3, s2), dw,
+                         stream=stream)
+    kc()
+    flops = 2.0 * M * N * K
+    us_kc = 1e3 * event_time_ms(torch, kc, reps, stream)
+    us_x = 1e3 * event_time_ms(torch, up.gemm_dw, reps, stream)
+    res["dw_up_kcontig_us"] = round(us_kc, 2)
+    res["dw_up_crosswise_us"] = round(us_x, 2)
+    res["dw_up_kcontig_TFLOPs"] = round(flops / (us_kc * 1e-6) / 1e12, 1)
+    # batched NT GEMM: 8 x (1024 x 2048) x 2048, distinct slices
+    B, bm, bn, bk = 8, 1024, 2048, 2048
+    a = torch.randint(0, 0x7e, (B, bm, bk), dtype=torch.uint8, device=dev)
+    b = torch.randint(0, 0x7e, (B, bn, bk), dtype=torch.uint8, device=dev)
+    c = torch.empty(B, bm, bn, dtype=torch.bfloat16, device=dev)
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    bmm = F.bind_fp8_gemm(F.Quantized(a, F.FP8_E4M3, one), F.Quantized(b, F.FP8_E4M3, one), c,
+                          stream=stream)
+    bmm()
+    us = 1e3 * event_time_ms(torch, bmm, reps, stream)
+    res["gemm_batched_8x1024x2048x2048_us"] = round(us, 2)
+    res["gemm_batched_8x1024x2048x2048_TFLOPs"] = round(2.0 * B * bm * bn * bk / (us * 1e-6) / 1e12, 1)
+    return res
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -483,6 +535,7 @@ def main():
         "per_linear": {k: {kk: round(vv, 2) for kk, vv in v.items()} for k, v in per.items()},
         "roofline": roofline,
     }
+    out["widened"] = widened_rows(torch, F, WL, wl, layers, stream, args.kernel_reps)
     if not args.no_cpu_baseline:
         layers_cpu = [WL.layer_inputs(wl, li) for li in range(len(wl.linears))]
         out["cpu_baseline"] = cpu_baseline(layers_cpu, args.cpu_seconds)
