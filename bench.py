@@ -303,7 +303,39 @@ def widened_rows(torch, F, WL, wl, layers, stream, reps):
     us = 1e3 * event_time_ms(torch, bmm, reps, stream)
     res["gemm_batched_8x1024x2048x2048_us"] = round(us, 2)
     res["gemm_batched_8x1024x2048x2048_TFLOPs"] = round(2.0 * B * bm * bn * bk / (us * 1e-6) / 1e12, 1)
+    res["e2e_train_step"] = e2e_train_step(torch, dev)
     return res
+
+
+def e2e_train_step(torch, dev, steps=5, warmup=3):
+    """ms per training step of the 12-layer dim-1024 transformer (B4 x T512,
+    synthetic tokens, fused AdamW) with FP8 linears and with bf16 ones."""
+    from scaled_quantize_fp8_amd import e2e as E
+    out = {"model": "12L dim1024 ffn4096 heads16 vocab32000, B4xT512, AdamW", "steps": steps}
+    for name, lin in (("bf16", E.bf16_linear), ("fp8", E.fp8_linear)):
+        m = E.Transformer(lin, device=dev)
+        tok, tgt = E.synthetic_batch(4, 512, 32000, dev)
+        opt = torch.optim.AdamW(m.parameters(), lr=1e-4, fused=True)
+        with E.attention_backends():
+            for _ in range(warmup):
+                opt.zero_grad(set_to_none=True)
+                m.loss(tok, tgt).backward()
+                opt.step()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                opt.zero_grad(set_to_none=True)
+                loss = m.loss(tok, tgt)
+                loss.backward()
+                opt.step()
+            b.record()
+            torch.cuda.synchronize()
+        out[f"{name}_ms_per_step"] = round(a.elapsed_time(b) / steps, 3)
+        out[f"{name}_final_loss"] = round(loss.item(), 4)
+        del m, opt
+    out["fp8_speedup"] = round(out["bf16_ms_per_step"] / out["fp8_ms_per_step"], 3)
+    return out
 
 
 def main():
