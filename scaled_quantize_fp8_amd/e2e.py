@@ -75,3 +75,49 @@ def synthetic_batch(batch, seq, vocab, device, seed=0):
     tok = torch.randint(0, vocab, (batch, seq), generator=g)
     tgt = torch.randint(0, vocab, (batch, seq), generator=g)
     return tok.to(device), tgt.to(device)
+
+
+def train(lin, steps, device, graph=False, warmup=3, seed=0, dims=None, batch=(4, 512)):
+    """Train a fresh model (same seed) on one synthetic batch: `warmup`
+    eager steps, then `steps` more either eager or as replays of one HIP
+    graph holding the whole step (forward, backward, fused AdamW).  Returns
+    (losses of the timed steps, ms per timed step)."""
+    dims = dims or {}
+    vocab = dims.get("vocab", 32000)
+    m = Transformer(lin, device=device, seed=seed, **dims)
+    tok, tgt = synthetic_batch(batch[0], batch[1], vocab, device, seed=seed)
+    opt = torch.optim.AdamW(m.parameters(), lr=1e-4, fused=True, capturable=graph)
+    losses = []
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with attention_backends(), torch.cuda.stream(side):
+        for _ in range(warmup):
+            opt.zero_grad(set_to_none=True)
+            m.loss(tok, tgt).backward()
+            opt.step()
+        if not graph:
+            start.record()
+            for _ in range(steps):
+                opt.zero_grad(set_to_none=True)
+                loss = m.loss(tok, tgt)
+                loss.backward()
+                opt.step()
+                losses.append(loss.detach().clone())
+            end.record()
+        else:
+            g = torch.cuda.CUDAGraph()
+            opt.zero_grad(set_to_none=True)
+            with torch.cuda.graph(g, stream=side):
+                loss = m.loss(tok, tgt)
+                loss.backward()
+                opt.step()
+            # the capture ran nothing: replay once per timed step
+            start.record()
+            for _ in range(steps):
+                g.replay()
+                losses.append(loss.detach().clone())
+            end.record()
+    torch.cuda.synchronize()
+    return [v.item() for v in losses], start.elapsed_time(end) / steps

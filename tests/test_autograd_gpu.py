@@ -69,3 +69,15 @@ def test_small_transformer_trains_like_bf16():
     assert abs(f8[0] - bf[0]) < 0.05 * bf[0]        # same initial model, same loss
     assert f8[-1] < f8[0] - 2.0 and bf[-1] < bf[0] - 2.0  # both memorize the batch
     assert abs(f8[-1] - bf[-1]) < 0.25 * bf[0]
+
+
+def test_graph_replays_match_eager_steps():
+    """The whole FP8 training step captured as one HIP graph: every replay
+    gives the loss the eager step gives (same model, same batch, same
+    optimizer state), so graph timings time the same computation."""
+    dims = dict(layers=2, d=256, heads=4, ffn=1024, vocab=1000)
+    eager, _ = E.train(E.fp8_linear, 6, DEV, graph=False, dims=dims, batch=(2, 128))
+    replay, _ = E.train(E.fp8_linear, 6, DEV, graph=True, dims=dims, batch=(2, 128))
+    assert all(math.isfinite(v) for v in replay)
+    np.testing.assert_allclose(replay, eager, rtol=1e-5, atol=1e-5)
+
