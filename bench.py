@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--workload", default="dim1536_m2048")
     p.add_argument("--kernel-reps", type=int, default=20, help="repeats of each isolated kernel timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-widened", action="store_true",
+                   help="skip the isolated timings of the entry points beyond the layer step "
+                        "(for a profile of the step alone)")
     p.add_argument("--cpu-seconds", type=float, default=25.0,
                    help="budget of the oracle sample (it stops after the linear that crosses it)")
     p.add_argument("--sweep-tiles", action="store_true",
@@ -555,7 +558,8 @@ def main():
         "per_linear": {k: {kk: round(vv, 2) for kk, vv in v.items()} for k, v in per.items()},
         "roofline": roofline,
     }
-    out["widened"] = widened_rows(torch, F, WL, wl, layers, stream, args.kernel_reps)
+    if not args.no_widened:
+        out["widened"] = widened_rows(torch, F, WL, wl, layers, stream, args.kernel_reps)
     if not args.no_cpu_baseline:
         layers_cpu = [WL.layer_inputs(wl, li) for li in range(len(wl.linears))]
         out["cpu_baseline"] = cpu_baseline(layers_cpu, args.cpu_seconds)
