@@ -239,6 +239,47 @@ FP8L_DEV void wait_vm() {
 }
 FP8L_DEV void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
+// Prologue work that does not feed the K loop: block 0's snapshot copies
+// for pre-quantized operands, the bias-gradient finalize (blocks of the first
+// tile column), and the loads of the epilogue's scales.  Kernels call it
+// after issuing their first DMA stages, so its memory latency overlaps
+// theirs instead of preceding them.  The loop's vmcnt waits stay exact:
+// loads return in issue order, and every load or store made here was issued
+// after the stage loads those waits refer to, so it can only make them
+// stricter.  The scales are only loaded here; the reciprocals are taken in
+// the epilogue (EpiScales::dq/inv_bs), so that no use of them makes the
+// prologue wait for the stage loads issued before them.
+struct EpiScales {
+  float sa, sb, bs;  // scale_a, scale_b, bias_scale for an FP8 bias (else 1)
+  FP8L_DEV float dq() const { return (1.0f / sa) * (1.0f / sb); }
+  FP8L_DEV float inv_bs() const { return 1.0f / bs; }
+};
+
+template <int BM>
+FP8L_DEV EpiScales prologue_side(const GemmArgs& g, int tn, int64_t i0) {
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+    if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
+    if (g.aux_amax_dst0) *g.aux_amax_dst0 = 0.0f;
+    if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;
+    if (g.aux_amax_dst1) *g.aux_amax_dst1 = 0.0f;
+  }
+  if (g.db && tn == 0 && tid < BM) {
+    const int64_t i = i0 + tid;
+    if (i < g.Mc) {
+      float s = 0.0f;
+      for (int r = 0; r < g.db_R; ++r) s += g.db_ws[(int64_t)r * g.Mc + i];
+      if (g.db_scale) s *= 1.0f / *g.db_scale;
+      g.db[i] = (uint16_t)f32_to_bf16(s);
+    }
+  }
+  EpiScales e;
+  e.sa = *g.scale_a;
+  e.sb = *g.scale_b;
+  e.bs = (g.bias_kind == kBiasE4M3 || g.bias_kind == kBiasE5M2) ? *g.bias_scale : 1.0f;
+  return e;
+}
+
 // One operand of the pipelined kernel.  R: tile extent along C; NW: waves.
 template <int L, int R, int NW>
 struct Op3 {
@@ -415,26 +456,6 @@ void gemm3_kernel(GemmArgs g) {
   tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
 
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
-    if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
-    if (g.aux_amax_dst0) *g.aux_amax_dst0 = 0.0f;
-    if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;
-    if (g.aux_amax_dst1) *g.aux_amax_dst1 = 0.0f;
-  }
-  if (g.db && tn == 0 && tid < BM) {
-    const int64_t i = i0 + tid;
-    if (i < g.Mc) {
-      float s = 0.0f;
-      for (int r = 0; r < g.db_R; ++r) s += g.db_ws[(int64_t)r * g.Mc + i];
-      if (g.db_scale) s *= 1.0f / *g.db_scale;
-      g.db[i] = (uint16_t)f32_to_bf16(s);
-    }
-  }
-  const float dq = (1.0f / *g.scale_a) * (1.0f / *g.scale_b);
-  const float inv_bs =
-      (g.bias_kind == kBiasE4M3 || g.bias_kind == kBiasE5M2) ? 1.0f / *g.bias_scale : 1.0f;
-  // nothing of the above may still count against vmcnt inside the loop
-  wait_vm<0>();
 
   const int64_t a_rows = (LA == kKContig) ? g.Mc : g.Kc;
   const int64_t b_rows = (LB == kKContig) ? g.Nc : g.Kc;
@@ -462,6 +483,7 @@ void gemm3_kernel(GemmArgs g) {
     oa.issue(ra, step_buf(s), s);
     ob.issue(rb, step_buf(s) + OA::kBytes, s);
   }
+  const EpiScales es = prologue_side<BM>(g, tn, i0);
   v8i fa[2][FM], fb[2][FN];
   if (nk > 0) {
     // step 0 landed: at most min(3, nk - 1) later steps still in flight
@@ -575,6 +597,7 @@ void gemm3_kernel(GemmArgs g) {
   constexpr int RS = BN * 2 + 16;  // LDS bytes per staged row
   mfma_drain();                    // accumulators are read by VALU below
   barrier_only();                  // every wave is done reading operand tiles
+  const float dq = es.dq(), inv_bs = es.inv_bs();
 #pragma unroll
   for (int b = 0; b < FN; ++b) {
 #pragma unroll

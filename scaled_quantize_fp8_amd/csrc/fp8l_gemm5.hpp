@@ -177,25 +177,6 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
   tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
 
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
-    if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
-    if (g.aux_amax_dst0) *g.aux_amax_dst0 = 0.0f;
-    if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;
-    if (g.aux_amax_dst1) *g.aux_amax_dst1 = 0.0f;
-  }
-  if (g.db && tn == 0 && tid < BM) {
-    const int64_t i = i0 + tid;
-    if (i < g.Mc) {
-      float s = 0.0f;
-      for (int r = 0; r < g.db_R; ++r) s += g.db_ws[(int64_t)r * g.Mc + i];
-      if (g.db_scale) s *= 1.0f / *g.db_scale;
-      g.db[i] = (uint16_t)f32_to_bf16(s);
-    }
-  }
-  const float dq = (1.0f / *g.scale_a) * (1.0f / *g.scale_b);
-  const float inv_bs =
-      (g.bias_kind == kBiasE4M3 || g.bias_kind == kBiasE5M2) ? 1.0f / *g.bias_scale : 1.0f;
-  wait_vm<0>();  // nothing above may count against vmcnt in the loop
 
   const int64_t a_rows = (LA == kKContig) ? g.Mc : g.Kc;
   const int64_t b_rows = (LB == kKContig) ? g.Nc : g.Kc;
@@ -247,6 +228,7 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
     load(s, J2{});
     load(s, J3{});
   }
+  const EpiScales es = prologue_side<BM>(g, tn, i0);
   if (ns > 0) {
     const int later = min(3, ns - 1);
     if (later >= 3) wait_vm<3 * kDma>();
@@ -304,6 +286,7 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
   constexpr int kXchg = 36864;  // >= BM * RS, 1 KB aligned
   static_assert(kXchg >= BM * RS && kXchg + 16 * 4096 <= 4 * 32768, "LDS split");
   mfma_drain();
+  const float dq = es.dq(), inv_bs = es.inv_bs();
   barrier_only();  // every wave's last stage reads are done
   auto xslot = [&](int a, int b, int g4) {
     return smem5 + kXchg + ((quad * 2 + a) * 2 + b) * 4096 + g4 * 1024 + lane * 16;
