@@ -12,9 +12,9 @@ Each linear is issued as fp8_quantize_pair(X, W) (one launch quantizing X
 and W with their rings), fp8_linear_fwd(X8, W8) (the GEMM), then
 fp8_linear_bwd_dw(G) (quantize G with column partials, then the dW GEMM
 with db) and fp8_linear_bwd_dx(G8) (the dX GEMM): the kernels the one-call
-fp8_linear_fwd(X, W) launches, with each GEMM a call of its own so that the
-forward and dX GEMM launches can be bracketed with events in the timed
-region for the roofline entry.
+fp8_linear_fwd(X, W) launches, with each GEMM a call of its own so that a
+forward or dX GEMM launch can be bracketed with events in the timed region
+for the roofline entry (one launch per step, rotating over the linears).
 
 Prints one JSON line (see the fields below).  --gpus N > 1 is refused: this
 benchmark measures one GPU.
@@ -443,22 +443,24 @@ def main():
     q_bytes = sum(L.quant_bytes(w) for L in layers for w in ("X", "W", "G"))
     quant_gbps = q_bytes / (q_us * 1e-6) / 1e9
 
-    # ---- timed region: exactly args.steps eager steps.  The launches of the
-    # GEMM kind that dominates the isolated timings (forward or dX: each a
-    # one-kernel call) are bracketed with events on the stream they run on;
-    # the event pairs are created up front, outside the timed region.
+    # ---- timed region: exactly args.steps eager steps.  In step s the launch
+    # of the GEMM kind that dominates the isolated timings (forward or dX:
+    # each a one-kernel call) of linear s mod 5 is bracketed with events on
+    # the stream it runs on, so over the steps every linear's launch is timed
+    # live while each step carries one event pair (an event record costs a
+    # few microseconds of the stream's time).  The event pairs are created up
+    # front, outside the timed region.
     dom = "fwd" if tot["fwd"] >= tot["dx"] else "dx"
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps * len(layers))]
-    ev_i = 0
+          for _ in range(args.steps)]
+    ev_layer = []
 
-    def run(kind, fn):
-        nonlocal ev_i
-        if kind != dom:
+    def run(kind, fn, step_i, li):
+        if kind != dom or li != step_i % len(layers):
             fn()
             return
-        a, b_ = ev[ev_i]
-        ev_i += 1
+        a, b_ = ev[step_i]
+        ev_layer.append(li)
         a.record(stream)
         fn()
         b_.record(stream)
@@ -469,12 +471,12 @@ def main():
     wall0 = time.perf_counter()
     with torch.cuda.stream(stream):
         t_start.record(stream)
-        for _ in range(args.steps):
-            for L in layers:
+        for si in range(args.steps):
+            for li, L in enumerate(layers):
                 L.quant_xw()
-                run("fwd", L.gemm_fwd)
+                run("fwd", L.gemm_fwd, si, li)
                 L.bwd_dw()
-                run("dx", L.bwd_dx)
+                run("dx", L.bwd_dx, si, li)
         t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -483,11 +485,18 @@ def main():
     step_flops = sum(3 * L.flops for L in layers)
     tflops = step_flops / (ms_per_step * 1e-3) / 1e12
 
-    # live launch durations of the dominant kind: average over its launches
-    # (the five linears' shapes in step order), with the matching flops
+    # live launch durations of the dominant kind: average over the bracketed
+    # launches, with the average flops of the same launches; per step, the
+    # sum over the linears of each one's average live duration
     live_ms = [a.elapsed_time(b_) for a, b_ in ev]
-    live = {"avg_ms": sum(live_ms) / len(live_ms), "total_ms": sum(live_ms) / args.steps,
-            "flops": sum(L.flops for L in layers) / len(layers)}
+    by_layer = {}
+    for li, ms in zip(ev_layer, live_ms):
+        by_layer.setdefault(li, []).append(ms)
+    live = {"avg_ms": sum(live_ms) / len(live_ms),
+            "total_ms": (sum(sum(v) / len(v) for v in by_layer.values())
+                         if len(by_layer) == len(layers) else None),
+            "flops": sum(layers[li].flops for li in ev_layer) / len(ev_layer),
+            "launches": len(live_ms)}
 
     # ---- the same step captured as one HIP graph and replayed
     graph_ms_per_step = None
@@ -526,7 +535,9 @@ def main():
                 "kernel": kernel_names[dom],
                 "launch_avg_us": round(live["avg_ms"] * 1e3, 2),
                 "flops_per_launch": live["flops"],
-                "live_us_per_step": round(live["total_ms"] * 1e3, 1),
+                "live_launches": live["launches"],
+                "live_us_per_step": (None if live["total_ms"] is None
+                                     else round(live["total_ms"] * 1e3, 1)),
                 "isolated_gemm_us_per_step": {k: round(v, 1) for k, v in tot.items()},
                 "dominant_gemm_by_isolated_totals": dominant_isolated}
 

@@ -240,8 +240,8 @@ FP8L_DEV void wait_vm() {
 FP8L_DEV void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
 // Prologue work that does not feed the K loop: block 0's snapshot copies
-// for pre-quantized operands, the bias-gradient finalize (blocks of the first
-// tile column), and the loads of the epilogue's scales.  Kernels call it
+// for pre-quantized operands, the bias-gradient finalize (shared by all
+// blocks), and the loads of the epilogue's scales.  Kernels call it
 // after issuing their first DMA stages, so its memory latency overlaps
 // theirs instead of preceding them.  The loop's vmcnt waits stay exact:
 // loads return in issue order, and every load or store made here was issued
@@ -255,8 +255,7 @@ struct EpiScales {
   FP8L_DEV float inv_bs() const { return 1.0f / bs; }
 };
 
-template <int BM>
-FP8L_DEV EpiScales prologue_side(const GemmArgs& g, int tn, int64_t i0) {
+FP8L_DEV EpiScales prologue_side(const GemmArgs& g) {
   const int tid = threadIdx.x;
   if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
@@ -264,13 +263,28 @@ FP8L_DEV EpiScales prologue_side(const GemmArgs& g, int tn, int64_t i0) {
     if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;
     if (g.aux_amax_dst1) *g.aux_amax_dst1 = 0.0f;
   }
-  if (g.db && tn == 0 && tid < BM) {
-    const int64_t i = i0 + tid;
-    if (i < g.Mc) {
+  if (g.db) {
+    // Every block takes a share of the Mc sums: 16 lanes per entry, lane
+    // q adding partial rows q, q + 16, ...; the 16 sums meet in a fixed
+    // xor tree, so the result does not depend on the launch shape's timing.
+    // (One thread per entry walking all db_R rows made the blocks that did
+    // it the launch's last by many microseconds.)
+    const int64_t nblk = (int64_t)gridDim.x * gridDim.y;
+    const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int per = (int)blockDim.x / 16;  // entries per block and pass
+    const int q = tid & 15;
+    for (int64_t i = b * per + tid / 16; i - tid / 16 < g.Mc; i += nblk * per) {
       float s = 0.0f;
-      for (int r = 0; r < g.db_R; ++r) s += g.db_ws[(int64_t)r * g.Mc + i];
-      if (g.db_scale) s *= 1.0f / *g.db_scale;
-      g.db[i] = (uint16_t)f32_to_bf16(s);
+      if (i < g.Mc)
+        for (int r = q; r < g.db_R; r += 16) s += g.db_ws[(int64_t)r * g.Mc + i];
+      s += __shfl_xor(s, 1, 16);
+      s += __shfl_xor(s, 2, 16);
+      s += __shfl_xor(s, 4, 16);
+      s += __shfl_xor(s, 8, 16);
+      if (q == 0 && i < g.Mc) {
+        if (g.db_scale) s *= 1.0f / *g.db_scale;
+        g.db[i] = (uint16_t)f32_to_bf16(s);
+      }
     }
   }
   EpiScales e;
@@ -483,7 +497,7 @@ void gemm3_kernel(GemmArgs g) {
     oa.issue(ra, step_buf(s), s);
     ob.issue(rb, step_buf(s) + OA::kBytes, s);
   }
-  const EpiScales es = prologue_side<BM>(g, tn, i0);
+  const EpiScales es = prologue_side(g);
   v8i fa[2][FM], fb[2][FN];
   if (nk > 0) {
     // step 0 landed: at most min(3, nk - 1) later steps still in flight

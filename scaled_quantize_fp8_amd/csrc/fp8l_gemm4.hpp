@@ -245,7 +245,7 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
 
   // prologue: DMA steps 0..3, read step 0, issue its first two MFMAs
   for (int s = 0; s < kStages3 && s <= nk; ++s) issue_step(s);
-  const EpiScales es = prologue_side<BM>(g, tn, i0);
+  const EpiScales es = prologue_side(g);
   if (nk > 0) {
     const int later = min(3, nk);  // steps 1..min(3, nk) may still be in flight
     if (later >= 3) wait_vm<3 * kDma>();

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
     load(s, J2{});
     load(s, J3{});
   }
-  const EpiScales es = prologue_side<BM>(g, tn, i0);
+  const EpiScales es = prologue_side(g);
   if (ns > 0) {
     const int later = min(3, ns - 1);
     if (later >= 3) wait_vm<3 * kDma>();
