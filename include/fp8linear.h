@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FP8_ABI_VERSION 1
+#define FP8_ABI_VERSION 2
 #define FP8_RING_MAX_HIST 1024
 
 typedef enum {
@@ -126,7 +126,7 @@ int fp8_abi_version(void);
 /* Static description of a status code. */
 const char* fp8_status_str(int status);
 
-/* Bytes of a ring's device buffer: 2176 + 4 * hist_len (0 if out of range). */
+/* Bytes of a ring's device buffer: 8320 + 4 * hist_len (0 if out of range). */
 size_t fp8_ring_bytes(int32_t hist_len);
 
 /*

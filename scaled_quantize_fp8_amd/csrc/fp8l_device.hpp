@@ -35,10 +35,10 @@ struct FmtTraits<kE5M2> {
   static constexpr float kMax = 57344.0f;
 };
 
-// Ring buffer in device memory: a 128-byte header, 16 election groups of
+// Ring buffer in device memory: a 128-byte header, 64 election groups of
 // 128 bytes (each on its own cache line so the blocks of different groups
 // never contend for one address), then float hist[H].
-constexpr int kGroups = 16;
+constexpr int kGroups = 64;
 struct RingGroup {
   uint32_t count;      // blocks of this group that finished (0 between launches)
   uint32_t pad0[15];
@@ -57,7 +57,7 @@ struct RingHdr {
   RingGroup group[kGroups];
 };
 static_assert(sizeof(RingGroup) == 128, "one election group per 128-byte line");
-static_assert(sizeof(RingHdr) == 128 + 16 * 128, "ring header layout");
+static_assert(sizeof(RingHdr) == 128 + 64 * 128, "ring header layout");
 
 // ---------------------------------------------------------------- scale
 

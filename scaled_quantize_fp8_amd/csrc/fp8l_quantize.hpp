@@ -12,12 +12,14 @@
 // Last-block election without contention: a single counter hit by thousands
 // of blocks serializes at roughly 11 ns per device atomic on MI355X, and an
 // agent-scope acquire/release around it writes back and invalidates the L2.
-// Instead the blocks are split into 16 groups, each with its own cache line
+// Instead the blocks are split into 64 groups, each with its own cache line
 // holding a counter and a running max.  A block folds its max into its group
-// and takes a group ticket; the group's last block forwards the group max to
-// the header and takes a header ticket; the 16th header ticket is the
-// launch's last block, which folds amax into hist[idx], takes the window max,
-// publishes the next scale and leaves every counter at zero.
+// and takes a group ticket; the group's last block takes a header ticket;
+// the last header ticket is the launch's last block, which collects the 64
+// group maxima in one parallel round of atomics, folds amax into hist[idx],
+// takes the window max, publishes the next scale and leaves every counter
+// and max at zero.  The launch's last block waits on four dependent device
+// atomics after its data (max, group ticket, header ticket, collection).
 //
 // The column-sum variant walks G [rows, cols] by column strips and row
 // chunks and also writes fp32 partial column sums (the bias gradient of
@@ -144,12 +146,11 @@ FP8L_DEV uint32_t block_max_u32(uint32_t v, uint32_t* sh4) {
   return r;
 }
 
-// Two-level last-block election (thread 0 only), in two halves so that a
-// block that wins its group can prefetch the window between them.
-// Group level: fold bm (this block's max |x| bits) into the block's group;
-// true in the group's last block, which receives the group max in *gm and
-// leaves the group's counter and max at zero.
-FP8L_DEV bool elect_group(RingHdr* h, uint32_t bid, uint32_t total, uint32_t bm, uint32_t* gm) {
+// Two-level last-block election.  Group level (thread 0): fold bm (this
+// block's max |x| bits) into the block's group max, then take a group
+// ticket; true in the group's last block, which resets the group counter.
+// The group max stays in place for the launch's last block to collect.
+FP8L_DEV bool elect_group(RingHdr* h, uint32_t bid, uint32_t total, uint32_t bm) {
   const uint32_t G = total < (uint32_t)kGroups ? total : (uint32_t)kGroups;
   const uint32_t g = bid % G;
   const uint32_t gsize = (total - g + G - 1) / G;
@@ -157,31 +158,32 @@ FP8L_DEV bool elect_group(RingHdr* h, uint32_t bid, uint32_t total, uint32_t bm,
   if (bm) atom_max(&grp->amax, bm);
   wait_vmem();  // the max is performed before the ticket is taken
   if (atom_add(&grp->count, 1u) != gsize - 1) return false;
-  // last block of its group: every block of the group has folded its max
-  *gm = atom_xchg(&grp->amax, 0u);
   atom_xchg(&grp->count, 0u);
   return true;
 }
 
-// Top level, for group winners: true in the launch's last block, which gets
-// the launch max in *amax.  consume: clear the header max (the last block
-// folds it) or leave it for the next launch (the amax pass of a seeding
-// quantize).
-FP8L_DEV bool elect_top(RingHdr* h, uint32_t total, uint32_t gm, bool consume, uint32_t* amax) {
+// Top level (thread 0 of a group's last block): true in the launch's last
+// block, which resets the top counter.
+FP8L_DEV bool elect_top(RingHdr* h, uint32_t total) {
   const uint32_t G = total < (uint32_t)kGroups ? total : (uint32_t)kGroups;
-  if (gm) atom_max(&h->top_amax, gm);
-  wait_vmem();
   if (atom_add(&h->top_count, 1u) != G - 1) return false;
   atom_xchg(&h->top_count, 0u);
-  *amax = consume ? atom_xchg(&h->top_amax, 0u) : atom_read(&h->top_amax);
   return true;
 }
 
-FP8L_DEV bool elect_last(RingHdr* h, uint32_t bid, uint32_t total, uint32_t bm, bool consume,
-                         uint32_t* amax) {
-  uint32_t gm = 0;
-  if (!elect_group(h, bid, total, bm, &gm)) return false;
-  return elect_top(h, total, gm, consume, amax);
+// The launch max, in the launch's last block (every thread calls it): one
+// lane per group takes its max and leaves 0 behind, all in one round trip.
+// Every group's max was performed before its last block's group ticket,
+// and that ticket before the top ticket that made this block the last.
+// consume: also take (and clear) the header max that the amax pass of a
+// seeding quantize leaves for the converting launch.
+FP8L_DEV uint32_t gather_amax(RingHdr* h, uint32_t total, bool consume, uint32_t* sh4) {
+  const uint32_t G = total < (uint32_t)kGroups ? total : (uint32_t)kGroups;
+  static_assert(kGroups < kQThreads, "one lane per group plus one");
+  uint32_t m = 0;
+  if (threadIdx.x < G) m = atom_xchg(&h->group[threadIdx.x].amax, 0u);
+  else if (consume && threadIdx.x == G) m = atom_xchg(&h->top_amax, 0u);
+  return block_max_u32(m, sh4);
 }
 
 // Scale the launch quantizes with.
@@ -208,17 +210,13 @@ FP8L_DEV float launch_scale(const QArgs& a) {
 template <int FMT, int SMODE>
 FP8L_DEV void finish_launch(const QArgs& a, uint32_t mx, float s, uint32_t bid, uint32_t total) {
   __shared__ uint32_t sh4[4];
-  __shared__ uint32_t sh_flag, sh_gm, sh_amax;
+  __shared__ uint32_t sh_flag;
   if constexpr (SMODE == kScaleDyn) {
     if (bid == 0 && threadIdx.x == 0) *a.scale_used = s;
     return;
   } else {
     const uint32_t bm = block_max_u32(mx, sh4);
-    if (threadIdx.x == 0) {
-      uint32_t gm = 0;
-      sh_flag = elect_group(a.ring, bid, total, bm, &gm) ? 1u : 0u;
-      sh_gm = gm;
-    }
+    if (threadIdx.x == 0) sh_flag = elect_group(a.ring, bid, total, bm) ? 1u : 0u;
     __syncthreads();
     if (!sh_flag) return;
     // A group winner may be the launch's last block: load the window and its
@@ -234,14 +232,10 @@ FP8L_DEV void finish_launch(const QArgs& a, uint32_t mx, float s, uint32_t bid, 
     }
     const uint32_t idx = a.ring->idx % (uint32_t)H;  // in range even for a corrupted header
     __syncthreads();  // every thread has read sh_flag before it is reused
-    if (threadIdx.x == 0) {
-      uint32_t am = 0;
-      sh_flag = elect_top(a.ring, total, sh_gm, true, &am) ? 1u : 0u;
-      sh_amax = am;
-    }
+    if (threadIdx.x == 0) sh_flag = elect_top(a.ring, total) ? 1u : 0u;
     __syncthreads();
     if (!sh_flag) return;
-    const uint32_t amax_bits = sh_amax;
+    const uint32_t amax_bits = gather_amax(a.ring, total, true, sh4);
     uint32_t m = 0;
 #pragma unroll
     for (int k = 0; k < FP8_RING_MAX_HIST / kQThreads; ++k) {
@@ -471,11 +465,14 @@ template <int IN>
 __global__ __launch_bounds__(kQThreads) void amax_ring_kernel(const void* x, int64_t n, int vec_ok,
                                                              RingHdr* h) {
   __shared__ uint32_t sh4[4];
+  __shared__ uint32_t sh_flag;
   const uint32_t bm = block_max_u32(flat_absmax<IN>(x, n, vec_ok), sh4);
-  if (threadIdx.x == 0) {
-    uint32_t am;
-    elect_last(h, blockIdx.x, gridDim.x, bm, false, &am);
-  }
+  if (threadIdx.x == 0)
+    sh_flag = (elect_group(h, blockIdx.x, gridDim.x, bm) && elect_top(h, gridDim.x)) ? 1u : 0u;
+  __syncthreads();
+  if (!sh_flag) return;
+  const uint32_t amax_bits = gather_amax(h, gridDim.x, false, sh4);
+  if (threadIdx.x == 0) atom_xchg(&h->top_amax, amax_bits);
 }
 
 // amax pass of a dynamic quantize: one device atomic max per block into

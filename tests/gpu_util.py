@@ -47,11 +47,16 @@ def f32_scalar(t: torch.Tensor) -> np.float32:
     return np.float32(t.detach().to("cpu").numpy().reshape(-1)[0])
 
 
+# device ring layout: 128-byte header, 64 election groups of 128 bytes, hist
+RING_GROUPS = 64
+RING_HDR_BYTES = 128 + 128 * RING_GROUPS
+
+
 def ring_state(ring) -> dict:
     """Read a device ring back: scale, idx, hist, amax_acc, counter, seeded."""
     b = ring.buf.detach().to("cpu").numpy()
     hdr = b[:128].view(np.uint32)
-    groups = b[128:2176].view(np.uint32).reshape(16, 32)
+    groups = b[128:RING_HDR_BYTES].view(np.uint32).reshape(RING_GROUPS, 32)
     H = int(hdr[4])
     return {
         "scale": b[:4].view(np.float32)[0],
@@ -62,7 +67,7 @@ def ring_state(ring) -> dict:
         "seeded": int(hdr[5]),
         "group_count": groups[:, 0].copy(),
         "group_amax": groups[:, 16].copy(),
-        "hist": b[2176:2176 + 4 * H].view(np.float32).copy(),
+        "hist": b[RING_HDR_BYTES:RING_HDR_BYTES + 4 * H].view(np.float32).copy(),
     }
 
 

@@ -45,15 +45,15 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8_abi_version() == 1
+    assert F.fp8_abi_version() == 2
     for st in range(6):
         assert F.status_str(st)
     assert F.status_str(99) == "unknown status"
 
 
 def test_sizes(lib):
-    assert F.fp8_ring_bytes(16) == 2176 + 64
-    assert F.fp8_ring_bytes(1024) == 2176 + 4096
+    assert F.fp8_ring_bytes(16) == 8320 + 64
+    assert F.fp8_ring_bytes(1024) == 8320 + 4096
     assert F.fp8_ring_bytes(0) == 0 and F.fp8_ring_bytes(1025) == 0
     assert F.fp8_db_workspace_bytes(2048, 6912) == 4 * 64 * 6912
     assert F.fp8_db_workspace_bytes(33, 10) == 4 * 2 * 10
