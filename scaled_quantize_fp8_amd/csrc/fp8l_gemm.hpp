@@ -178,6 +178,32 @@ FP8L_DEV float bias_at(const GemmArgs& g, int64_t j, float inv_bs) {
 
 // Tile order: groups of 8 tile-rows walk the tile-columns so the blocks
 // resident together share A rows and B columns in L2.
+// Bias-gradient finalize, db[i] = bf16(mult * sum_r ws[r][i]), shared by all
+// blocks of the launch: 16 lanes per entry, lane q adding partial rows q,
+// q + 16, ...; the 16 sums meet in a fixed xor tree, so the result does not
+// depend on the launch shape.  Every thread of the block calls it (the
+// shuffles need whole 16-lane groups; the loop's trip count is uniform).
+FP8L_DEV void db_finalize(const GemmArgs& g) {
+  const int tid = threadIdx.x;
+  const int64_t nblk = (int64_t)gridDim.x * gridDim.y;
+  const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int per = (int)blockDim.x / 16;  // entries per block and pass
+  const int q = tid & 15;
+  for (int64_t i = b * per + tid / 16; i - tid / 16 < g.Mc; i += nblk * per) {
+    float s = 0.0f;
+    if (i < g.Mc)
+      for (int r = q; r < g.db_R; r += 16) s += g.db_ws[(int64_t)r * g.Mc + i];
+    s += __shfl_xor(s, 1, 16);
+    s += __shfl_xor(s, 2, 16);
+    s += __shfl_xor(s, 4, 16);
+    s += __shfl_xor(s, 8, 16);
+    if (q == 0 && i < g.Mc) {
+      if (g.db_scale) s *= 1.0f / *g.db_scale;
+      g.db[i] = (uint16_t)f32_to_bf16(s);
+    }
+  }
+}
+
 FP8L_DEV void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int G = 8;
   const int per_group = G * tiles_n;
@@ -208,16 +234,7 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_kernel(GemmArgs g) {
     if (g.aux_amax_dst1) *g.aux_amax_dst1 = 0.0f;
   }
 
-  // bias-gradient finalize by the blocks of the first tile column
-  if (g.db && tn == 0 && tid < kBM) {
-    const int64_t i = i0 + tid;
-    if (i < g.Mc) {
-      float s = 0.0f;
-      for (int r = 0; r < g.db_R; ++r) s += g.db_ws[(int64_t)r * g.Mc + i];
-      if (g.db_scale) s *= 1.0f / *g.db_scale;
-      g.db[i] = (uint16_t)f32_to_bf16(s);
-    }
-  }
+  if (g.db) db_finalize(g);
 
   const int wm = wave >> 1, wn = wave & 1;
   v4f acc[4][4];

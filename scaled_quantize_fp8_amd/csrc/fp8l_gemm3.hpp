@@ -263,30 +263,9 @@ FP8L_DEV EpiScales prologue_side(const GemmArgs& g) {
     if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;
     if (g.aux_amax_dst1) *g.aux_amax_dst1 = 0.0f;
   }
-  if (g.db) {
-    // Every block takes a share of the Mc sums: 16 lanes per entry, lane
-    // q adding partial rows q, q + 16, ...; the 16 sums meet in a fixed
-    // xor tree, so the result does not depend on the launch shape's timing.
-    // (One thread per entry walking all db_R rows made the blocks that did
-    // it the launch's last by many microseconds.)
-    const int64_t nblk = (int64_t)gridDim.x * gridDim.y;
-    const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-    const int per = (int)blockDim.x / 16;  // entries per block and pass
-    const int q = tid & 15;
-    for (int64_t i = b * per + tid / 16; i - tid / 16 < g.Mc; i += nblk * per) {
-      float s = 0.0f;
-      if (i < g.Mc)
-        for (int r = q; r < g.db_R; r += 16) s += g.db_ws[(int64_t)r * g.Mc + i];
-      s += __shfl_xor(s, 1, 16);
-      s += __shfl_xor(s, 2, 16);
-      s += __shfl_xor(s, 4, 16);
-      s += __shfl_xor(s, 8, 16);
-      if (q == 0 && i < g.Mc) {
-        if (g.db_scale) s *= 1.0f / *g.db_scale;
-        g.db[i] = (uint16_t)f32_to_bf16(s);
-      }
-    }
-  }
+  // (One thread per entry walking all db_R rows, in the first tile column's
+  // blocks only, made those blocks the launch's last by many microseconds.)
+  if (g.db) db_finalize(g);
   EpiScales e;
   e.sa = *g.scale_a;
   e.sb = *g.scale_b;
