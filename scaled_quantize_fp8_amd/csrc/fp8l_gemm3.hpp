@@ -310,6 +310,29 @@ struct Op3 {
     }
     inlim = (L == kKContig) ? klim : rlim;
     kstep = (L == kKContig) ? (uint32_t)kBK3 : (uint32_t)(kBK3 * ld);
+    if constexpr (L != kKContig) {
+      // columns past the edge: an offset past every resource (loop-invariant)
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i)
+        if ((int64_t)inner[i] >= inlim) base[i] = 0x80000000u;
+    }
+  }
+
+  // DMA instruction I of a K step that lies wholly inside K, through the
+  // resource over the whole operand: the lane's fixed offset, and the step's
+  // advance soff (uniform) as the instruction's scalar offset.  The range
+  // check sees only the lane's offset, which is enough here: rows past the
+  // operand's last one and columns past its edge (whose offsets init set to
+  // 2^31) have offsets past the range and read zeros, and every other byte
+  // the step reads lies inside the operand because the step ends at or
+  // before K.  Against issue_step this drops the per-step resource and the
+  // per-lane K test and select.
+  template <int I>
+  FP8L_DEV void issue_full(__amdgpu_buffer_rsrc_t rs, uint8_t* s, uint32_t soff, int wave) const {
+    const uint32_t voff = base[I];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(s + (wave * kPerWave + I) * 1024), 16, voff,
+        soff, 0, 0);
   }
 
   // DMA instruction i of K step kt into the step buffer at s.

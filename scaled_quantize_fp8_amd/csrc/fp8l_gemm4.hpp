@@ -261,10 +261,20 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
 
   // Step kt: on entry MFMAs (a0, *) of step kt are issued; fa holds step kt's
   // A fragments, fb[CUR] its B fragments.
-  auto kstep_body = [&](int kt, auto cur_tag) {
+  // FAST: the refill of this step (step kt+4) lies wholly inside K, so its
+  // loads take the whole-operand resources with the advance as scalar
+  // offset (issue_full), the refill is
+  // unconditional and the wait count is fixed; the last steps take the
+  // general form (partial step, the zero step past K, no refill).
+  const __amdgpu_buffer_rsrc_t ra_all = make_rsrc(g.a, a_bytes);
+  const __amdgpu_buffer_rsrc_t rb_all = make_rsrc(g.b, b_bytes);
+  auto kstep_body = [&](int kt, auto cur_tag, auto fast_tag) {
     constexpr int CUR = decltype(cur_tag)::value;
     constexpr int NXT = CUR ^ 1;
-    {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    if constexpr (FAST) {
+      wait_vm<2 * kDma>();
+    } else {
       // step kt+1 landed: later steps kt+2 .. min(kt+3, nk) may be in flight
       const int later = min(2, nk - kt - 1);
       if (later >= 2) wait_vm<2 * kDma>();
@@ -272,14 +282,19 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
       else wait_vm<0>();
     }
     barrier_only();  // step kt+1 visible to all; step kt's buffer is free
-    const bool refill = kt + kStages3 <= nk;
+    const bool refill = FAST || kt + kStages3 <= nk;
     const int kf = kt + kStages3;
     uint8_t* const sf = step_buf(kf);
-    const __amdgpu_buffer_rsrc_t ra_k = oa.step_rsrc(g.a, a_bytes, kf);
-    const __amdgpu_buffer_rsrc_t rb_k = ob.step_rsrc(g.b, b_bytes, kf);
     auto load = [&](auto j_tag) {
       constexpr int j = decltype(j_tag)::value;
-      if (refill) {
+      if constexpr (FAST) {
+        if constexpr (j < OA::kPerWave)
+          oa.template issue_full<j>(ra_all, sf, (uint32_t)kf * oa.kstep, wv);
+        else
+          ob.template issue_full<j - OA::kPerWave>(rb_all, sf + OA::kBytes, (uint32_t)kf * ob.kstep, wv);
+      } else if (refill) {
+        const __amdgpu_buffer_rsrc_t ra_k = oa.step_rsrc(g.a, a_bytes, kf);
+        const __amdgpu_buffer_rsrc_t rb_k = ob.step_rsrc(g.b, b_bytes, kf);
         if constexpr (j < OA::kPerWave)
           oa.template issue_step<j>(ra_k, sf, kf, wv);
         else
@@ -328,9 +343,19 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
       readA(I3{}, fa[3], m, I2{});
     }
   };
-  for (int kt = 0; kt < nk; kt += 2) {
-    kstep_body(kt, std::integral_constant<int, 0>{});
-    kstep_body(kt + 1, std::integral_constant<int, 1>{});
+  // steps whose refill (step kt+4) ends at or before K: kt + 4 < nf, with
+  // nf the number of whole 64-byte K steps; an even count, as the loop
+  // below takes two steps per iteration
+  const int nf = (int)(g.Kc / kBK3);
+  const int kfast = max(0, min(nk, nf - kStages3)) & ~1;
+  int kt = 0;
+  for (; kt < kfast; kt += 2) {
+    kstep_body(kt, std::integral_constant<int, 0>{}, std::true_type{});
+    kstep_body(kt + 1, std::integral_constant<int, 1>{}, std::true_type{});
+  }
+  for (; kt < nk; kt += 2) {
+    kstep_body(kt, std::integral_constant<int, 0>{}, std::false_type{});
+    kstep_body(kt + 1, std::integral_constant<int, 1>{}, std::false_type{});
   }
   wait_vm<0>();  // the DMA of step nk (zeros) must not land in the staging area
 
