@@ -99,15 +99,15 @@ FP8L_DEV void kc1o(uint32_t a0, uint32_t a1, v8i& n0, const MfmaSlot (&m)[4]) {
   n0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 }
 
-// k-contiguous fragment pair at offsets 0 and 2048
-template <int FA, int FB, int NM>
+// k-contiguous fragment pair at offsets 0 and D1
+template <int FA, int FB, int NM, int D1 = 2048>
 FP8L_DEV void kc2o(uint32_t a0, uint32_t a1, v8i& n0, v8i& n1, const MfmaSlot (&m)[4]) {
   v4i r0, r1, r2, r3;
 #define FP8L_KC2O(n)                                                                           \
   asm volatile(FP8L_RKC(r0, a0, o0) FP8L_RKC(r1, a1, o0) FP8L_RKC(r2, a0, o1)                  \
                    FP8L_RKC(r3, a1, o1) FP8L_MF##n "s_waitcnt lgkmcnt(0)"                      \
                : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3), FP8L_CO##n     \
-               : [a0] "v"(a0), [a1] "v"(a1), [o0] "n"(0), [o1] "n"(2048), FP8L_CI##n, FP8L_FMT \
+               : [a0] "v"(a0), [a1] "v"(a1), [o0] "n"(0), [o1] "n"(D1), FP8L_CI##n, FP8L_FMT   \
                : "memory")
   if constexpr (NM == 1) FP8L_KC2O(1);
   else if constexpr (NM == 2) FP8L_KC2O(2);

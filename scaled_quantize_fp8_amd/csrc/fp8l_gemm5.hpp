@@ -64,7 +64,12 @@ FP8L_DEV void read1(const uint8_t* s, int f, v8i& n0) {
 //   kLoads        DMA instructions per wave per stage
 //   sub(x, s)     base of sub-step s inside the stage region x
 //   frag_addrs    lane addresses of a fragment pair in a sub-step
+//   pair_base     the two address registers read_at takes for that pair
+//   read_at       the pair's reads at those addresses plus a stage offset,
+//                 fused with NM MFMAs
 //   load<J>       DMA instruction J of stage st into the stage region
+//   load_full<J>  the same for a stage that lies wholly inside K, through
+//                 the resource over the whole operand (see Op3::issue_full)
 template <int L, int R, int NW>
 struct Stage128;
 
@@ -108,6 +113,14 @@ struct Stage128<kKContig, R, NW> {
         0, 0);
   }
 
+  template <int J>
+  FP8L_DEV void load_full(__amdgpu_buffer_rsrc_t rs, uint8_t* x, int st, int wave) const {
+    const uint32_t voff = base[J];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(x + (wave * kLoads + J) * 1024), 16, voff,
+        (uint32_t)st * (2 * kBK3), 0, 0);
+  }
+
   FP8L_DEV static const uint8_t* sub(const uint8_t* x, int s) { return x + 512 * s; }
 
   FP8L_DEV static uint32_t row_off(int r) { return ((r >> 3) << 10) + ((r & 7) << 6); }
@@ -125,12 +138,19 @@ struct Stage128<kKContig, R, NW> {
     }
   }
 
-  template <int FA, int FB, int NM>
-  FP8L_DEV static void read2_fused(const uint8_t* s, int f0, v8i& n0, v8i& n1,
-                                   const MfmaSlot (&m)[4]) {
+  // the two chunk addresses of fragment f0; fragment f0 + 32 lies 4096
+  // bytes further (4 blocks of 8 rows, same swizzle)
+  FP8L_DEV static void pair_base(const uint8_t* s, int f0, uint32_t b[2]) {
     uint32_t a[8];
     frag_addrs(s, f0, a);
-    fused_kc<FA, FB, NM>(a, n0, n1, m);
+    b[0] = a[0];
+    b[1] = a[1];
+  }
+
+  template <int FA, int FB, int NM>
+  FP8L_DEV static void read_at(const uint32_t b[2], uint32_t d, v8i& n0, v8i& n1,
+                               const MfmaSlot (&m)[4]) {
+    kc2o<FA, FB, NM, 4096>(b[0] + d, b[1] + d, n0, n1, m);
   }
 
   FP8L_DEV static void read2(const uint8_t* s, int f0, v8i& x0, v8i& x1) {
@@ -158,7 +178,28 @@ struct Stage128<kCross, R, NW> : Op3<kCross, R, NW> {
     this->template issue_one<0>(rs, x + J * Base::kBytes, 2 * st + J);
   }
 
+  template <int J>
+  FP8L_DEV void load_full(__amdgpu_buffer_rsrc_t rs, uint8_t* x, int st, int wave) const {
+    this->template issue_full<0>(rs, x + J * Base::kBytes, (uint32_t)(2 * st + J) * this->kstep,
+                                 wave);
+  }
+
   FP8L_DEV static const uint8_t* sub(const uint8_t* x, int s) { return x + Base::kBytes * s; }
+
+  // one base per fragment (f0 and f0 + 32); a fragment's four transpose
+  // reads lie 8 R bytes apart
+  FP8L_DEV static void pair_base(const uint8_t* s, int f0, uint32_t b[2]) {
+    uint32_t a[8];
+    Base::frag_addrs(s, f0, a);
+    b[0] = a[0];
+    b[1] = a[4];
+  }
+
+  template <int FA, int FB, int NM>
+  FP8L_DEV static void read_at(const uint32_t b[2], uint32_t d, v8i& n0, v8i& n1,
+                               const MfmaSlot (&m)[4]) {
+    x2o<FA, FB, NM, 8 * R>(b[0] + d, b[1] + d, n0, n1, m);
+  }
 };
 
 template <int LA, int LB, int FA, int FB>
@@ -213,6 +254,14 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
     else
       ob.template load<(j >> 1)>(rb, b + OA::kBytes, st, wv);
   };
+  auto load_full = [&](int st, auto j_tag) {
+    constexpr int j = decltype(j_tag)::value;
+    uint8_t* const b = stage_buf(st);
+    if constexpr ((j & 1) == 0)
+      oa.template load_full<(j >> 1)>(ra, b, st, wv);
+    else
+      ob.template load_full<(j >> 1)>(rb, b + OA::kBytes, st, wv);
+  };
   using J0 = std::integral_constant<int, 0>;
   using J1 = std::integral_constant<int, 1>;
   using J2 = std::integral_constant<int, 2>;
@@ -240,41 +289,67 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
     OB::read2(OB::sub(stage_buf(0) + OA::kBytes, kq), rb0, fb[0][0], fb[0][1]);
   }
 
+  // this wave's fragment address registers in stage 0 (sub-step kq); a
+  // stage adds its byte offset
+  uint32_t pa[2], pb[2];
+  OA::pair_base(OA::sub(smem5, kq), ra0, pa);
+  OB::pair_base(OB::sub(smem5 + OA::kBytes, kq), rb0, pb);
+
   // Stage st: fa/fb[CUR] hold its fragments; two read blocks fetch stage
   // st+1's into [NXT], each carrying two of stage st's four MFMAs.
-  auto stage_body = [&](int st, auto cur_tag) {
+  // FAST: the refill (stage st+4) lies wholly inside K, so it is
+  // unconditional, takes load_full and the wait count is fixed; the last
+  // stages take the general form (partial stage, zero stages, no refill).
+  auto stage_body = [&](int st, auto cur_tag, auto fast_tag) {
     constexpr int CUR = decltype(cur_tag)::value;
     constexpr int NXT = CUR ^ 1;
-    {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    if constexpr (FAST) {
+      wait_vm<2 * kDma>();
+    } else {
       const int later = min(2, ns - 2 - st);
       if (later >= 2) wait_vm<2 * kDma>();
       else if (later == 1) wait_vm<kDma>();
       else wait_vm<0>();
     }
     barrier_only();  // stage st+1 visible to all; stage st's buffer is free
-    const bool refill = st + kStages3 < ns;
-    const uint8_t* const nb = stage_buf(st + 1);
+    const bool refill = FAST || st + kStages3 < ns;
+    const uint32_t d = (uint32_t)(((st + 1) % kStages3) * kStage);
+    auto refill2 = [&](auto j0_tag, auto j1_tag) {
+      if constexpr (FAST) {
+        load_full(st + kStages3, j0_tag);
+        load_full(st + kStages3, j1_tag);
+      } else if (refill) {
+        load(st + kStages3, j0_tag);
+        load(st + kStages3, j1_tag);
+      }
+    };
     {
       const MfmaSlot m[4] = {slot(0, 0, CUR), slot(0, 1, CUR), slot(0, 0, CUR), slot(0, 0, CUR)};
-      OA::template read2_fused<FA, FB, 2>(OA::sub(nb, kq), ra0, fa[NXT][0], fa[NXT][1], m);
+      OA::template read_at<FA, FB, 2>(pa, d, fa[NXT][0], fa[NXT][1], m);
     }
-    if (refill) {
-      load(st + kStages3, J0{});
-      load(st + kStages3, J1{});
-    }
+    refill2(J0{}, J1{});
     {
       const MfmaSlot m[4] = {slot(1, 0, CUR), slot(1, 1, CUR), slot(1, 0, CUR), slot(1, 0, CUR)};
-      OB::template read2_fused<FA, FB, 2>(OB::sub(nb + OA::kBytes, kq), rb0, fb[NXT][0],
-                                          fb[NXT][1], m);
+      OB::template read_at<FA, FB, 2>(pb, d, fb[NXT][0], fb[NXT][1], m);
     }
-    if (refill) {
-      load(st + kStages3, J2{});
-      load(st + kStages3, J3{});
-    }
+    refill2(J2{}, J3{});
   };
-  for (int st = 0; st < ns; st += 2) {
-    stage_body(st, std::integral_constant<int, 0>{});
-    stage_body(st + 1, std::integral_constant<int, 1>{});
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using Fast = std::true_type;
+  using Slow = std::false_type;
+  // stages whose refill ends at or before K (stage = 128 bytes of K)
+  const int nfull = (int)(g.Kc / (2 * kBK3));
+  const int sfast = max(0, min(ns, nfull - kStages3)) & ~1;
+  int st = 0;
+  for (; st < sfast; st += 2) {
+    stage_body(st, C0{}, Fast{});
+    stage_body(st + 1, C1{}, Fast{});
+  }
+  for (; st < ns; st += 2) {
+    stage_body(st, C0{}, Slow{});
+    stage_body(st + 1, C1{}, Slow{});
   }
 
   // The two K halves of a quadrant meet in LDS: wave kq keeps fragment row
