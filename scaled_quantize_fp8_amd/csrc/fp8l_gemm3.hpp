@@ -446,6 +446,115 @@ struct Op3 {
   }
 };
 
+// Fragment reads addressed with the instruction's immediate offset, so a
+// step needs one or two address registers per operand.  A k-contiguous
+// fragment 32 rows further lies exactly 2048 bytes further (the chunk
+// swizzle repeats every 4 rows); the four 8-row reads of a crosswise
+// fragment lie 8 R bytes apart (the swizzle repeats every 8 k rows).
+#define FP8L_RKC(r, a, o) "ds_read_b128 %[" #r "], %[" #a "] offset:%[" #o "]\n\t"
+#define FP8L_RX(r, a, o) "ds_read_b64_tr_b8 %[" #r "], %[" #a "] offset:%[" #o "]\n\t"
+
+// k-contiguous fragment at offset OFF from the lane addresses a0, a1
+template <int FA, int FB, int NM, int OFF>
+FP8L_DEV void kc1o(uint32_t a0, uint32_t a1, v8i& n0, const MfmaSlot (&m)[4]) {
+  v4i r0, r1;
+#define FP8L_KC1O(n)                                                                      \
+  asm volatile(FP8L_RKC(r0, a0, o0) FP8L_RKC(r1, a1, o0) FP8L_MF##n "s_waitcnt lgkmcnt(0)" \
+               : [r0] "=&v"(r0), [r1] "=&v"(r1), FP8L_CO##n                                \
+               : [a0] "v"(a0), [a1] "v"(a1), [o0] "n"(OFF), FP8L_CI##n, FP8L_FMT           \
+               : "memory")
+  if constexpr (NM == 1) FP8L_KC1O(1);
+  else if constexpr (NM == 2) FP8L_KC1O(2);
+  else if constexpr (NM == 3) FP8L_KC1O(3);
+  else FP8L_KC1O(4);
+#undef FP8L_KC1O
+  n0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+}
+
+// k-contiguous fragment pair at offsets O0 and O0 + D1
+template <int FA, int FB, int NM, int D1 = 2048, int O0 = 0>
+FP8L_DEV void kc2o(uint32_t a0, uint32_t a1, v8i& n0, v8i& n1, const MfmaSlot (&m)[4]) {
+  v4i r0, r1, r2, r3;
+#define FP8L_KC2O(n)                                                                           \
+  asm volatile(FP8L_RKC(r0, a0, o0) FP8L_RKC(r1, a1, o0) FP8L_RKC(r2, a0, o1)                  \
+                   FP8L_RKC(r3, a1, o1) FP8L_MF##n "s_waitcnt lgkmcnt(0)"                      \
+               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3), FP8L_CO##n     \
+               : [a0] "v"(a0), [a1] "v"(a1), [o0] "n"(O0), [o1] "n"(O0 + D1), FP8L_CI##n,    \
+                 FP8L_FMT                                                                      \
+               : "memory")
+  if constexpr (NM == 1) FP8L_KC2O(1);
+  else if constexpr (NM == 2) FP8L_KC2O(2);
+  else if constexpr (NM == 3) FP8L_KC2O(3);
+  else FP8L_KC2O(4);
+#undef FP8L_KC2O
+  n0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  n1 = v8i{r2.x, r2.y, r2.z, r2.w, r3.x, r3.y, r3.z, r3.w};
+}
+
+// crosswise fragment from base b: reads at b + t * DT, t = 0..3
+template <int FA, int FB, int NM, int DT>
+FP8L_DEV void x1o(uint32_t b, v8i& n0, const MfmaSlot (&m)[4]) {
+  v2i r0, r1, r2, r3;
+#define FP8L_X1O(n)                                                                            \
+  asm volatile(FP8L_RX(r0, p0, o0) FP8L_RX(r1, p0, o1) FP8L_RX(r2, p0, o2) FP8L_RX(r3, p0, o3) \
+                   FP8L_MF##n "s_waitcnt lgkmcnt(0)"                                           \
+               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3), FP8L_CO##n     \
+               : [p0] "v"(b), [o0] "n"(0), [o1] "n"(DT), [o2] "n"(2 * DT), [o3] "n"(3 * DT),     \
+                 FP8L_CI##n, FP8L_FMT                                                          \
+               : "memory")
+  if constexpr (NM == 1) FP8L_X1O(1);
+  else if constexpr (NM == 2) FP8L_X1O(2);
+  else if constexpr (NM == 3) FP8L_X1O(3);
+  else FP8L_X1O(4);
+#undef FP8L_X1O
+  n0 = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+}
+
+// crosswise fragment pair from bases b0, b1
+template <int FA, int FB, int NM, int DT>
+FP8L_DEV void x2o(uint32_t b0, uint32_t b1, v8i& n0, v8i& n1, const MfmaSlot (&m)[4]) {
+  v2i r0, r1, r2, r3, r4, r5, r6, r7;
+#define FP8L_X2O(n)                                                                             \
+  asm volatile(FP8L_RX(r0, p0, o0) FP8L_RX(r1, p0, o1) FP8L_RX(r2, p0, o2) FP8L_RX(r3, p0, o3)  \
+                   FP8L_RX(r4, p1, o0) FP8L_RX(r5, p1, o1) FP8L_RX(r6, p1, o2)                  \
+                       FP8L_RX(r7, p1, o3) FP8L_MF##n "s_waitcnt lgkmcnt(0)"                    \
+               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3), [r4] "=&v"(r4), \
+                 [r5] "=&v"(r5), [r6] "=&v"(r6), [r7] "=&v"(r7), FP8L_CO##n                     \
+               : [p0] "v"(b0), [p1] "v"(b1), [o0] "n"(0), [o1] "n"(DT), [o2] "n"(2 * DT),        \
+                 [o3] "n"(3 * DT), FP8L_CI##n, FP8L_FMT                                         \
+               : "memory")
+  if constexpr (NM == 1) FP8L_X2O(1);
+  else if constexpr (NM == 2) FP8L_X2O(2);
+  else if constexpr (NM == 3) FP8L_X2O(3);
+  else FP8L_X2O(4);
+#undef FP8L_X2O
+  n0 = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+  n1 = v8i{r4.x, r4.y, r5.x, r5.y, r6.x, r6.y, r7.x, r7.y};
+}
+
+// Lane address registers of one operand's fragments in the stage-0 buffer
+// (add a stage's byte offset to use them for that stage).  k-contiguous:
+// the two chunk addresses of fragment f0 (fragment f0 + 32 i is at offset
+// 2048 i).  Crosswise: one base per fragment f0 + 32 i, i < NF.
+template <typename Op, int NF>
+struct FragBase {
+  uint32_t a[(Op::kLayout == kKContig) ? 2 : NF];
+  FP8L_DEV void init(const uint8_t* s0, int f0) {
+    uint32_t t[8];
+    if constexpr (Op::kLayout == kKContig) {
+      Op::frag_addrs(s0, f0, t);
+      a[0] = t[0];
+      a[1] = t[1];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NF; ++i) {
+        Op::frag_addrs(s0, f0 + 32 * i, t);
+        a[i] = t[0];
+      }
+    }
+  }
+};
+
 template <int BM, int BN, int WGM, int WGN>
 constexpr int gemm3_lds_bytes() {
   // operand ring, or the staged output tile if that is larger
@@ -481,6 +590,7 @@ void gemm3_kernel(GemmArgs g) {
   OB ob;
   oa.init(g.lda, i0, g.Mc, g.Kc);
   ob.init(g.ldb, j0, g.Nc, g.Kc);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // uniform wave index
 
   const int wm = wave / WGN, wn = wave % WGN;
   v16f acc[FM][FN];
@@ -527,14 +637,27 @@ void gemm3_kernel(GemmArgs g) {
     const int a = e / FN, b = e % FN;
     return MfmaSlot{&acc[a][b], &fb[CUR][b], &fa[CUR][a]};
   };
-  auto kstep_body = [&](int kt, auto cur_tag) {
+  // fragment address registers in the step-0 buffer (a step adds its
+  // buffer's byte offset)
+  FragBase<OA, FM> fra;
+  FragBase<OB, FN> frb;
+  fra.init(smem3, wm * WTM);
+  frb.init(smem3 + OA::kBytes, wn * WTN);
+  // FAST: the refill of this step (step kt+4) lies wholly inside K, so it
+  // is unconditional, goes through the whole-operand resources with the
+  // advance as scalar offset (Op3::issue_full) and the wait count is fixed;
+  // the last steps take the general form.
+  auto kstep_body = [&](int kt, auto cur_tag, auto fast_tag) {
     constexpr int CUR = decltype(cur_tag)::value;
     constexpr int NXT = CUR ^ 1;
+    constexpr bool FAST = decltype(fast_tag)::value;
     {
       const MfmaSlot m[4] = {slot(CUR, 0), slot(CUR, 1), slot(CUR, 0), slot(CUR, 0)};
       mfma_only<FA, FB, 2>(m);
     }
-    {
+    if constexpr (FAST) {
+      wait_vm<2 * kDma>();
+    } else {
       // step kt+1 landed: at most min(2, nk-2-kt) later steps in flight
       const int later = min(2, nk - 2 - kt);
       if (later >= 2) wait_vm<2 * kDma>();
@@ -546,8 +669,10 @@ void gemm3_kernel(GemmArgs g) {
     // groups: each load instruction occupies the wave until the load path
     // accepts it, and issued between groups it overlaps the MFMAs already
     // in flight instead of stalling them all at once.
-    const bool refill = kt + kStages3 < nk;
-    uint8_t* const sf = step_buf(kt + kStages3);
+    const bool refill = FAST || kt + kStages3 < nk;
+    const int kf = kt + kStages3;
+    uint8_t* const sf = step_buf(kf);
+    const uint32_t d = (uint32_t)(((kt + 1) % kStages3) * kStep);
     static_for<kGroups>([&](auto gi_tag) {
       constexpr int gi = decltype(gi_tag)::value;
       // group gi issues entries [e0, e0 + n) of the MFMA list and the DMA
@@ -560,11 +685,16 @@ void gemm3_kernel(GemmArgs g) {
       constexpr int nt = nl < n - 1 ? nl : n - 1;  // loads placed between MFMAs
       auto load = [&](auto j_tag) {
         constexpr int j = decltype(j_tag)::value;
-        if (refill) {
+        if constexpr (FAST) {
           if constexpr (j < OA::kPerWave)
-            oa.template issue_one<j>(ra, sf, kt + kStages3);
+            oa.template issue_full<j>(ra, sf, (uint32_t)kf * oa.kstep, wv);
           else
-            ob.template issue_one<j - OA::kPerWave>(rb, sf + OA::kBytes, kt + kStages3);
+            ob.template issue_full<j - OA::kPerWave>(rb, sf + OA::kBytes, (uint32_t)kf * ob.kstep, wv);
+        } else if (refill) {
+          if constexpr (j < OA::kPerWave)
+            oa.template issue_one<j>(ra, sf, kf);
+          else
+            ob.template issue_one<j - OA::kPerWave>(rb, sf + OA::kBytes, kf);
         }
       };
       // loads that find no MFMA to follow go first
@@ -573,14 +703,23 @@ void gemm3_kernel(GemmArgs g) {
         constexpr int nf = n - nt;  // MFMAs inside the read block
         const MfmaSlot m[4] = {slot(CUR, e0), slot(CUR, nf > 1 ? e0 + 1 : e0),
                                slot(CUR, nf > 2 ? e0 + 2 : e0), slot(CUR, nf > 3 ? e0 + 3 : e0)};
-        const uint8_t* sn = step_buf(kt + 1);
+        // fragments 2h, 2h+1 of the operand (64 h rows/columns further)
+        auto read_pair = [&](const auto& fr, auto lay_tag, auto rows_tag, v8i& n0, v8i& n1,
+                             auto h_tag) {
+          constexpr int lay = decltype(lay_tag)::value, R = decltype(rows_tag)::value;
+          constexpr int h = decltype(h_tag)::value;
+          if constexpr (lay == kKContig)
+            kc2o<FA, FB, nf, 2048, 4096 * h>(fr.a[0] + d, fr.a[1] + d, n0, n1, m);
+          else
+            x2o<FA, FB, nf, 8 * R>(fr.a[2 * h] + d, fr.a[2 * h + 1] + d, n0, n1, m);
+        };
         if constexpr (gi < FM / 2)
-          OA::template read2_fused<FA, FB, nf>(sn, wm * WTM + 64 * gi, fa[NXT][2 * gi],
-                                               fa[NXT][2 * gi + 1], m);
+          read_pair(fra, std::integral_constant<int, LA>{}, std::integral_constant<int, BM>{},
+                    fa[NXT][2 * gi], fa[NXT][2 * gi + 1], std::integral_constant<int, gi>{});
         else
-          OB::template read2_fused<FA, FB, nf>(sn + OA::kBytes, wn * WTN + 64 * (gi - FM / 2),
-                                               fb[NXT][2 * (gi - FM / 2)],
-                                               fb[NXT][2 * (gi - FM / 2) + 1], m);
+          read_pair(frb, std::integral_constant<int, LB>{}, std::integral_constant<int, BN>{},
+                    fb[NXT][2 * (gi - FM / 2)], fb[NXT][2 * (gi - FM / 2) + 1],
+                    std::integral_constant<int, gi - FM / 2>{});
       }
       // then each remaining load right after an MFMA issue, in its shadow
       static_for<nt>([&](auto t) {
@@ -597,9 +736,16 @@ void gemm3_kernel(GemmArgs g) {
   // with a single register assignment: the padded step's DMA lies past K and
   // lands as exact zeros (+0 products leave every sum unchanged), and the
   // last step's reads of a successor fetch a stale buffer that is never used.
-  for (int kt = 0; kt < nk; kt += 2) {
-    kstep_body(kt, std::integral_constant<int, 0>{});
-    kstep_body(kt + 1, std::integral_constant<int, 1>{});
+  const int nfull = (int)(g.Kc / kBK3);  // K steps that end at or before K
+  const int kfast = max(0, min(nk, nfull - kStages3)) & ~1;
+  int kt = 0;
+  for (; kt < kfast; kt += 2) {
+    kstep_body(kt, std::integral_constant<int, 0>{}, std::true_type{});
+    kstep_body(kt + 1, std::integral_constant<int, 1>{}, std::true_type{});
+  }
+  for (; kt < nk; kt += 2) {
+    kstep_body(kt, std::integral_constant<int, 0>{}, std::false_type{});
+    kstep_body(kt + 1, std::integral_constant<int, 1>{}, std::false_type{});
   }
 
   // Epilogue.  Each lane's accumulators hold 4 consecutive columns per

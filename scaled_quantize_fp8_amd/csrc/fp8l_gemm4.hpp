@@ -74,114 +74,6 @@ FP8L_DEV void read1_fused(const uint8_t* s, int f, v8i& n0, const MfmaSlot (&m)[
     fused_x1<FA, FB, NM>(a, n0, m);
 }
 
-// Fragment reads addressed with the instruction's immediate offset, so a
-// step needs one or two address registers per operand.  A k-contiguous
-// fragment 32 rows further lies exactly 2048 bytes further (the chunk
-// swizzle repeats every 4 rows); the four 8-row reads of a crosswise
-// fragment lie 8 R bytes apart (the swizzle repeats every 8 k rows).
-#define FP8L_RKC(r, a, o) "ds_read_b128 %[" #r "], %[" #a "] offset:%[" #o "]\n\t"
-#define FP8L_RX(r, a, o) "ds_read_b64_tr_b8 %[" #r "], %[" #a "] offset:%[" #o "]\n\t"
-
-// k-contiguous fragment at offset OFF from the lane addresses a0, a1
-template <int FA, int FB, int NM, int OFF>
-FP8L_DEV void kc1o(uint32_t a0, uint32_t a1, v8i& n0, const MfmaSlot (&m)[4]) {
-  v4i r0, r1;
-#define FP8L_KC1O(n)                                                                      \
-  asm volatile(FP8L_RKC(r0, a0, o0) FP8L_RKC(r1, a1, o0) FP8L_MF##n "s_waitcnt lgkmcnt(0)" \
-               : [r0] "=&v"(r0), [r1] "=&v"(r1), FP8L_CO##n                                \
-               : [a0] "v"(a0), [a1] "v"(a1), [o0] "n"(OFF), FP8L_CI##n, FP8L_FMT           \
-               : "memory")
-  if constexpr (NM == 1) FP8L_KC1O(1);
-  else if constexpr (NM == 2) FP8L_KC1O(2);
-  else if constexpr (NM == 3) FP8L_KC1O(3);
-  else FP8L_KC1O(4);
-#undef FP8L_KC1O
-  n0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-}
-
-// k-contiguous fragment pair at offsets 0 and D1
-template <int FA, int FB, int NM, int D1 = 2048>
-FP8L_DEV void kc2o(uint32_t a0, uint32_t a1, v8i& n0, v8i& n1, const MfmaSlot (&m)[4]) {
-  v4i r0, r1, r2, r3;
-#define FP8L_KC2O(n)                                                                           \
-  asm volatile(FP8L_RKC(r0, a0, o0) FP8L_RKC(r1, a1, o0) FP8L_RKC(r2, a0, o1)                  \
-                   FP8L_RKC(r3, a1, o1) FP8L_MF##n "s_waitcnt lgkmcnt(0)"                      \
-               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3), FP8L_CO##n     \
-               : [a0] "v"(a0), [a1] "v"(a1), [o0] "n"(0), [o1] "n"(D1), FP8L_CI##n, FP8L_FMT   \
-               : "memory")
-  if constexpr (NM == 1) FP8L_KC2O(1);
-  else if constexpr (NM == 2) FP8L_KC2O(2);
-  else if constexpr (NM == 3) FP8L_KC2O(3);
-  else FP8L_KC2O(4);
-#undef FP8L_KC2O
-  n0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-  n1 = v8i{r2.x, r2.y, r2.z, r2.w, r3.x, r3.y, r3.z, r3.w};
-}
-
-// crosswise fragment from base b: reads at b + t * DT, t = 0..3
-template <int FA, int FB, int NM, int DT>
-FP8L_DEV void x1o(uint32_t b, v8i& n0, const MfmaSlot (&m)[4]) {
-  v2i r0, r1, r2, r3;
-#define FP8L_X1O(n)                                                                            \
-  asm volatile(FP8L_RX(r0, p0, o0) FP8L_RX(r1, p0, o1) FP8L_RX(r2, p0, o2) FP8L_RX(r3, p0, o3) \
-                   FP8L_MF##n "s_waitcnt lgkmcnt(0)"                                           \
-               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3), FP8L_CO##n     \
-               : [p0] "v"(b), [o0] "n"(0), [o1] "n"(DT), [o2] "n"(2 * DT), [o3] "n"(3 * DT),     \
-                 FP8L_CI##n, FP8L_FMT                                                          \
-               : "memory")
-  if constexpr (NM == 1) FP8L_X1O(1);
-  else if constexpr (NM == 2) FP8L_X1O(2);
-  else if constexpr (NM == 3) FP8L_X1O(3);
-  else FP8L_X1O(4);
-#undef FP8L_X1O
-  n0 = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
-}
-
-// crosswise fragment pair from bases b0, b1
-template <int FA, int FB, int NM, int DT>
-FP8L_DEV void x2o(uint32_t b0, uint32_t b1, v8i& n0, v8i& n1, const MfmaSlot (&m)[4]) {
-  v2i r0, r1, r2, r3, r4, r5, r6, r7;
-#define FP8L_X2O(n)                                                                             \
-  asm volatile(FP8L_RX(r0, p0, o0) FP8L_RX(r1, p0, o1) FP8L_RX(r2, p0, o2) FP8L_RX(r3, p0, o3)  \
-                   FP8L_RX(r4, p1, o0) FP8L_RX(r5, p1, o1) FP8L_RX(r6, p1, o2)                  \
-                       FP8L_RX(r7, p1, o3) FP8L_MF##n "s_waitcnt lgkmcnt(0)"                    \
-               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3), [r4] "=&v"(r4), \
-                 [r5] "=&v"(r5), [r6] "=&v"(r6), [r7] "=&v"(r7), FP8L_CO##n                     \
-               : [p0] "v"(b0), [p1] "v"(b1), [o0] "n"(0), [o1] "n"(DT), [o2] "n"(2 * DT),        \
-                 [o3] "n"(3 * DT), FP8L_CI##n, FP8L_FMT                                         \
-               : "memory")
-  if constexpr (NM == 1) FP8L_X2O(1);
-  else if constexpr (NM == 2) FP8L_X2O(2);
-  else if constexpr (NM == 3) FP8L_X2O(3);
-  else FP8L_X2O(4);
-#undef FP8L_X2O
-  n0 = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
-  n1 = v8i{r4.x, r4.y, r5.x, r5.y, r6.x, r6.y, r7.x, r7.y};
-}
-
-// Lane address registers of one operand's fragments in the stage-0 buffer
-// (add a stage's byte offset to use them for that stage).  k-contiguous:
-// the two chunk addresses of fragment f0 (fragment f0 + 32 i is at offset
-// 2048 i).  Crosswise: one base per fragment f0 + 32 i, i < NF.
-template <typename Op, int NF>
-struct FragBase {
-  uint32_t a[(Op::kLayout == kKContig) ? 2 : NF];
-  FP8L_DEV void init(const uint8_t* s0, int f0) {
-    uint32_t t[8];
-    if constexpr (Op::kLayout == kKContig) {
-      Op::frag_addrs(s0, f0, t);
-      a[0] = t[0];
-      a[1] = t[1];
-    } else {
-#pragma unroll
-      for (int i = 0; i < NF; ++i) {
-        Op::frag_addrs(s0, f0 + 32 * i, t);
-        a[i] = t[0];
-      }
-    }
-  }
-};
-
 template <int LA, int LB, int FA, int FB>
 __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   batch_slice(g);
