@@ -16,6 +16,13 @@ fp8_linear_fwd(X, W) launches, with each GEMM a call of its own so that a
 forward or dX GEMM launch can be bracketed with events in the timed region
 for the roofline entry (one launch per step, rotating over the linears).
 
+Beside the headline (warm: the same buffers every step) the line carries a
+cold-cache step (the same step with its inputs rotated over enough copies of
+the layer, >= 1 GiB of bf16 inputs, that none is found in L2 or the MALL) and
+the step of every other full-size workload: the dim1024 layer at M = 2048,
+the dim1536 layer at M = 512, the generic 4096 <-> 11008 pair at M = 4096
+with dynamic scaling, and the dim1536 layer with W and bias pre-quantized.
+
 Prints one JSON line (see the fields below).  --gpus N > 1 is refused: this
 benchmark measures one GPU.
 """
@@ -45,6 +52,8 @@ def parse():
     p.add_argument("--workload", default="dim1536_m2048")
     p.add_argument("--kernel-reps", type=int, default=20, help="repeats of each isolated kernel timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-other-configs", action="store_true",
+                   help="skip the cold-cache step and the other workloads' steps")
     p.add_argument("--no-widened", action="store_true",
                    help="skip the isolated timings of the entry points beyond the layer step "
                         "(for a profile of the step alone)")
@@ -64,12 +73,18 @@ def parse():
 
 
 class Layer:
-    """Device buffers, rings and bound C calls of one linear."""
+    """Device buffers, rings and bound C calls of one linear.  Delayed
+    workloads get a ring per quantized tensor, dynamic ones none; the
+    pre-quantized workload takes W and the bias as e4m3 codes with their
+    scales (made once here) and quantizes only X in the forward.  inputs:
+    CPU tensors (X, W, b, G) to copy instead of generating them."""
 
-    def __init__(self, F, WL, wl, li, dev, stream):
+    def __init__(self, F, WL, wl, li, dev, stream, inputs=None):
         import torch
 
-        X, W, b, G = WL.layer_inputs(wl, li)
+        X, W, b, G = WL.layer_inputs(wl, li) if inputs is None else inputs
+        self.delayed = wl.delayed
+        self.prequant = wl.name.startswith("prequant")
         self.name = wl.linears[li].name
         self.M, self.K = X.shape
         self.N = W.shape[0]
@@ -84,21 +99,34 @@ class Layer:
         self.db = e(N, dt=torch.bfloat16)
         self.ws = e(max(1, F.fp8_db_workspace_bytes(M, N) // 4), dt=torch.float32)
         self.sx, self.sw, self.sg, self.ax, self.aw, self.ag = (f() for _ in range(6))
-        self.rx, self.rw, self.rg = (F.ScaleRing(wl.hist_len, stream=stream) for _ in range(3))
+        ring = (lambda: F.ScaleRing(wl.hist_len, stream=stream)) if wl.delayed else (lambda: None)
+        self.rx, self.rw, self.rg = ring(), ring(), ring()
         self.flops = 2.0 * M * N * K  # per GEMM
         x8q = F.Quantized(self.x8, F.FP8_E4M3, self.sx)
         w8q = F.Quantized(self.w8, F.FP8_E4M3, self.sw)
         g8q = F.Quantized(self.g8, F.FP8_E5M2, self.sg)
+        bias = self.b
+        if self.prequant:
+            # W8 and b8 with their dynamic scales, made once (the pre-quantized
+            # operands a caller would hand in)
+            self.b8, self.sb, ab = e(N), f(), f()
+            F.fp8_quantize(self.W, F.FP8_E4M3, self.w8, None, self.sw, self.aw, stream=stream)
+            F.fp8_quantize(self.b, F.FP8_E4M3, self.b8, None, self.sb, ab, stream=stream)
+            bias = F.Quantized(self.b8, F.FP8_E4M3, self.sb)
         # the calls of a training step (the forward as quantize pair + GEMM)
         self.bwd_dw = F.bind_fp8_linear_bwd_dw(self.G, F.FP8_E5M2, x8q, self.dw, self.db, self.ws,
                                                self.rg, self.g8, self.sg, self.ag, stream=stream)
         self.bwd_dx = F.bind_fp8_linear_bwd_dx(g8q, F.FP8_E5M2, w8q, self.dx, stream=stream)
         # single-kernel calls (pre-quantized operands) for isolated timings
-        self.gemm_fwd = F.bind_fp8_linear_fwd(x8q, w8q, self.b, F.FP8_E4M3, self.y, stream=stream)
+        self.gemm_fwd = F.bind_fp8_linear_fwd(x8q, w8q, bias, F.FP8_E4M3, self.y, stream=stream)
         self.gemm_dw = F.bind_fp8_linear_bwd_dw(g8q, F.FP8_E5M2, x8q, self.dw, stream=stream)
-        self.quant_xw = F.bind_fp8_quantize_pair(self.X, self.x8, self.rx, self.sx, self.ax,
-                                                 self.W, self.w8, self.rw, self.sw, self.aw,
-                                                 F.FP8_E4M3, stream=stream)
+        if self.prequant:  # the forward's quantize: X only
+            self.quant_xw = F.bind_fp8_quantize(self.X, F.FP8_E4M3, self.x8, self.rx, self.sx,
+                                                self.ax, stream=stream)
+        else:
+            self.quant_xw = F.bind_fp8_quantize_pair(self.X, self.x8, self.rx, self.sx, self.ax,
+                                                     self.W, self.w8, self.rw, self.sw, self.aw,
+                                                     F.FP8_E4M3, stream=stream)
         self.quant = {
             "X": F.bind_fp8_quantize(self.X, F.FP8_E4M3, self.x8, self.rx, self.sx, self.ax,
                                      stream=stream),
@@ -109,8 +137,15 @@ class Layer:
         }
 
     def quant_bytes(self, which):
+        """Algorithmic bytes of one quantize of X, W or G: bf16 read + fp8
+        write, plus the second read of the dynamic path's amax pass."""
         n = {"X": self.M * self.K, "W": self.N * self.K, "G": self.M * self.N}[which]
-        return 3.0 * n  # bf16 read + fp8 write
+        return (3.0 if self.delayed else 5.0) * n
+
+    def step_quant_bytes(self):
+        """Quantize bytes of one training step of this linear (W is not
+        quantized on the pre-quantized path)."""
+        return sum(self.quant_bytes(w) for w in (("X", "G") if self.prequant else ("X", "W", "G")))
 
 
 def event_time_ms(torch, fn, reps, stream):
@@ -257,6 +292,132 @@ def cpu_baseline(layers_cpu, budget_s, min_s=10.0):
                       f"GEMMs + db, fp64 accumulation; {dt:.1f} s on {os.cpu_count()} host cpus"}
 
 
+def layer_step(layers):
+    """One training step over the linears: the forward's quantize launch and
+    GEMM, the weight gradient (G quantized there, with db), the input
+    gradient from G8."""
+    def step():
+        for L in layers:
+            L.quant_xw()
+            L.gemm_fwd()
+            L.bwd_dw()
+            L.bwd_dx()
+    return step
+
+
+def isolated_timings(torch, layers, reps, stream):
+    """Per-linear isolated kernel times (events behind a GPU sleep); the
+    per-kind GEMM totals of a step; the step's quantize time as it issues
+    it (the forward's quantize launch and the G quantize) and its rate."""
+    per = {}
+    for L in layers:
+        per[L.name] = {
+            "fwd_gemm_us": 1e3 * event_time_ms(torch, L.gemm_fwd, reps, stream),
+            "dx_gemm_us": 1e3 * event_time_ms(torch, L.bwd_dx, reps, stream),
+            "dw_gemm_us": 1e3 * event_time_ms(torch, L.gemm_dw, reps, stream),
+        }
+        for w in ("X", "W", "G"):
+            us = 1e3 * event_time_ms(torch, L.quant[w], reps, stream)
+            per[L.name][f"quant_{w}_us"] = us
+            per[L.name][f"quant_{w}_GBps"] = L.quant_bytes(w) / (us * 1e-6) / 1e9
+        us = 1e3 * event_time_ms(torch, L.quant_xw, reps, stream)
+        fwd_bytes = L.quant_bytes("X") + (0.0 if L.prequant else L.quant_bytes("W"))
+        per[L.name]["quant_fwd_us"] = us
+        per[L.name]["quant_fwd_GBps"] = fwd_bytes / (us * 1e-6) / 1e9
+    for L in layers:
+        p = per[L.name]
+        for g_ in ("fwd", "dx", "dw"):
+            p[f"{g_}_TFLOPs"] = L.flops / (p[f"{g_}_gemm_us"] * 1e-6) / 1e12
+    tot = {g_: sum(per[L.name][f"{g_}_gemm_us"] for L in layers) for g_ in ("fwd", "dx", "dw")}
+    q_us = sum(per[L.name]["quant_fwd_us"] + per[L.name]["quant_G_us"] for L in layers)
+    q_bytes = sum(L.step_quant_bytes() for L in layers)
+    return per, tot, q_us, q_bytes / (q_us * 1e-6) / 1e9
+
+
+def timed_steps_ms(torch, step, steps, stream):
+    """ms per step over `steps` eager steps (GPU events, or the host wall
+    clock if that is longer)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        a.record(stream)
+        for _ in range(steps):
+            step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return max(a.elapsed_time(b), (time.perf_counter() - w0) * 1e3) / steps
+
+
+def workload_label(wl):
+    names = "/".join(L.name for L in wl.linears)
+    dims = ", ".join(f"{L.name} {L.K}->{L.N}" for L in wl.linears)
+    mode = f"delayed scaling H={wl.hist_len}" if wl.delayed else "dynamic scaling"
+    pre = "; W and bias pre-quantized e4m3" if wl.name.startswith("prequant") else ""
+    return f"{wl.name}: {dims}; M={wl.M} tokens; {names} fwd+dW(+db)+dX; {mode}{pre}"
+
+
+def other_configs(torch, F, WL, dev, stream, skip, steps, reps):
+    """The step of every other full-size workload on its own: ms per step,
+    TFLOP/s and % of the FP8 peak over its GEMMs, quantize GB/s as the step
+    issues it, and the isolated GEMM totals per kind."""
+    res = {}
+    for name in ("dim1024_m2048", "dim1536_m512", "generic_m4096", "prequant_dim1536_m2048"):
+        if name == skip:
+            continue
+        wl = WL.WORKLOADS[name]
+        layers = [Layer(F, WL, wl, li, dev, stream) for li in range(len(wl.linears))]
+        step = layer_step(layers)
+        for _ in range(2):  # the first step seeds the rings
+            step()
+        per, tot, q_us, q_gbps = isolated_timings(torch, layers, reps, stream)
+        ms = timed_steps_ms(torch, step, steps, stream)
+        flops = sum(3 * L.flops for L in layers)
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {
+            "workload": workload_label(wl),
+            "gemms_per_step": 3 * len(layers),
+            "ms_per_step": round(ms, 4),
+            "TFLOPs": round(tf, 2),
+            "pct_fp8_peak": round(100 * tf / MI355X_FP8_DENSE_TFLOPS, 2),
+            "quantize_GBps": round(q_gbps, 1),
+            "quantize_pct_hbm": round(100 * q_gbps / MI355X_HBM_GBPS, 2),
+            "quant_us_per_step": round(q_us, 1),
+            "gemm_us_per_step": {k: round(v, 1) for k, v in tot.items()},
+            "gemm_TFLOPs": {k: round(sum(L.flops for L in layers) / (v * 1e-6) / 1e12, 1)
+                            for k, v in tot.items()},
+        }
+        del layers, step
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return res
+
+
+def cold_steps(torch, F, WL, wl, dev, stream, steps, min_bytes=1 << 30):
+    """ms per step with the step's inputs rotated over copies of the layer
+    (at least 1 GiB of bf16 inputs in all, past the 256 MB MALL and the
+    4 MB L2s), so that a step finds none of its inputs or weights in cache."""
+    cpu = [WL.layer_inputs(wl, li) for li in range(len(wl.linears))]
+    per_set = sum(t.numel() * t.element_size() for inp in cpu for t in inp)
+    R = max(2, -(-min_bytes // per_set))
+    sets = [layer_step([Layer(F, WL, wl, li, dev, stream, inputs=cpu[li])
+                        for li in range(len(cpu))]) for _ in range(R)]
+    for st in sets:  # seed every copy's rings
+        st()
+    calls = [0]
+
+    def step():
+        sets[calls[0] % R]()
+        calls[0] += 1
+    ms = timed_steps_ms(torch, step, steps, stream)
+    flops = sum(3 * 2.0 * wl.M * L.N * L.K for L in wl.linears)
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 4), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+            "rotated_copies": R, "rotated_input_MB": round(R * per_set / 1e6, 1)}
+
+
 def widened_rows(torch, F, WL, wl, layers, stream, reps):
     """Isolated timings of the entry points beyond the layer step (not part of
     the step or its value): the transposed and dual quantize, the weight
@@ -358,13 +519,7 @@ def main():
     wl = WL.WORKLOADS[args.workload]
     stream = torch.cuda.Stream()
     layers = [Layer(F, WL, wl, li, dev, stream) for li in range(len(wl.linears))]
-
-    def step():
-        for L in layers:
-            L.quant_xw()
-            L.gemm_fwd()
-            L.bwd_dw()
-            L.bwd_dx()
+    step = layer_step(layers)
 
     if args.sweep_tiles:
         step()  # seed the rings and fill the quantized operands
@@ -418,30 +573,7 @@ def main():
 
     # ---- isolated per-kernel timings (events behind a GPU sleep), before the
     # timed region: they decide which GEMM kind the live events follow
-    reps = args.kernel_reps
-    per = {}
-    for L in layers:
-        per[L.name] = {
-            "fwd_gemm_us": 1e3 * event_time_ms(torch, L.gemm_fwd, reps, stream),
-            "dx_gemm_us": 1e3 * event_time_ms(torch, L.bwd_dx, reps, stream),
-            "dw_gemm_us": 1e3 * event_time_ms(torch, L.gemm_dw, reps, stream),
-        }
-        for w in ("X", "W", "G"):
-            us = 1e3 * event_time_ms(torch, L.quant[w], reps, stream)
-            per[L.name][f"quant_{w}_us"] = us
-            per[L.name][f"quant_{w}_GBps"] = L.quant_bytes(w) / (us * 1e-6) / 1e9
-        us = 1e3 * event_time_ms(torch, L.quant_xw, reps, stream)
-        per[L.name]["quant_XW_pair_us"] = us
-        per[L.name]["quant_XW_pair_GBps"] = (L.quant_bytes("X") + L.quant_bytes("W")) / (us * 1e-6) / 1e9
-    for L in layers:
-        p = per[L.name]
-        for g_ in ("fwd", "dx", "dw"):
-            p[f"{g_}_TFLOPs"] = L.flops / (p[f"{g_}_gemm_us"] * 1e-6) / 1e12
-    tot = {g_: sum(per[L.name][f"{g_}_gemm_us"] for L in layers) for g_ in ("fwd", "dx", "dw")}
-    # quantize as the step issues it: the X/W pair launch and the G quantize
-    q_us = sum(per[L.name]["quant_XW_pair_us"] + per[L.name]["quant_G_us"] for L in layers)
-    q_bytes = sum(L.quant_bytes(w) for L in layers for w in ("X", "W", "G"))
-    quant_gbps = q_bytes / (q_us * 1e-6) / 1e9
+    per, tot, q_us, quant_gbps = isolated_timings(torch, layers, args.kernel_reps, stream)
 
     # ---- timed region: exactly args.steps eager steps.  In step s the launch
     # of the GEMM kind that dominates the isolated timings (forward or dX:
@@ -554,9 +686,8 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: dim1536/ffn6912 layer, M={wl.M} tokens, "
-                               "qkv/out/up/gate/down fwd+dW(+db)+dX, delayed scaling H=16",
-                   "global_batch": wl.M, "gemms_per_step": 15},
+        "config": {"workload": workload_label(wl), "global_batch": wl.M,
+                   "gemms_per_step": 3 * len(layers)},
         "pct_fp8_peak": round(100 * tflops / MI355X_FP8_DENSE_TFLOPS, 2),
         "quantize_GBps": round(quant_gbps, 1),
         "quantize_pct_hbm": round(100 * quant_gbps / MI355X_HBM_GBPS, 2),
@@ -571,6 +702,10 @@ def main():
     }
     if not args.no_widened:
         out["widened"] = widened_rows(torch, F, WL, wl, layers, stream, args.kernel_reps)
+    if not args.no_other_configs:
+        out["cold"] = cold_steps(torch, F, WL, wl, dev, stream, args.steps)
+        out["other_configs"] = other_configs(torch, F, WL, dev, stream, wl.name, args.steps,
+                                             args.kernel_reps)
     if not args.no_cpu_baseline:
         layers_cpu = [WL.layer_inputs(wl, li) for li in range(len(wl.linears))]
         out["cpu_baseline"] = cpu_baseline(layers_cpu, args.cpu_seconds)
