@@ -183,16 +183,31 @@ FP8L_DEV float bias_at(const GemmArgs& g, int64_t j, float inv_bs) {
 // q + 16, ...; the 16 sums meet in a fixed xor tree, so the result does not
 // depend on the launch shape.  Every thread of the block calls it (the
 // shuffles need whole 16-lane groups; the loop's trip count is uniform).
+// NT: threads per block.  A lane loads four of its partial rows at a time
+// and adds them in row order, so the sum is the plain sequential one.
+template <int NT>
 FP8L_DEV void db_finalize(const GemmArgs& g) {
   const int tid = threadIdx.x;
   const int64_t nblk = (int64_t)gridDim.x * gridDim.y;
   const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-  const int per = (int)blockDim.x / 16;  // entries per block and pass
+  constexpr int per = NT / 16;  // entries per block and pass
   const int q = tid & 15;
   for (int64_t i = b * per + tid / 16; i - tid / 16 < g.Mc; i += nblk * per) {
     float s = 0.0f;
-    if (i < g.Mc)
-      for (int r = q; r < g.db_R; r += 16) s += g.db_ws[(int64_t)r * g.Mc + i];
+    if (i < g.Mc) {
+      const float* col = g.db_ws + i;
+      const int64_t st = g.Mc;
+      int r = q;
+      for (; r + 48 < g.db_R; r += 64) {
+        const float v0 = col[(int64_t)r * st], v1 = col[(int64_t)(r + 16) * st];
+        const float v2 = col[(int64_t)(r + 32) * st], v3 = col[(int64_t)(r + 48) * st];
+        s += v0;
+        s += v1;
+        s += v2;
+        s += v3;
+      }
+      for (; r < g.db_R; r += 16) s += col[(int64_t)r * st];
+    }
     s += __shfl_xor(s, 1, 16);
     s += __shfl_xor(s, 2, 16);
     s += __shfl_xor(s, 4, 16);
@@ -234,7 +249,7 @@ __global__ __launch_bounds__(kGThreads, 2) void gemm_kernel(GemmArgs g) {
     if (g.aux_amax_dst1) *g.aux_amax_dst1 = 0.0f;
   }
 
-  if (g.db) db_finalize(g);
+  if (g.db) db_finalize<kGThreads>(g);
 
   const int wm = wave >> 1, wn = wave & 1;
   v4f acc[4][4];

@@ -239,39 +239,84 @@ FP8L_DEV void wait_vm() {
 }
 FP8L_DEV void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
-// Prologue work that does not feed the K loop: block 0's snapshot copies
-// for pre-quantized operands, the bias-gradient finalize (shared by all
-// blocks), and the loads of the epilogue's scales.  Kernels call it
-// after issuing their first DMA stages, so its memory latency overlaps
-// theirs instead of preceding them.  The loop's vmcnt waits stay exact:
-// loads return in issue order, and every load or store made here was issued
-// after the stage loads those waits refer to, so it can only make them
-// stricter.  The scales are only loaded here; the reciprocals are taken in
-// the epilogue (EpiScales::dq/inv_bs), so that no use of them makes the
-// prologue wait for the stage loads issued before them.
+// The epilogue's scales, loaded ahead of the first DMA stages (older than
+// every stage load, they leave the loop's in-order vmcnt waits exact) and
+// first used in the epilogue: the reciprocals are taken there
+// (EpiScales::dq/inv_bs), so no use of them makes the prologue wait.
 struct EpiScales {
   float sa, sb, bs;  // scale_a, scale_b, bias_scale for an FP8 bias (else 1)
   FP8L_DEV float dq() const { return (1.0f / sa) * (1.0f / sb); }
   FP8L_DEV float inv_bs() const { return 1.0f / bs; }
 };
 
-FP8L_DEV EpiScales prologue_side(const GemmArgs& g) {
-  const int tid = threadIdx.x;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
-    if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
-    if (g.aux_amax_dst0) *g.aux_amax_dst0 = 0.0f;
-    if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;
-    if (g.aux_amax_dst1) *g.aux_amax_dst1 = 0.0f;
-  }
-  // (One thread per entry walking all db_R rows, in the first tile column's
-  // blocks only, made those blocks the launch's last by many microseconds.)
-  if (g.db) db_finalize(g);
+FP8L_DEV EpiScales load_scales(const GemmArgs& g) {
   EpiScales e;
   e.sa = *g.scale_a;
   e.sb = *g.scale_b;
   e.bs = (g.bias_kind == kBiasE4M3 || g.bias_kind == kBiasE5M2) ? *g.bias_scale : 1.0f;
   return e;
 }
+
+// Work beside the tile: block 0's snapshot copies for pre-quantized
+// operands and the bias-gradient finalize (shared by all blocks; one
+// thread per entry walking all rows, in the first tile column's blocks
+// only, made those blocks the launch's last by many microseconds).  Kernels
+// call it after the K loop and the MFMA drain, when no operand DMA is in
+// flight: a wait for these loads then waits for nothing else (in the
+// prologue the first such wait held every stage in flight).
+// NT: threads per block.
+template <int NT>
+FP8L_DEV void side_work(const GemmArgs& g) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
+    if (g.aux_amax_dst0) *g.aux_amax_dst0 = 0.0f;
+    if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;
+    if (g.aux_amax_dst1) *g.aux_amax_dst1 = 0.0f;
+  }
+  if (g.db) db_finalize<NT>(g);
+}
+
+// Bias of the block's BN output columns, staged in LDS for the epilogue so
+// that it does not wait a memory latency for them.  Wave 0 fetches the raw
+// codes (bf16 or fp8 bytes) with one DMA load issued before any operand
+// stage: loads complete in issue order, so the prologue's wait for the
+// first stage covers it, and no register holds the codes (a register
+// destination would make the compiler wait for it, and so for every stage
+// in flight, at its first use).  Lane l carries bytes [16 l, 16 l + 16) of
+// the block's columns; lanes past the bias read zeros, so the area is
+// kBytes = 1 KB.  The DMA path needs every 16-byte piece wholly inside or
+// wholly outside the bias (N times the code size a multiple of 16);
+// otherwise, and without bias, the epilogue reads the bias from memory as
+// before (bias_at).  get() decodes as bias_at does, bit for bit.
+template <int BN>
+struct BiasStage {
+  static constexpr int kBytes = 1024;
+  static_assert(2 * BN <= kBytes, "bias codes of the block in one DMA load");
+  FP8L_DEV static int code_bytes(const GemmArgs& g) { return g.bias_kind == kBiasBF16 ? 2 : 1; }
+  FP8L_DEV static bool staged(const GemmArgs& g) {
+    return g.bias_kind != kBiasNone && (g.Nc * code_bytes(g)) % 16 == 0;
+  }
+  // wave: this wave's index (uniform)
+  FP8L_DEV static void load(const GemmArgs& g, int64_t j0, uint8_t* sb, int wave) {
+    if (wave != 0 || !staged(g)) return;
+    const int eb = code_bytes(g);
+    const uint32_t bytes = (uint32_t)(g.Nc * eb);
+    const uint32_t first = (uint32_t)(j0 * eb);
+    const int lane = threadIdx.x & 63;
+    const uint32_t off = first + 16u * lane;
+    const uint32_t voff = (16 * lane < BN * eb && off < bytes) ? off : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(g.bias, bytes),
+                                             (__attribute__((address_space(3))) void*)sb, 16,
+                                             voff, 0, 0, 0);
+  }
+  // bias of block column jl (the value bias_at gives for column j0 + jl)
+  FP8L_DEV static float get(const GemmArgs& g, const uint8_t* sb, int64_t j0, int jl,
+                            float inv_bs) {
+    if (!staged(g)) return j0 + jl < g.Nc ? bias_at(g, j0 + jl, inv_bs) : 0.0f;
+    if (g.bias_kind == kBiasBF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(sb)[jl]);
+    return fp8_to_f32_rt(sb[jl], g.bias_kind == kBiasE4M3 ? kE4M3 : kE5M2) * inv_bs;
+  }
+};
 
 // One operand of the pipelined kernel.  R: tile extent along C; NW: waves.
 template <int L, int R, int NW>
@@ -555,11 +600,17 @@ struct FragBase {
   }
 };
 
-template <int BM, int BN, int WGM, int WGN>
-constexpr int gemm3_lds_bytes() {
-  // operand ring, or the staged output tile if that is larger
+// LDS: the operand ring, or the staged output tile if that is larger, then
+// the bias of the block's BN columns (BiasStage).
+template <int BM, int BN>
+constexpr int gemm3_bias_off() {
   return kStages3 * (BM + BN) * kBK3 > BM * (BN * 2 + 16) ? kStages3 * (BM + BN) * kBK3
                                                          : BM * (BN * 2 + 16);
+}
+
+template <int BM, int BN, int WGM, int WGN>
+constexpr int gemm3_lds_bytes() {
+  return gemm3_bias_off<BM, BN>() + BiasStage<BN>::kBytes;
 }
 
 template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB>
@@ -580,6 +631,7 @@ void gemm3_kernel(GemmArgs g) {
   int tm, tn;
   tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
+  uint8_t* const sbias = smem3 + gemm3_bias_off<BM, BN>();  // BiasStage area
 
 
   const int64_t a_rows = (LA == kKContig) ? g.Mc : g.Kc;
@@ -605,11 +657,12 @@ void gemm3_kernel(GemmArgs g) {
   auto step_buf = [&](int kt) { return smem3 + (kt % kStages3) * kStep; };
 
   // prologue: DMA steps 0..3, then step 0's fragments
+  BiasStage<BN>::load(g, j0, sbias, wv);  // ahead of the stages (see BiasStage)
+  const EpiScales es = load_scales(g);
   for (int s = 0; s < kStages3 && s < nk; ++s) {
     oa.issue(ra, step_buf(s), s);
     ob.issue(rb, step_buf(s) + OA::kBytes, s);
   }
-  const EpiScales es = prologue_side(g);
   v8i fa[2][FM], fb[2][FN];
   if (nk > 0) {
     // step 0 landed: at most min(3, nk - 1) later steps still in flight
@@ -758,6 +811,7 @@ void gemm3_kernel(GemmArgs g) {
   //   column wn*WTN + 32b + 8(e>>2) + 4(lane>>5) + (e&3) of the block tile
   constexpr int RS = BN * 2 + 16;  // LDS bytes per staged row
   mfma_drain();                    // accumulators are read by VALU below
+  side_work<64 * WGM * WGN>(g);    // after the drain: it may reuse fragment registers
   barrier_only();                  // every wave is done reading operand tiles
   const float dq = es.dq(), inv_bs = es.inv_bs();
 #pragma unroll
@@ -765,12 +819,11 @@ void gemm3_kernel(GemmArgs g) {
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       const int jl = wn * WTN + 32 * b + 8 * grp + 4 * (lane >> 5);
-      const int64_t j = j0 + jl;
       float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (g.bias_kind != kBiasNone) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          if (j + t < g.Nc) bias[t] = bias_at(g, j + t, inv_bs);
+          bias[t] = BiasStage<BN>::get(g, sbias, j0, jl + t, inv_bs);
       }
 #pragma unroll
       for (int a = 0; a < FM; ++a) {

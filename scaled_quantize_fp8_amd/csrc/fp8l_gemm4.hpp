@@ -74,6 +74,11 @@ FP8L_DEV void read1_fused(const uint8_t* s, int f, v8i& n0, const MfmaSlot (&m)[
     fused_x1<FA, FB, NM>(a, n0, m);
 }
 
+// LDS: the operand ring or the staged output tile, then the bias of the
+// block's 256 columns (BiasStage).
+constexpr int kGemm4BiasOff =
+    kStages3 * 512 * kBK3 > 256 * (256 * 2 + 16) ? kStages3 * 512 * kBK3 : 256 * (256 * 2 + 16);
+
 template <int LA, int LB, int FA, int FB>
 __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   batch_slice(g);
@@ -92,6 +97,7 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   int tm, tn;
   tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
+  uint8_t* const sbias = smem4 + kGemm4BiasOff;  // BiasStage area
 
 
   const int64_t a_rows = (LA == kKContig) ? g.Mc : g.Kc;
@@ -136,8 +142,9 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   auto slot = [&](int a, int b, int buf) { return MfmaSlot{&acc[a][b], &fb[buf][b], &fa[a]}; };
 
   // prologue: DMA steps 0..3, read step 0, issue its first two MFMAs
+  BiasStage<BN>::load(g, j0, sbias, wv);  // ahead of the stages (see BiasStage)
+  const EpiScales es = load_scales(g);
   for (int s = 0; s < kStages3 && s <= nk; ++s) issue_step(s);
-  const EpiScales es = prologue_side(g);
   if (nk > 0) {
     const int later = min(3, nk);  // steps 1..min(3, nk) may still be in flight
     if (later >= 3) wait_vm<3 * kDma>();
@@ -255,6 +262,7 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   // through LDS (rows padded by 16 bytes) and stored as whole rows.
   constexpr int RS = BN * 2 + 16;
   mfma_drain();
+  side_work<64 * NW>(g);  // after the drain: its VALU work may reuse fragment registers
   const float dq = es.dq(), inv_bs = es.inv_bs();
   barrier_only();
 #pragma unroll
@@ -262,12 +270,11 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       const int jl = rb0 + 32 * b + 8 * grp + 4 * (lane >> 5);
-      const int64_t j = j0 + jl;
       float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (g.bias_kind != kBiasNone) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          if (j + t < g.Nc) bias[t] = bias_at(g, j + t, inv_bs);
+          bias[t] = BiasStage<BN>::get(g, sbias, j0, jl + t, inv_bs);
       }
 #pragma unroll
       for (int a = 0; a < FM; ++a) {
@@ -292,8 +299,6 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   }
 }
 
-constexpr int gemm4_lds_bytes() {
-  return kStages3 * 512 * kBK3 > 256 * (256 * 2 + 16) ? kStages3 * 512 * kBK3 : 256 * (256 * 2 + 16);
-}
+constexpr int gemm4_lds_bytes() { return kGemm4BiasOff + BiasStage<256>::kBytes; }
 
 }  // namespace fp8l

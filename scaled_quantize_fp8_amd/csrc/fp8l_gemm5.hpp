@@ -202,6 +202,12 @@ struct Stage128<kCross, R, NW> : Op3<kCross, R, NW> {
   }
 };
 
+// LDS: the operand ring (the output staging and the K-half exchange reuse
+// it), then the bias of the block's 128 columns (BiasStage).
+constexpr int kGemm5BiasOff = kStages3 * 2 * 256 * kBK3 > 128 * (128 * 2 + 16)
+                                  ? kStages3 * 2 * 256 * kBK3
+                                  : 128 * (128 * 2 + 16);
+
 template <int LA, int LB, int FA, int FB>
 __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
   batch_slice(g);
@@ -217,6 +223,7 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
   int tm, tn;
   tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
+  uint8_t* const sbias = smem5 + kGemm5BiasOff;  // BiasStage area
 
 
   const int64_t a_rows = (LA == kKContig) ? g.Mc : g.Kc;
@@ -271,13 +278,14 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
   v8i fa[2][2], fb[2][2];
   auto slot = [&](int a, int b, int par) { return MfmaSlot{&acc[a][b], &fb[par][b], &fa[par][a]}; };
 
+  BiasStage<BN>::load(g, j0, sbias, wv);  // ahead of the stages (see BiasStage)
+  const EpiScales es = load_scales(g);
   for (int s = 0; s < kStages3 && s < ns; ++s) {
     load(s, J0{});
     load(s, J1{});
     load(s, J2{});
     load(s, J3{});
   }
-  const EpiScales es = prologue_side(g);
   if (ns > 0) {
     const int later = min(3, ns - 1);
     if (later >= 3) wait_vm<3 * kDma>();
@@ -361,6 +369,7 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
   constexpr int kXchg = 36864;  // >= BM * RS, 1 KB aligned
   static_assert(kXchg >= BM * RS && kXchg + 16 * 4096 <= 4 * 32768, "LDS split");
   mfma_drain();
+  side_work<64 * NW>(g);  // after the drain: its VALU work may reuse fragment registers
   const float dq = es.dq(), inv_bs = es.inv_bs();
   barrier_only();  // every wave's last stage reads are done
   auto xslot = [&](int a, int b, int g4) {
@@ -395,12 +404,11 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       const int jl = rb0 + 32 * b + 8 * grp + 4 * (lane >> 5);
-      const int64_t j = j0 + jl;
       float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (g.bias_kind != kBiasNone) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          if (j + t < g.Nc) bias[t] = bias_at(g, j + t, inv_bs);
+          bias[t] = BiasStage<BN>::get(g, sbias, j0, jl + t, inv_bs);
       }
       float v[4];
 #pragma unroll
@@ -421,9 +429,6 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
   }
 }
 
-constexpr int gemm5_lds_bytes() {
-  return kStages3 * 2 * 256 * kBK3 > 128 * (128 * 2 + 16) ? kStages3 * 2 * 256 * kBK3
-                                                          : 128 * (128 * 2 + 16);
-}
+constexpr int gemm5_lds_bytes() { return kGemm5BiasOff + BiasStage<128>::kBytes; }
 
 }  // namespace fp8l

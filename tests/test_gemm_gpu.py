@@ -124,7 +124,9 @@ def test_random_codes_tolerance(M, N, K, fa, fb, tile):
 
 
 @pytest.mark.parametrize("bias_kind", ["bf16", "e4m3", "e5m2"])
-@pytest.mark.parametrize("N", [256, 77])
+# 256 and 264: codes staged in LDS by the kernels (N times the code size a
+# multiple of 16; 264 ends in a partial tile), 77: read from memory
+@pytest.mark.parametrize("N", [256, 264, 77])
 def test_fused_bias(bias_kind, N, tile):
     rng = np.random.default_rng(N)
     M, K = 160, 384
