@@ -1,0 +1,104 @@
+"""A training step of one FP8 linear captured as a HIP graph and replayed.
+
+The step is the benchmark's: the paired X/W quantize, the forward GEMM with
+a bf16 bias, the weight gradient (G quantized with its ring, db) and the
+input gradient from G8.  Two copies of the same linear start from the same
+inputs; after a seeding step run eagerly on both, one copy's step is
+captured and replayed while the other runs eagerly.  Between replays the
+program does its own eager work (it rescales X in both copies, so that the
+rings see a changing amax) and synchronizes; every replay must give the
+eager step's bytes exactly: codes, scales, amax, ring state and the bf16
+outputs (the GEMMs are deterministic).  The calls record no memset nodes:
+the library issues only kernels.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_quantize_fp8_amd as F
+from tests.gpu_util import DEV, ring_state
+
+pytestmark = pytest.mark.gpu
+
+FX, FG = F.FP8_E4M3, F.FP8_E5M2
+
+
+class Linear:
+    """Buffers, rings and the bound calls of one linear's step on a stream."""
+
+    def __init__(self, X, W, b, G, stream, hist_len=4):
+        M, K = X.shape
+        N = W.shape[0]
+        e = lambda *s, dt=torch.uint8: torch.empty(*s, dtype=dt, device=DEV)
+        z = lambda: torch.zeros(1, dtype=torch.float32, device=DEV)
+        self.X, self.W, self.b, self.G = (t.to(DEV).clone() for t in (X, W, b, G))
+        self.x8, self.w8, self.g8 = e(M, K), e(N, K), e(M, N)
+        self.y, self.dx, self.dw = e(M, N, dt=torch.bfloat16), e(M, K, dt=torch.bfloat16), \
+            e(N, K, dt=torch.bfloat16)
+        self.db = e(N, dt=torch.bfloat16)
+        self.ws = e(max(1, F.fp8_db_workspace_bytes(M, N) // 4), dt=torch.float32)
+        self.sx, self.sw, self.sg, self.ax, self.aw, self.ag = (z() for _ in range(6))
+        self.rx, self.rw, self.rg = (F.ScaleRing(hist_len, stream=stream) for _ in range(3))
+        x8q = F.Quantized(self.x8, FX, self.sx)
+        w8q = F.Quantized(self.w8, FX, self.sw)
+        g8q = F.Quantized(self.g8, FG, self.sg)
+        self.calls = [
+            F.bind_fp8_quantize_pair(self.X, self.x8, self.rx, self.sx, self.ax, self.W, self.w8,
+                                     self.rw, self.sw, self.aw, FX, stream=stream),
+            F.bind_fp8_linear_fwd(x8q, w8q, self.b, FX, self.y, stream=stream),
+            F.bind_fp8_linear_bwd_dw(self.G, FG, x8q, self.dw, self.db, self.ws, self.rg, self.g8,
+                                     self.sg, self.ag, stream=stream),
+            F.bind_fp8_linear_bwd_dx(g8q, FG, w8q, self.dx, stream=stream),
+        ]
+
+    def step(self):
+        for c in self.calls:
+            c()
+
+    def snapshot(self):
+        out = {k: getattr(self, k).cpu().view(torch.uint8).numpy().copy()
+               for k in ("x8", "w8", "g8", "y", "dx", "dw", "db", "sx", "sw", "sg", "ax", "aw",
+                         "ag")}
+        for name in ("rx", "rw", "rg"):
+            for k, v in ring_state(getattr(self, name)).items():
+                out[f"{name}.{k}"] = np.asarray(v).copy()
+        return out
+
+
+def _inputs(M, K, N, seed):
+    rng = np.random.default_rng(seed)
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    return (bf(rng.standard_normal((M, K))), bf(rng.standard_normal((N, K)) * 0.02),
+            bf(rng.standard_normal(N) * 0.01), bf(rng.standard_normal((M, N)) * 1e-3))
+
+
+# (384, 320, 640): 128x128 tiles; (2048, 256, 4096): the 256x256 8-wave kernel
+@pytest.mark.parametrize("M,K,N", [(384, 320, 640), (2048, 256, 4096)])
+def test_graph_replays_match_eager(M, K, N):
+    stream = torch.cuda.Stream()
+    X0, W, b, G = _inputs(M, K, N, seed=M + N)
+    eager = Linear(X0, W, b, G, stream)
+    graphed = Linear(X0, W, b, G, stream)
+    with torch.cuda.stream(stream):
+        eager.step()  # seeding step: the first call through each ring
+        graphed.step()
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        graphed.step()
+    torch.cuda.synchronize()
+
+    x0 = X0.to(DEV).float()
+    for i, f in enumerate((1.0, 3.0, 0.25, 8.0, 1.0)):
+        with torch.cuda.stream(stream):
+            xi = (x0 * f).to(torch.bfloat16)
+            eager.X.copy_(xi)
+            graphed.X.copy_(xi)
+            eager.step()
+            g.replay()
+        torch.cuda.synchronize()
+        a, r = eager.snapshot(), graphed.snapshot()
+        for k in a:
+            assert np.array_equal(a[k], r[k]), f"replay {i}: {k} differs from the eager step"
