@@ -66,9 +66,12 @@ def parse():
                    help="no GPU: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of "
                         "'--only KIND' and '--only copy' runs into the HBM-traffic record that "
                         "the roofline entry reads, and exit")
+    p.add_argument("--mfma-from", default=None, metavar="MFMAUTIL_CSV",
+                   help="no GPU: turn a rocprofv3 --pmc MfmaUtil CSV of an '--only gemm' run "
+                        "into the per-kind MFMA-utilisation record under profiles/, and exit")
     p.add_argument("--only", default=None,
-                   help="profiling aid: run only this kernel class (fwd, dx, dw, quant, copy) "
-                        "for --steps iterations and exit")
+                   help="profiling aid: run only this kernel class (fwd, dx, dw, gemm = all "
+                        "three, quant, copy) for --steps iterations and exit")
     return p.parse_args()
 
 
@@ -207,17 +210,35 @@ def _pmc_per_dispatch(path, counter):
     return out
 
 
+def traffic_key(kind, workload):
+    """Name of the traffic record of a GEMM kind (fwd, dx, dw) or of the
+    quantize (quant) on a workload."""
+    return f"quant_{workload}" if kind == "quant" else f"gemm_{kind}_{workload}"
+
+
+def quant_launch_bytes(workload):
+    """Algorithmic bytes of the '--only quant' launches of one step (the
+    flat quantize of X, W and G of every linear, bf16 in, fp8 out)."""
+    from scaled_quantize_fp8_amd import workloads as WL
+    wl = WL.WORKLOADS[workload]
+    return [3.0 * n for L in wl.linears for n in (wl.M * L.K, L.N * L.K, wl.M * L.N)]
+
+
 def traffic_record(kind, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload):
-    """HBM bytes per launch of the KIND GEMM kernel: FETCH_SIZE and WRITE_SIZE
-    averaged over its dispatches, each scaled by the factor that makes the
-    same counter read COPY_BYTES for the 256 MiB copy of the calibration run."""
+    """HBM bytes per launch of the KIND GEMM kernel (or of the flat quantize,
+    KIND quant): FETCH_SIZE and WRITE_SIZE averaged over its dispatches,
+    each scaled by the factor that makes the same counter read COPY_BYTES
+    for the 256 MiB copy of the calibration run."""
     def per_kernel(path, counter, match):
         vals = [v for name, v in _pmc_per_dispatch(path, counter).values() if match(name)]
         if not vals:
             raise SystemExit(f"{path}: no dispatch of the kernel with {counter}")
         return sum(vals) / len(vals), len(vals)
 
-    is_gemm = lambda n: gemm_kind_of(n) == kind
+    if kind == "quant":
+        is_gemm = lambda n: "fp8l::quantize_flat_kernel<" in n
+    else:
+        is_gemm = lambda n: gemm_kind_of(n) == kind
     # the copy: the largest dispatches of the calibration run (torch's copy_)
     def copy_kib(path, counter):
         vals = sorted(v for _, v in _pmc_per_dispatch(path, counter).values())
@@ -232,7 +253,52 @@ def traffic_record(kind, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, w
             "dispatches": [n_f, n_w], "fetch_kib_raw": fetch_kib, "write_kib_raw": write_kib,
             "fetch_scale": f_scale, "write_scale": w_scale,
             "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
-            "hbm_bytes_per_launch": rd + wr}
+            "hbm_bytes_per_launch": rd + wr,
+            **({"algorithmic_bytes_per_launch": sum(quant_launch_bytes(workload))
+                / len(quant_launch_bytes(workload))} if kind == "quant" else {})}
+
+
+def mfma_record(csv_path, workload):
+    """MFMA utilisation (MfmaUtil: MFMA-busy cycles over active cycles x
+    SIMDs, in percent) of each GEMM kind, averaged over its dispatches in a
+    rocprofv3 --pmc MfmaUtil run of '--only gemm'."""
+    by = {}
+    for name, v in _pmc_per_dispatch(csv_path, "MfmaUtil").values():
+        kind = gemm_kind_of(name)
+        if kind:
+            by.setdefault(kind, []).append(v)
+    if not by:
+        raise SystemExit(f"{csv_path}: no GEMM dispatch with MfmaUtil")
+    return {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+            "mfma_util_pct": {k: round(sum(v) / len(v), 2) for k, v in sorted(by.items())},
+            "dispatches": {k: len(v) for k, v in sorted(by.items())}}
+
+
+def load_mfma(workload):
+    """Per-kind MFMA utilisation (percent) from the committed record, or None
+    if absent or taken on different kernel sources."""
+    path = os.path.join(PROFILE_DIR, f"mfma_util_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("mfma_util_pct")
+
+
+def load_quant_traffic(workload):
+    """Measured vs algorithmic HBM bytes per flat-quantize launch from the
+    committed record, or None if absent or taken on different sources."""
+    path = traffic_path(traffic_key("quant", workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return {"hbm_bytes_per_launch": round(rec["hbm_bytes_per_launch"]),
+            "algorithmic_bytes_per_launch": round(rec["algorithmic_bytes_per_launch"])}
 
 
 def traffic_path(kernel_key: str) -> str:
@@ -496,7 +562,15 @@ def main():
         kind, *csvs = args.traffic_from
         rec = traffic_record(kind, *csvs, workload=args.workload)
         os.makedirs(PROFILE_DIR, exist_ok=True)
-        with open(traffic_path(f"gemm_{kind}_{args.workload}"), "w") as f:
+        with open(traffic_path(traffic_key(kind, args.workload)), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
+    if args.mfma_from:
+        rec = mfma_record(args.mfma_from, args.workload)
+        os.makedirs(PROFILE_DIR, exist_ok=True)
+        with open(os.path.join(PROFILE_DIR, f"mfma_util_{args.workload}.txt"), "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")
         print(json.dumps(rec))
@@ -554,15 +628,11 @@ def main():
                     dst.copy_(src)
                     continue
                 for L in layers:
-                    if args.only == "fwd":
-                        L.gemm_fwd()
-                    elif args.only == "dx":
-                        L.bwd_dx()
-                    elif args.only == "dw":
-                        L.gemm_dw()
-                    elif args.only == "quant":
-                        for w in ("X", "W", "G"):
-                            L.quant[w]()
+                    calls = {"fwd": [L.gemm_fwd], "dx": [L.bwd_dx], "dw": [L.gemm_dw],
+                             "gemm": [L.gemm_fwd, L.bwd_dx, L.gemm_dw],
+                             "quant": [L.quant[w] for w in ("X", "W", "G")]}[args.only]
+                    for fn in calls:
+                        fn()
         torch.cuda.synchronize()
         print(json.dumps({"only": args.only, "steps": args.steps}))
         return
@@ -660,7 +730,7 @@ def main():
               "(dX = G8 W8, W8 read crosswise; tile chosen per shape)",
     }
     achieved = live["flops"] / (live["avg_ms"] * 1e-3) / 1e12
-    traffic = load_traffic(f"gemm_{dom}_" + args.workload)
+    traffic = load_traffic(traffic_key(dom, args.workload))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_FP8_DENSE_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP8_DENSE_TFLOPS, 4),
                 "traffic": traffic,
@@ -671,6 +741,7 @@ def main():
                 "live_us_per_step": (None if live["total_ms"] is None
                                      else round(live["total_ms"] * 1e3, 1)),
                 "isolated_gemm_us_per_step": {k: round(v, 1) for k, v in tot.items()},
+                "mfma_util_pct_by_kind": load_mfma(args.workload),
                 "dominant_gemm_by_isolated_totals": dominant_isolated}
 
     out = {
@@ -691,6 +762,7 @@ def main():
         "pct_fp8_peak": round(100 * tflops / MI355X_FP8_DENSE_TFLOPS, 2),
         "quantize_GBps": round(quant_gbps, 1),
         "quantize_pct_hbm": round(100 * quant_gbps / MI355X_HBM_GBPS, 2),
+        "quantize_traffic": load_quant_traffic(args.workload),
         "wall_s_timed": round(wall, 4),
         "graph_ms_per_step": None if graph_ms_per_step is None else round(graph_ms_per_step, 4),
         "graph_TFLOPs": None if graph_ms_per_step is None else
