@@ -167,6 +167,24 @@ def event_time_ms(torch, fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
+def bracket_overhead_us(torch, fn, reps, stream):
+    """How much longer a launch measures when an event pair brackets it on
+    its own (as the live roofline figures do) than its share of one pair
+    around reps back-to-back launches: both taken on the same call, behind
+    a GPU sleep, in microseconds."""
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(reps)]
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(2_000_000)
+        for a, b in pairs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+    pairs[-1][1].synchronize()
+    single = sum(a.elapsed_time(b) for a, b in pairs) / reps
+    return 1e3 * (single - event_time_ms(torch, fn, reps, stream))
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "scaled_quantize_fp8_amd", "csrc")
@@ -216,12 +234,19 @@ def traffic_key(kind, workload):
     return f"quant_{workload}" if kind == "quant" else f"gemm_{kind}_{workload}"
 
 
-def quant_launch_bytes(workload):
-    """Algorithmic bytes of the '--only quant' launches of one step (the
-    flat quantize of X, W and G of every linear, bf16 in, fp8 out)."""
+def quant_launch_bytes(workload, dispatches):
+    """Average algorithmic bytes (bf16 in, fp8 out) of the flat-quantize
+    dispatches of an '--only quant --steps S' run: S steps of X, W and G of
+    every linear, plus the X and W quantizes of the seeding step before
+    them (whose G goes through the column-sum kernel)."""
     from scaled_quantize_fp8_amd import workloads as WL
     wl = WL.WORKLOADS[workload]
-    return [3.0 * n for L in wl.linears for n in (wl.M * L.K, L.N * L.K, wl.M * L.N)]
+    xw = [3.0 * n for L in wl.linears for n in (wl.M * L.K, L.N * L.K)]
+    g = [3.0 * wl.M * L.N for L in wl.linears]
+    steps, rem = divmod(dispatches - len(xw), len(xw) + len(g))
+    if rem or steps < 1:
+        raise SystemExit(f"{dispatches} flat-quantize dispatches do not fit whole steps")
+    return (steps * (sum(xw) + sum(g)) + sum(xw)) / dispatches
 
 
 def traffic_record(kind, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload):
@@ -249,13 +274,21 @@ def traffic_record(kind, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, w
     w_scale = COPY_BYTES / (copy_kib(copy_write_csv, "WRITE_SIZE") * 1024)
     rd = fetch_kib * 1024 * f_scale
     wr = write_kib * 1024 * w_scale
+    runs = [f"rocprofv3 --pmc {c} --output-format csv -d $REPO/gpurun_out/traffic -o t_{w}_{c} -- "
+            f"python3 $REPO/bench.py --only {w} --steps 3"
+            for w in (kind, "copy") for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    cmds = ["cd /tmp && export TMPDIR=/tmp"] + runs + [
+        f"python3 bench.py --traffic-from {kind} " + " ".join(
+            f"gpurun_out/traffic/t_{w}_{c}_counter_collection.csv"
+            for w in (kind, "copy") for c in ("FETCH_SIZE", "WRITE_SIZE"))]
     return {"kernel_kind": kind, "workload": workload, "kernel_source_hash": kernel_source_hash(),
+            "commands": cmds,
             "dispatches": [n_f, n_w], "fetch_kib_raw": fetch_kib, "write_kib_raw": write_kib,
             "fetch_scale": f_scale, "write_scale": w_scale,
             "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
             "hbm_bytes_per_launch": rd + wr,
-            **({"algorithmic_bytes_per_launch": sum(quant_launch_bytes(workload))
-                / len(quant_launch_bytes(workload))} if kind == "quant" else {})}
+            **({"algorithmic_bytes_per_launch": quant_launch_bytes(workload, n_f)}
+               if kind == "quant" else {})}
 
 
 def mfma_record(csv_path, workload):
@@ -269,7 +302,11 @@ def mfma_record(csv_path, workload):
             by.setdefault(kind, []).append(v)
     if not by:
         raise SystemExit(f"{csv_path}: no GEMM dispatch with MfmaUtil")
-    return {"workload": workload, "kernel_source_hash": kernel_source_hash(),
+    cmds = ["cd /tmp && export TMPDIR=/tmp",
+            "rocprofv3 --pmc MfmaUtil --output-format csv -d $REPO/gpurun_out/traffic -o t_gemm_MfmaUtil "
+            "-- python3 $REPO/bench.py --only gemm --steps 3",
+            "python3 bench.py --mfma-from gpurun_out/traffic/t_gemm_MfmaUtil_counter_collection.csv"]
+    return {"workload": workload, "kernel_source_hash": kernel_source_hash(), "commands": cmds,
             "mfma_util_pct": {k: round(sum(v) / len(v), 2) for k, v in sorted(by.items())},
             "dispatches": {k: len(v) for k, v in sorted(by.items())}}
 
@@ -738,6 +775,9 @@ def main():
                 "launch_avg_us": round(live["avg_ms"] * 1e3, 2),
                 "flops_per_launch": live["flops"],
                 "live_launches": live["launches"],
+                "live_bracket_overhead_us": round(sum(
+                    bracket_overhead_us(torch, getattr(L, {"fwd": "gemm_fwd", "dx": "bwd_dx"}[dom]),
+                                        args.kernel_reps, stream) for L in layers) / len(layers), 2),
                 "live_us_per_step": (None if live["total_ms"] is None
                                      else round(live["total_ms"] * 1e3, 1)),
                 "isolated_gemm_us_per_step": {k: round(v, 1) for k, v in tot.items()},
