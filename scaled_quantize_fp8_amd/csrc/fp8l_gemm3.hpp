@@ -169,54 +169,6 @@ FP8L_DEV void mfma_only(const MfmaSlot (&m)[4]) {
 #undef FP8L_ONLY
 }
 
-template <int FA, int FB, int NM>
-FP8L_DEV void fused_kc(const uint32_t ad[4], v8i& n0, v8i& n1, const MfmaSlot (&m)[4]) {
-  v4i r0, r1, r2, r3;
-#define FP8L_KC(n)                                                                        \
-  asm volatile("ds_read_b128 %[r0], %[a0]\n\t"                                            \
-               "ds_read_b128 %[r1], %[a1]\n\t"                                            \
-               "ds_read_b128 %[r2], %[a2]\n\t"                                            \
-               "ds_read_b128 %[r3], %[a3]\n\t" FP8L_MF##n "s_waitcnt lgkmcnt(0)"          \
-               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3), FP8L_CO##n \
-               : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]),      \
-                 FP8L_CI##n, FP8L_FMT                                                     \
-               : "memory")
-  if constexpr (NM == 1) FP8L_KC(1);
-  else if constexpr (NM == 2) FP8L_KC(2);
-  else if constexpr (NM == 3) FP8L_KC(3);
-  else FP8L_KC(4);
-#undef FP8L_KC
-  n0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-  n1 = v8i{r2.x, r2.y, r2.z, r2.w, r3.x, r3.y, r3.z, r3.w};
-}
-
-template <int FA, int FB, int NM>
-FP8L_DEV void fused_x(const uint32_t ad[8], v8i& n0, v8i& n1, const MfmaSlot (&m)[4]) {
-  v2i r0, r1, r2, r3, r4, r5, r6, r7;
-#define FP8L_X(n)                                                                            \
-  asm volatile("ds_read_b64_tr_b8 %[r0], %[a0]\n\t"                                          \
-               "ds_read_b64_tr_b8 %[r1], %[a1]\n\t"                                          \
-               "ds_read_b64_tr_b8 %[r2], %[a2]\n\t"                                          \
-               "ds_read_b64_tr_b8 %[r3], %[a3]\n\t"                                          \
-               "ds_read_b64_tr_b8 %[r4], %[a4]\n\t"                                          \
-               "ds_read_b64_tr_b8 %[r5], %[a5]\n\t"                                          \
-               "ds_read_b64_tr_b8 %[r6], %[a6]\n\t"                                          \
-               "ds_read_b64_tr_b8 %[r7], %[a7]\n\t" FP8L_MF##n "s_waitcnt lgkmcnt(0)"        \
-               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3),             \
-                 [r4] "=&v"(r4), [r5] "=&v"(r5), [r6] "=&v"(r6), [r7] "=&v"(r7), FP8L_CO##n \
-               : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]),         \
-                 [a4] "v"(ad[4]), [a5] "v"(ad[5]), [a6] "v"(ad[6]), [a7] "v"(ad[7]),         \
-                 FP8L_CI##n, FP8L_FMT                                                        \
-               : "memory")
-  if constexpr (NM == 1) FP8L_X(1);
-  else if constexpr (NM == 2) FP8L_X(2);
-  else if constexpr (NM == 3) FP8L_X(3);
-  else FP8L_X(4);
-#undef FP8L_X
-  n0 = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
-  n1 = v8i{r4.x, r4.y, r5.x, r5.y, r6.x, r6.y, r7.x, r7.y};
-}
-
 // VALU reads of MFMA results need wait states the compiler cannot insert
 // for asm MFMAs (a 16-pass MFMA needs 18); pad generously.
 FP8L_DEV void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
@@ -466,19 +418,6 @@ struct Op3 {
         }
       }
     }
-  }
-
-  // Reads of a fragment pair for the next step fused with NM MFMAs of the
-  // current one.
-  template <int FA, int FB, int NM>
-  FP8L_DEV static void read2_fused(const uint8_t* s, int f0, v8i& n0, v8i& n1,
-                                   const MfmaSlot (&m)[4]) {
-    uint32_t a[8];
-    frag_addrs(s, f0, a);
-    if constexpr (L == kKContig)
-      fused_kc<FA, FB, NM>(a, n0, n1, m);
-    else
-      fused_x<FA, FB, NM>(a, n0, n1, m);
   }
 
   FP8L_DEV static void read2(const uint8_t* s, int f0, v8i& x0, v8i& x1) {

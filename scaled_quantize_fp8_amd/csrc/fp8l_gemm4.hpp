@@ -23,57 +23,6 @@
 
 namespace fp8l {
 
-// One fragment (32 rows x 64 k) read fused with NM MFMAs; k-contiguous tiles
-// take two ds_read_b128, crosswise tiles four ds_read_b64_tr_b8.
-template <int FA, int FB, int NM>
-FP8L_DEV void fused_kc1(const uint32_t ad[2], v8i& n0, const MfmaSlot (&m)[4]) {
-  v4i r0, r1;
-#define FP8L_KC1(n)                                                                  \
-  asm volatile("ds_read_b128 %[r0], %[a0]\n\t"                                       \
-               "ds_read_b128 %[r1], %[a1]\n\t" FP8L_MF##n "s_waitcnt lgkmcnt(0)"     \
-               : [r0] "=&v"(r0), [r1] "=&v"(r1), FP8L_CO##n                          \
-               : [a0] "v"(ad[0]), [a1] "v"(ad[1]), FP8L_CI##n, FP8L_FMT              \
-               : "memory")
-  if constexpr (NM == 1) FP8L_KC1(1);
-  else if constexpr (NM == 2) FP8L_KC1(2);
-  else if constexpr (NM == 3) FP8L_KC1(3);
-  else FP8L_KC1(4);
-#undef FP8L_KC1
-  n0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-}
-
-template <int FA, int FB, int NM>
-FP8L_DEV void fused_x1(const uint32_t ad[4], v8i& n0, const MfmaSlot (&m)[4]) {
-  v2i r0, r1, r2, r3;
-#define FP8L_X1(n)                                                                        \
-  asm volatile("ds_read_b64_tr_b8 %[r0], %[a0]\n\t"                                       \
-               "ds_read_b64_tr_b8 %[r1], %[a1]\n\t"                                       \
-               "ds_read_b64_tr_b8 %[r2], %[a2]\n\t"                                       \
-               "ds_read_b64_tr_b8 %[r3], %[a3]\n\t" FP8L_MF##n "s_waitcnt lgkmcnt(0)"     \
-               : [r0] "=&v"(r0), [r1] "=&v"(r1), [r2] "=&v"(r2), [r3] "=&v"(r3),          \
-                 FP8L_CO##n                                                               \
-               : [a0] "v"(ad[0]), [a1] "v"(ad[1]), [a2] "v"(ad[2]), [a3] "v"(ad[3]),      \
-                 FP8L_CI##n, FP8L_FMT                                                     \
-               : "memory")
-  if constexpr (NM == 1) FP8L_X1(1);
-  else if constexpr (NM == 2) FP8L_X1(2);
-  else if constexpr (NM == 3) FP8L_X1(3);
-  else FP8L_X1(4);
-#undef FP8L_X1
-  n0 = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
-}
-
-// Read one fragment of operand Op (tile index f) fused with NM MFMAs.
-template <typename Op, int FA, int FB, int NM>
-FP8L_DEV void read1_fused(const uint8_t* s, int f, v8i& n0, const MfmaSlot (&m)[4]) {
-  uint32_t a[8];
-  Op::frag_addrs(s, f, a);  // the first fragment of the pair at f
-  if constexpr (Op::kLayout == kKContig)
-    fused_kc1<FA, FB, NM>(a, n0, m);
-  else
-    fused_x1<FA, FB, NM>(a, n0, m);
-}
-
 // LDS: the operand ring or the staged output tile, then the bias of the
 // block's 256 columns (BiasStage).
 constexpr int kGemm4BiasOff =

@@ -28,36 +28,6 @@
 
 namespace fp8l {
 
-// One fragment (tile index f) of operand Op, read without MFMAs.
-template <typename Op>
-FP8L_DEV void read1(const uint8_t* s, int f, v8i& n0) {
-  uint32_t a[8];
-  Op::frag_addrs(s, f, a);  // the first fragment of the pair at f
-  if constexpr (Op::kLayout == kKContig) {
-    v4i r0, r1;
-    asm volatile(
-        "ds_read_b128 %0, %2\n\t"
-        "ds_read_b128 %1, %3\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1)
-        : "v"(a[0]), "v"(a[1])
-        : "memory");
-    n0 = v8i{r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
-  } else {
-    v2i r0, r1, r2, r3;
-    asm volatile(
-        "ds_read_b64_tr_b8 %0, %4\n\t"
-        "ds_read_b64_tr_b8 %1, %5\n\t"
-        "ds_read_b64_tr_b8 %2, %6\n\t"
-        "ds_read_b64_tr_b8 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-        : "memory");
-    n0 = v8i{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
-  }
-}
-
 // One operand staged 128 bytes of K at a time (two 64-byte sub-steps), R
 // rows or columns of C, NW waves; same interface for both layouts:
 //   kBytes        LDS bytes per stage
