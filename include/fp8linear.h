@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FP8_ABI_VERSION 2
+#define FP8_ABI_VERSION 3
 #define FP8_RING_MAX_HIST 1024
 
 typedef enum {
@@ -322,6 +322,45 @@ int fp8_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, fp8_operand_t a, in
              int64_t lda, int64_t stride_a, fp8_operand_t b, int32_t layout_b, int64_t ldb,
              int64_t stride_b, fp8_operand_t bias, void* c, int64_t ldc, int64_t stride_c,
              hipStream_t stream);
+
+/*
+ * FP8-in / FP8-out GEMM ([P1] entry on the custom op for an FP8-in/FP8-out
+ * GEMM on pre-quantized operands; [P1] entry on the fp8 bias dequantized
+ * after the operand scaling and before any output quantization; [P3] entry
+ * on dropping the fp8-output template parameter, after which every other
+ * GEMM here writes bf16).  The forward layout, pre-quantized:
+ *
+ *   y[i, j] = sum_k A(i, k) B(j, k) / (sa sb) + bias[j]        (fp32)
+ *   c8[i, j] = enc_fmt_out( fl32( y[i, j] * s_out ) )
+ *
+ * y is the fp32 value the bf16-output GEMMs round to bf16 (fp32
+ * accumulation, one fma with the bias); enc is the quantize's conversion
+ * (round to nearest even, saturating, NaN -> 0x7F | sign).  s_out comes from
+ * the output's delayed-scaling ring exactly as fp8_quantize takes it: the
+ * ring's current scale, or, on the ring's first use, S(max |y|) from an
+ * extra amax pass over the same GEMM (two launches instead of one).  The
+ * launch's last block then folds max |y| (over the M x N outputs) into
+ * hist[idx], advances idx and publishes fmt_max / max(hist) as the next
+ * scale, as a quantize launch does.
+ *
+ *   a, b       fp8 codes (E4M3 or E5M2) with device scales: A [M,K] and
+ *              B [N,K], both k-contiguous (rows of K codes).
+ *   bias       [N]: data NULL = none; BF16; or fp8 codes with scale =
+ *              bias_scale (dec(b8)/bias_scale).
+ *   fmt_out    FP8_E4M3 or FP8_E5M2: the format of c8.
+ *   ring_out   required: the output's scale ring (fp8_ring_init).
+ *   c8         device [M,N] bytes out, 16-byte aligned.
+ *   scale_used device float out, required: the s_out the codes were made
+ *              with (dequantize c8 by 1/s_out).
+ *   amax_out   device float out or NULL: max |y|.
+ * Shapes: K and N multiples of 16, a, b and c8 16-byte aligned (one tiled
+ * kernel runs it), else FP8_ERR_SHAPE; any M.  M or N = 0 does nothing.
+ * Errors: as fp8_gemm, plus FP8_ERR_RING for an invalid ring or a
+ * scale_used / amax_out inside the ring header.
+ */
+int fp8_gemm_fp8out(int64_t M, int64_t N, int64_t K, fp8_operand_t a, fp8_operand_t b,
+                    fp8_operand_t bias, int32_t fmt_out, fp8_ring_t* ring_out, uint8_t* c8,
+                    float* scale_used, float* amax_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

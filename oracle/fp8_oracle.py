@@ -324,6 +324,25 @@ def bias_grad(g_values) -> GemmRef:
                    abs_sum=np.abs(g).sum(axis=0))
 
 
+def gemm_fp8out(a8, fmt_a: int, b8, fmt_b: int, sa, sb, bias, fmt_out: int,
+                ring: ScaleRing):
+    """FP8-in / FP8-out GEMM ([P1] entry on the custom op for an FP8-in /
+    FP8-out GEMM; [P1] entry on the fp8 bias dequantized after the operand
+    scaling and before any output quantization).
+
+    y[m,n] = sum_k a8[m,k] b8[n,k] / (sa sb) + bias[n], as linear_fwd, and
+    the output is one quantize step of fl32(y) with the output's ring.
+    Reading: the pages name the op only; what is quantized is the fp32
+    value the bf16-output GEMM would round, with the quantize's own scale
+    and ring rules.  bias: None or float64 values (bias_values).  Returns
+    (q, s_used, amax, ref)."""
+    A = decode_array(a8, fmt_a)
+    B = decode_array(b8, fmt_b)
+    ref = _finish(A @ B.T, np.abs(A) @ np.abs(B).T, _inv(sa) * _inv(sb), bias)
+    q, s_used, a = quantize_step(ref.r.astype(np.float32), fmt_out, ring)
+    return q, s_used, a, ref
+
+
 def dequantized(q, fmt: int, s) -> np.ndarray:
     """dec(q) / s in float64."""
     return decode_array(q, fmt) / float(np.float32(s))

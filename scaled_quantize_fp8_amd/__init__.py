@@ -32,7 +32,7 @@ _FMT_DT = {FP8_E4M3: FP8_DT_E4M3, FP8_E5M2: FP8_DT_E5M2}
 C_SYMBOLS = (
     "fp8_abi_version", "fp8_status_str", "fp8_ring_bytes", "fp8_ring_init", "fp8_quantize",
     "fp8_quantize_pair", "fp8_linear_fwd", "fp8_linear_bwd_dx", "fp8_db_workspace_bytes",
-    "fp8_linear_bwd_dw", "fp8_gemm", "fp8_quantize_2d",
+    "fp8_linear_bwd_dw", "fp8_gemm", "fp8_quantize_2d", "fp8_gemm_fp8out",
 )
 
 
@@ -80,9 +80,10 @@ def lib() -> ctypes.CDLL:
         L.fp8_quantize_2d.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, rp, vp, vp, vp]
         L.fp8_gemm.argtypes = [i64, i64, i64, i64, op, i32, i64, i64, op, i32, i64, i64, op, vp,
                                i64, i64, vp]
+        L.fp8_gemm_fp8out.argtypes = [i64, i64, i64, op, op, op, i32, rp, vp, vp, vp, vp]
         for name in ("fp8_ring_init", "fp8_quantize", "fp8_quantize_pair", "fp8_quantize_2d",
                      "fp8_linear_fwd", "fp8_gemm", "fp8_linear_bwd_dx",
-                     "fp8_linear_bwd_dw"):
+                     "fp8_linear_bwd_dw", "fp8_gemm_fp8out"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -353,3 +354,28 @@ def fp8_gemm(a, b, c, bias=None, stream=None):
 def bind_fp8_gemm(a, b, c, bias=None, stream=None):
     return _bind("fp8_gemm", _gemm_args(a, b, c, bias, stream))
 
+
+
+def _gemm_fp8out_args(a, b, c8, fmt_out, ring_out, scale_used, amax_out, bias, stream):
+    M, K = a.codes.shape
+    N = b.codes.shape[0]
+    if b.codes.shape[1] != K or tuple(c8.shape) != (M, N):
+        raise ValueError("fp8_gemm_fp8out: a [M,K], b [N,K], c8 [M,N]")
+    return (ctypes.c_int64(M), ctypes.c_int64(N), ctypes.c_int64(K), _operand(a), _operand(b),
+            _operand(bias), ctypes.c_int32(fmt_out), _ring(ring_out), _vp(c8), _vp(scale_used),
+            _vp(amax_out), ctypes.c_void_p(_stream(stream)))
+
+
+def fp8_gemm_fp8out(a, b, c8, fmt_out, ring_out, scale_used, amax_out=None, bias=None,
+                    stream=None):
+    """c8 = enc_fmt_out(fl32(y * s_out)), y = a b^T / (sa sb) (+ bias) in fp32,
+    s_out from ring_out (delayed scaling; folded with max |y|).  a, b:
+    Quantized with contiguous codes [M, K] and [N, K]; c8: uint8 [M, N]."""
+    _check(lib().fp8_gemm_fp8out(*_gemm_fp8out_args(a, b, c8, fmt_out, ring_out, scale_used,
+                                                    amax_out, bias, stream)), "fp8_gemm_fp8out")
+
+
+def bind_fp8_gemm_fp8out(a, b, c8, fmt_out, ring_out, scale_used, amax_out=None, bias=None,
+                         stream=None):
+    return _bind("fp8_gemm_fp8out", _gemm_fp8out_args(a, b, c8, fmt_out, ring_out, scale_used,
+                                                      amax_out, bias, stream))

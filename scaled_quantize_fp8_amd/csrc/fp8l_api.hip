@@ -237,14 +237,15 @@ void launch_gemm_t(GemmArgs& g, hipStream_t st) {
                      st, g);
 }
 
-template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB>
+template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB, int EPI = kEpiBF16,
+          int OF = kE4M3>
 void launch_gemm3_t(GemmArgs& g, hipStream_t st) {
   constexpr int lds = gemm3_lds_bytes<BM, BN, WGM, WGN>();
   static bool attr_set[64] = {false};
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    (void)hipFuncSetAttribute((const void*)gemm3_kernel<BM, BN, WGM, WGN, LA, LB, FA, FB>,
+    (void)hipFuncSetAttribute((const void*)gemm3_kernel<BM, BN, WGM, WGN, LA, LB, FA, FB, EPI, OF>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr_set[dev] = true;
   }
@@ -252,7 +253,7 @@ void launch_gemm3_t(GemmArgs& g, hipStream_t st) {
   g.tiles_n = (int32_t)((g.Nc + BN - 1) / BN);
   if (g.tiles_m < 1) g.tiles_m = 1;
   if (g.tiles_n < 1) g.tiles_n = 1;
-  hipLaunchKernelGGL((gemm3_kernel<BM, BN, WGM, WGN, LA, LB, FA, FB>),
+  hipLaunchKernelGGL((gemm3_kernel<BM, BN, WGM, WGN, LA, LB, FA, FB, EPI, OF>),
                      dim3((unsigned)(g.tiles_m * g.tiles_n), (unsigned)g.batch), dim3(64 * WGM * WGN),
                      lds, st, g);
 }
@@ -296,6 +297,21 @@ void launch_gemm3_f(GemmArgs& g, int fa, int fb, hipStream_t st) {
   else if (fa == kE4M3 && fb == kE5M2) launch_gemm3_t<BM, BN, WGM, WGN, LA, LB, kE4M3, kE5M2>(g, st);
   else if (fa == kE5M2 && fb == kE4M3) launch_gemm3_t<BM, BN, WGM, WGN, LA, LB, kE5M2, kE4M3>(g, st);
   else launch_gemm3_t<BM, BN, WGM, WGN, LA, LB, kE5M2, kE5M2>(g, st);
+}
+
+// The FP8-output GEMM runs on gemm3's 128x128 block (4 waves, two blocks
+// per CU) with one of the fp8 epilogues.
+template <int FA, int FB, int EPI, int OF>
+void launch_gemm3_q(GemmArgs& g, hipStream_t st) {
+  launch_gemm3_t<128, 128, 2, 2, kKContig, kKContig, FA, FB, EPI, OF>(g, st);
+}
+
+template <int EPI, int OF>
+void launch_gemm3_q_f(GemmArgs& g, int fa, int fb, hipStream_t st) {
+  if (fa == kE4M3 && fb == kE4M3) launch_gemm3_q<kE4M3, kE4M3, EPI, OF>(g, st);
+  else if (fa == kE4M3 && fb == kE5M2) launch_gemm3_q<kE4M3, kE5M2, EPI, OF>(g, st);
+  else if (fa == kE5M2 && fb == kE4M3) launch_gemm3_q<kE5M2, kE4M3, EPI, OF>(g, st);
+  else launch_gemm3_q<kE5M2, kE5M2, EPI, OF>(g, st);
 }
 
 template <int LA, int LB, int FA, int FB>
@@ -767,5 +783,71 @@ int fp8_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, fp8_operand_t a, in
     launch_gemm_l<kCross, kKContig>(g, fa, fb, stream);
   else
     launch_gemm_l<kCross, kCross>(g, fa, fb, stream);
+  return hip_status();
+}
+
+int fp8_gemm_fp8out(int64_t M, int64_t N, int64_t K, fp8_operand_t a, fp8_operand_t b,
+                    fp8_operand_t bias, int32_t fmt_out, fp8_ring_t* ring_out, uint8_t* c8,
+                    float* scale_used, float* amax_out, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return FP8_ERR_SHAPE;
+  if (!mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return FP8_ERR_SHAPE;
+  if (!is_fp8_dtype(a.dtype) || !is_fp8_dtype(b.dtype) || !valid_fmt(fmt_out)) return FP8_ERR_DTYPE;
+  int bias_kind = kBiasNone;
+  if (bias.data) {
+    if (bias.dtype == FP8_DT_BF16) bias_kind = kBiasBF16;
+    else if (bias.dtype == FP8_DT_E4M3) bias_kind = kBiasE4M3;
+    else if (bias.dtype == FP8_DT_E5M2) bias_kind = kBiasE5M2;
+    else return FP8_ERR_DTYPE;
+    if (bias_kind != kBiasBF16 && !bias.scale) return FP8_ERR_NULL;
+  }
+  if (!a.scale || !b.scale || !scale_used || !ring_out) return FP8_ERR_NULL;
+  int st = check_ring(ring_out);
+  if (st) return st;
+  if (check_alias(ring_out, scale_used) || check_alias(ring_out, amax_out)) return FP8_ERR_RING;
+  if (M == 0 || N == 0) return FP8_OK;
+  if (K > 0 && (!a.data || !b.data)) return FP8_ERR_NULL;
+  if (!c8) return FP8_ERR_NULL;
+  // the one kernel this runs on: 16-byte operand and code pieces that never
+  // straddle a row end, byte offsets that fit a buffer descriptor
+  if (K % 16 != 0 || N % 16 != 0 || !aligned16(a.data) || !aligned16(b.data) || !aligned16(c8) ||
+      (M + 256) * K >= (1LL << 31) || (N + 256) * K >= (1LL << 31))
+    return FP8_ERR_SHAPE;
+
+  GemmArgs g = {};
+  g.a = reinterpret_cast<const uint8_t*>(a.data);
+  g.lda = K;
+  g.b = reinterpret_cast<const uint8_t*>(b.data);
+  g.ldb = K;
+  g.Mc = M;
+  g.Nc = N;
+  g.Kc = K;
+  g.ldc = N;
+  g.scale_a = a.scale;
+  g.scale_b = b.scale;
+  g.bias = bias.data;
+  g.bias_kind = bias_kind;
+  g.bias_scale = bias.scale;
+  g.batch = 1;
+  g.c8 = c8;
+  g.oring = reinterpret_cast<RingHdr*>(ring_out->dev);
+  g.ohist = reinterpret_cast<float*>(reinterpret_cast<char*>(ring_out->dev) + sizeof(RingHdr));
+  g.ohist_len = ring_out->hist_len;
+  g.oscale_used = scale_used;
+  g.oamax = amax_out;
+  finish_gemm_args(g);
+  const int fa = dtype_fmt(a.dtype), fb = dtype_fmt(b.dtype);
+  const bool e4 = fmt_out == FP8_E4M3;
+  if (!ring_out->seeded) {
+    // seeding call: an amax pass leaves max |y| in the ring header, then the
+    // converting pass quantizes with S(max |y|) and folds it into the window
+    launch_gemm3_q_f<kEpiAmax, kE4M3>(g, fa, fb, stream);
+    if (e4) launch_gemm3_q_f<kEpiFp8Seed, kE4M3>(g, fa, fb, stream);
+    else launch_gemm3_q_f<kEpiFp8Seed, kE5M2>(g, fa, fb, stream);
+    ring_out->seeded = 1;
+  } else if (e4) {
+    launch_gemm3_q_f<kEpiFp8Ring, kE4M3>(g, fa, fb, stream);
+  } else {
+    launch_gemm3_q_f<kEpiFp8Ring, kE5M2>(g, fa, fb, stream);
+  }
   return hip_status();
 }

@@ -74,6 +74,14 @@ struct GemmArgs {
   // (bytes) and c + z bsc (elements); a stride of 0 broadcasts the slice
   int64_t bsa, bsb, bsc;
   int32_t batch;  // >= 1
+  // FP8 output (fp8_gemm_fp8out): codes c8 [Mc, ldc], made with the output
+  // ring's scale; the launch's last block folds max |y| into that ring.
+  uint8_t* c8;
+  RingHdr* oring;
+  float* ohist;
+  int32_t ohist_len;
+  float* oscale_used;
+  float* oamax;
 };
 
 // Move the operand pointers to this block's batch slice (blockIdx.y).

@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "fp8l_gemm.hpp"
+#include "fp8l_quantize.hpp"
 
 namespace fp8l {
 
@@ -552,9 +553,100 @@ constexpr int gemm3_lds_bytes() {
   return gemm3_bias_off<BM, BN>() + BiasStage<BN>::kBytes;
 }
 
-template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB>
+// Epilogue of gemm3_kernel: bf16 output, or the FP8-output GEMM's passes
+// (codes with the ring's scale, codes with the scale of a seeding amax pass,
+// or that amax pass alone).
+enum { kEpiBF16 = 0, kEpiFp8Ring = 1, kEpiFp8Seed = 2, kEpiAmax = 3 };
+
+// FP8-output epilogue (fp8_gemm_fp8out).  y = acc (1/sa)(1/sb) + bias in
+// fp32, the value the bf16 epilogue rounds; then q = enc(fl32(y s)) with the
+// output ring's scale s, the quantize kernels' conversion (RNE, saturating,
+// NaN to 0x7F | sign).  Codes are staged in LDS (rows padded by 16 bytes)
+// and stored as 16-byte row pieces (the ragged end of a row byte by byte).
+// max |y| over the block's outputs inside M x N goes to the launch's
+// last-block election, which folds it into the output ring as a quantize
+// launch does; kEpiAmax computes and elects max |y| only, leaving it for
+// the converting pass of a seeding call.  acc: the block's accumulators in
+// gemm3's fragment layout; sbias: the BiasStage area.
+template <int BM, int BN, int WTM, int WTN, int EPI, int OF, int FM, int FN>
+FP8L_DEV void fp8_out_epilogue(const GemmArgs& g, const v16f (&acc)[FM][FN], float dq,
+                               float inv_bs, const uint8_t* sbias, uint8_t* smem, int64_t i0,
+                               int64_t j0, int wm, int wn) {
+  constexpr int RSB = BN + 16;  // LDS bytes per staged row of codes
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint32_t bid = blockIdx.y * gridDim.x + blockIdx.x, total = gridDim.x * gridDim.y;
+  float s = 0.0f;
+  if constexpr (EPI == kEpiFp8Ring) {
+    s = g.oring->scale;
+  } else if constexpr (EPI == kEpiFp8Seed) {
+    // amax left in the header by the amax pass that ran just before
+    const float m = __uint_as_float(
+        __hip_atomic_load(&g.oring->top_amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    s = scale_from_amax(m, FmtTraits<OF>::kMax, g.oring->scale);
+  }
+  const int64_t rows_left = g.Mc - i0, cols_left = g.Nc - j0;
+  uint32_t mx = 0;
+#pragma unroll
+  for (int b = 0; b < FN; ++b) {
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const int jl = wn * WTN + 32 * b + 8 * grp + 4 * (lane >> 5);
+      float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (g.bias_kind != kBiasNone) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bias[t] = BiasStage<BN>::get(g, sbias, j0, jl + t, inv_bs);
+      }
+#pragma unroll
+      for (int a = 0; a < FM; ++a) {
+        const int il = wm * WTM + 32 * a + (lane & 31);
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = __builtin_fmaf(acc[a][b][4 * grp + t], dq, bias[t]);
+        if (il < rows_left) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (jl + t < cols_left) mx = max(mx, absbits(v[t]));
+        }
+        if constexpr (EPI != kEpiAmax)
+          *reinterpret_cast<uint32_t*>(smem + il * RSB + jl) = quant4<OF>(v, s);
+      }
+    }
+  }
+  if constexpr (EPI == kEpiAmax) {
+    amax_pass_finish(g.oring, mx, bid, total);
+  } else {
+    lds_barrier();
+    constexpr int kChunks = BN / 16;
+#pragma unroll 2
+    for (int q = tid; q < BM * kChunks; q += kQThreads) {
+      const int r = q / kChunks, ch = q % kChunks;
+      if (r < rows_left && 16 * ch < cols_left) {
+        uint8_t* dst = g.c8 + (i0 + r) * g.ldc + j0 + 16 * ch;
+        const uint8_t* src = smem + r * RSB + 16 * ch;
+        if (16 * ch + 16 <= cols_left) {
+          __builtin_nontemporal_store(*reinterpret_cast<const v4u*>(src),
+                                      reinterpret_cast<v4u*>(dst));
+        } else {
+          for (int k = 0; k < cols_left - 16 * ch; ++k) dst[k] = src[k];
+        }
+      }
+    }
+    QArgs qa = {};
+    qa.ring = g.oring;
+    qa.hist = g.ohist;
+    qa.hist_len = g.ohist_len;
+    qa.scale_used = g.oscale_used;
+    qa.amax_out = g.oamax;
+    finish_launch<OF, EPI == kEpiFp8Seed ? kScaleSeed : kScaleRing>(qa, mx, s, bid, total);
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB, int EPI = kEpiBF16,
+          int OF = kE4M3>
 __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN <= 128 * 128) ? 2 : 1)
 void gemm3_kernel(GemmArgs g) {
+  static_assert(EPI == kEpiBF16 || WGM * WGN * 64 == kQThreads,
+                "the FP8-output epilogue's election takes 256-thread blocks");
   batch_slice(g);
   constexpr int NW = WGM * WGN;
   using OA = Op3<LA, BM, NW>;
@@ -753,6 +845,10 @@ void gemm3_kernel(GemmArgs g) {
   side_work<64 * WGM * WGN>(g);    // after the drain: it may reuse fragment registers
   barrier_only();                  // every wave is done reading operand tiles
   const float dq = es.dq(), inv_bs = es.inv_bs();
+  if constexpr (EPI != kEpiBF16) {
+    fp8_out_epilogue<BM, BN, WTM, WTN, EPI, OF>(g, acc, dq, inv_bs, sbias, smem3, i0, j0, wm, wn);
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < FN; ++b) {
 #pragma unroll

@@ -117,6 +117,20 @@ FP8L_DEV uint2 quant8(const float v[8], float s, uint32_t lane_max) {
   return make_uint2(w[0], w[1]);
 }
 
+// Quantize 4 values with scale s into one packed word, NaN as in quant8.
+template <int FMT>
+FP8L_DEV uint32_t quant4(const float v[4], float s) {
+  uint32_t w = cvt4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (absbits(v[i]) > 0x7f800000u) {
+      const uint32_t code = 0x7fu | ((__float_as_uint(v[i]) >> 24) & 0x80u);
+      w = (w & ~(0xffu << (8 * i))) | (code << (8 * i));
+    }
+  }
+  return w;
+}
+
 // Elements [e, e + cnt), cnt <= 8, one at a time (ragged or unaligned).
 // vals receives the values (0 past cnt).  Returns the max |x| bits.
 template <int IN, int FMT>
@@ -184,6 +198,22 @@ FP8L_DEV uint32_t gather_amax(RingHdr* h, uint32_t total, bool consume, uint32_t
   if (threadIdx.x < G) m = atom_xchg(&h->group[threadIdx.x].amax, 0u);
   else if (consume && threadIdx.x == G) m = atom_xchg(&h->top_amax, 0u);
   return block_max_u32(m, sh4);
+}
+
+// End of an amax pass (the first pass of a seeding quantize, or of a
+// seeding FP8-output GEMM): the launch's last block leaves max |x| in the
+// ring header's top_amax, the counters back at zero, for the converting
+// launch that follows.  mx: this thread's max |x| bits.
+FP8L_DEV void amax_pass_finish(RingHdr* h, uint32_t mx, uint32_t bid, uint32_t total) {
+  __shared__ uint32_t sh4[4];
+  __shared__ uint32_t sh_flag;
+  const uint32_t bm = block_max_u32(mx, sh4);
+  if (threadIdx.x == 0)
+    sh_flag = (elect_group(h, bid, total, bm) && elect_top(h, total)) ? 1u : 0u;
+  __syncthreads();
+  if (!sh_flag) return;
+  const uint32_t amax_bits = gather_amax(h, total, false, sh4);
+  if (threadIdx.x == 0) atom_xchg(&h->top_amax, amax_bits);
 }
 
 // Scale the launch quantizes with.
@@ -464,15 +494,7 @@ FP8L_DEV uint32_t flat_absmax(const void* x, int64_t n, int vec_ok) {
 template <int IN>
 __global__ __launch_bounds__(kQThreads) void amax_ring_kernel(const void* x, int64_t n, int vec_ok,
                                                              RingHdr* h) {
-  __shared__ uint32_t sh4[4];
-  __shared__ uint32_t sh_flag;
-  const uint32_t bm = block_max_u32(flat_absmax<IN>(x, n, vec_ok), sh4);
-  if (threadIdx.x == 0)
-    sh_flag = (elect_group(h, blockIdx.x, gridDim.x, bm) && elect_top(h, gridDim.x)) ? 1u : 0u;
-  __syncthreads();
-  if (!sh_flag) return;
-  const uint32_t amax_bits = gather_amax(h, gridDim.x, false, sh4);
-  if (threadIdx.x == 0) atom_xchg(&h->top_amax, amax_bits);
+  amax_pass_finish(h, flat_absmax<IN>(x, n, vec_ok), blockIdx.x, gridDim.x);
 }
 
 // amax pass of a dynamic quantize: one device atomic max per block into

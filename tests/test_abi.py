@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8_abi_version() == 2
+    assert F.fp8_abi_version() == 3
     for st in range(6):
         assert F.status_str(st)
     assert F.status_str(99) == "unknown status"

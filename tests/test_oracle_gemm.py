@@ -197,3 +197,30 @@ def test_tolerance_contract_shape():
     tol = O.gemm_tolerance(ref)
     X, W = O.decode_array(x8, O.E4M3), O.decode_array(w8, O.E4M3)
     assert np.allclose(tol, 2.0 ** -7 * (np.abs(X) @ np.abs(W).T) / 8.0 + O.bf16_ulp(ref.r))
+
+
+def test_fp8out_hand_worked_steps():
+    """The FP8-output GEMM on a 2x2x2 case worked by hand: A = [[1, 2],
+    [3, 1]], B = [[1, 0], [1, 1]] (e4m3 codes 0x38 = 1, 0x40 = 2, 0x44 = 3),
+    sa = sb = 1, so A B^T = [[1, 3], [3, 4]].
+      step 0, bias [0, 3]: y = [[1, 6], [3, 7]]; the fresh ring seeds
+        s = 448 / 7 = 64; y s = 64, 384, 192, 448 -> 0x68, 0x7C, 0x74, 0x7E;
+        hist [7, 0, 0], next scale 64.
+      step 1, bias [0, 1]: y = [[1, 4], [3, 5]]; s = 64; y s = 64, 256,
+        192, 320 -> 0x68, 0x78, 0x74, 0x7A; hist [7, 5, 0], scale 64.
+      step 2, bias [0, 10]: y = [[1, 13], [3, 14]]; s = 64; 832 and 896
+        saturate to 448 (0x7E); hist [7, 5, 14], next scale 448 / 14 = 32."""
+    a8 = np.array([[0x38, 0x40], [0x44, 0x38]], dtype=np.uint8)
+    b8 = np.array([[0x38, 0x00], [0x38, 0x38]], dtype=np.uint8)
+    ring = O.ScaleRing(3)
+    expect = [
+        ([0.0, 3.0], [[0x68, 0x7C], [0x74, 0x7E]], 64.0, 7.0, [7, 0, 0], 64.0),
+        ([0.0, 1.0], [[0x68, 0x78], [0x74, 0x7A]], 64.0, 5.0, [7, 5, 0], 64.0),
+        ([0.0, 10.0], [[0x68, 0x7E], [0x74, 0x7E]], 64.0, 14.0, [7, 5, 14], 32.0),
+    ]
+    for bias, codes, s_used, a, hist, nxt in expect:
+        q, s, am, _ = O.gemm_fp8out(a8, O.E4M3, b8, O.E4M3, 1.0, 1.0, np.array(bias),
+                                     O.E4M3, ring)
+        assert q.tolist() == codes
+        assert float(s) == s_used and float(am) == a
+        assert ring.hist.tolist() == hist and float(ring.scale) == nxt
