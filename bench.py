@@ -195,9 +195,10 @@ def kernel_source_hash() -> str:
 
 
 COPY_BYTES = 256 << 20            # the --only copy calibration moves this much each way
-# GEMM kinds by the last four template arguments <.., LA, LB, FA, FB> of the
-# pipelined kernels (gemm3_kernel<BM, BN, WGM, WGN, ...>, gemm4_kernel<...>,
-# gemm5_kernel<...>)
+# GEMM kinds by the operand template arguments <.., LA, LB, FA, FB> of the
+# pipelined kernels: the first four of gemm4_kernel<...> and gemm5_kernel<...>,
+# the four after BM, BN, WGM, WGN of gemm3_kernel<...> (followed there by its
+# epilogue mode and output format)
 KIND_OPERANDS = {"fwd": (0, 0, 0, 0), "dx": (0, 1, 1, 0), "dw": (1, 1, 1, 0)}
 
 
@@ -206,7 +207,13 @@ def gemm_kind_of(kernel_name: str):
     head = kernel_name.split("(")[0].replace("void ", "").strip()
     if not any(head.startswith(f"fp8l::gemm{v}_kernel<") for v in (3, 4, 5)):
         return None
-    args = tuple(int(a) for a in head[head.index("<") + 1:head.rindex(">")].split(","))[-4:]
+    targs = [int(a) for a in head[head.index("<") + 1:head.rindex(">")].split(",")]
+    if head.startswith("fp8l::gemm3_kernel<"):
+        if len(targs) > 8 and targs[8] != 0:  # an FP8-output epilogue
+            return None
+        args = tuple(targs[4:8])
+    else:
+        args = tuple(targs[:4])
     for kind, ops in KIND_OPERANDS.items():
         if args == ops:
             return kind
@@ -525,7 +532,7 @@ def widened_rows(torch, F, WL, wl, layers, stream, reps):
     """Isolated timings of the entry points beyond the layer step (not part of
     the step or its value): the transposed and dual quantize, the weight
     gradient run k-contiguous from transposed operands next to the crosswise
-    one, and a batched fp8_gemm."""
+    one, a batched fp8_gemm, and the FP8-output forward next to the bf16 one."""
     dev = "cuda:0"
     up = next(L for L in layers if L.name == "up")
     M, N, K = up.M, up.N, up.K
@@ -570,6 +577,20 @@ def widened_rows(torch, F, WL, wl, layers, stream, reps):
     us = 1e3 * event_time_ms(torch, bmm, reps, stream)
     res["gemm_batched_8x1024x2048x2048_us"] = round(us, 2)
     res["gemm_batched_8x1024x2048x2048_TFLOPs"] = round(2.0 * B * bm * bn * bk / (us * 1e-6) / 1e12, 1)
+    # FP8-in / FP8-out forward of up (2048 x 6912 x 1536), steady ring, next
+    # to the bf16-output forward of the same operands
+    c8 = torch.empty(M, N, dtype=torch.uint8, device=dev)
+    ring = F.ScaleRing(wl.hist_len, stream=stream)
+    su, am = (torch.zeros(1, dtype=torch.float32, device=dev) for _ in range(2))
+    q8 = F.bind_fp8_gemm_fp8out(F.Quantized(up.x8, F.FP8_E4M3, up.sx),
+                                F.Quantized(up.w8, F.FP8_E4M3, up.sw), c8, F.FP8_E4M3, ring, su,
+                                am, bias=up.b, stream=stream)
+    q8()  # seeds the ring (amax pass + converting pass)
+    us_q = 1e3 * event_time_ms(torch, q8, reps, stream)
+    us_b = 1e3 * event_time_ms(torch, up.gemm_fwd, reps, stream)
+    res["gemm_fp8out_up_fwd_us"] = round(us_q, 2)
+    res["gemm_fp8out_up_fwd_TFLOPs"] = round(flops / (us_q * 1e-6) / 1e12, 1)
+    res["gemm_bf16out_up_fwd_us"] = round(us_b, 2)
     res["e2e_train_step"] = e2e_train_step(torch, dev)
     return res
 
