@@ -299,29 +299,16 @@ void launch_gemm3_f(GemmArgs& g, int fa, int fb, hipStream_t st) {
   else launch_gemm3_t<BM, BN, WGM, WGN, LA, LB, kE5M2, kE5M2>(g, st);
 }
 
-// The FP8-output GEMM runs on gemm3's 128x128 block (4 waves, two blocks
-// per CU) with one of the fp8 epilogues.
-template <int FA, int FB, int EPI, int OF>
-void launch_gemm3_q(GemmArgs& g, hipStream_t st) {
-  launch_gemm3_t<128, 128, 2, 2, kKContig, kKContig, FA, FB, EPI, OF>(g, st);
-}
 
-template <int EPI, int OF>
-void launch_gemm3_q_f(GemmArgs& g, int fa, int fb, hipStream_t st) {
-  if (fa == kE4M3 && fb == kE4M3) launch_gemm3_q<kE4M3, kE4M3, EPI, OF>(g, st);
-  else if (fa == kE4M3 && fb == kE5M2) launch_gemm3_q<kE4M3, kE5M2, EPI, OF>(g, st);
-  else if (fa == kE5M2 && fb == kE4M3) launch_gemm3_q<kE5M2, kE4M3, EPI, OF>(g, st);
-  else launch_gemm3_q<kE5M2, kE5M2, EPI, OF>(g, st);
-}
 
-template <int LA, int LB, int FA, int FB>
+template <int LA, int LB, int FA, int FB, int EPI = kEpiBF16, int OF = kE4M3>
 void launch_gemm4_t(GemmArgs& g, hipStream_t st) {
   constexpr int lds = gemm4_lds_bytes();
   static bool attr_set[64] = {false};
   int dev = 0;
   (void)hipGetDevice(&dev);
   if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    (void)hipFuncSetAttribute((const void*)gemm4_kernel<LA, LB, FA, FB>,
+    (void)hipFuncSetAttribute((const void*)gemm4_kernel<LA, LB, FA, FB, EPI, OF>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr_set[dev] = true;
   }
@@ -329,7 +316,7 @@ void launch_gemm4_t(GemmArgs& g, hipStream_t st) {
   g.tiles_n = (int32_t)((g.Nc + 255) / 256);
   if (g.tiles_m < 1) g.tiles_m = 1;
   if (g.tiles_n < 1) g.tiles_n = 1;
-  hipLaunchKernelGGL((gemm4_kernel<LA, LB, FA, FB>),
+  hipLaunchKernelGGL((gemm4_kernel<LA, LB, FA, FB, EPI, OF>),
                      dim3((unsigned)(g.tiles_m * g.tiles_n), (unsigned)g.batch), dim3(512), lds, st,
                      g);
 }
@@ -340,6 +327,26 @@ void launch_gemm4_f(GemmArgs& g, int fa, int fb, hipStream_t st) {
   else if (fa == kE4M3 && fb == kE5M2) launch_gemm4_t<LA, LB, kE4M3, kE5M2>(g, st);
   else if (fa == kE5M2 && fb == kE4M3) launch_gemm4_t<LA, LB, kE5M2, kE4M3>(g, st);
   else launch_gemm4_t<LA, LB, kE5M2, kE5M2>(g, st);
+}
+
+// The FP8-output GEMM runs with one of the fp8 epilogues on the 256x256
+// 8-wave kernel when its tiles fill at least half the CUs (the bf16 rule),
+// else on gemm3's 128x128 block (4 waves, two blocks per CU).
+template <int FA, int FB, int EPI, int OF>
+void launch_fp8out_t(GemmArgs& g, hipStream_t st) {
+  const int64_t tiles256 = ((g.Mc + 255) / 256) * ((g.Nc + 255) / 256);
+  if (2 * tiles256 >= cu_count())
+    launch_gemm4_t<kKContig, kKContig, FA, FB, EPI, OF>(g, st);
+  else
+    launch_gemm3_t<128, 128, 2, 2, kKContig, kKContig, FA, FB, EPI, OF>(g, st);
+}
+
+template <int EPI, int OF>
+void launch_fp8out(GemmArgs& g, int fa, int fb, hipStream_t st) {
+  if (fa == kE4M3 && fb == kE4M3) launch_fp8out_t<kE4M3, kE4M3, EPI, OF>(g, st);
+  else if (fa == kE4M3 && fb == kE5M2) launch_fp8out_t<kE4M3, kE5M2, EPI, OF>(g, st);
+  else if (fa == kE5M2 && fb == kE4M3) launch_fp8out_t<kE5M2, kE4M3, EPI, OF>(g, st);
+  else launch_fp8out_t<kE5M2, kE5M2, EPI, OF>(g, st);
 }
 
 template <int LA, int LB, int FA, int FB>
@@ -840,14 +847,14 @@ int fp8_gemm_fp8out(int64_t M, int64_t N, int64_t K, fp8_operand_t a, fp8_operan
   if (!ring_out->seeded) {
     // seeding call: an amax pass leaves max |y| in the ring header, then the
     // converting pass quantizes with S(max |y|) and folds it into the window
-    launch_gemm3_q_f<kEpiAmax, kE4M3>(g, fa, fb, stream);
-    if (e4) launch_gemm3_q_f<kEpiFp8Seed, kE4M3>(g, fa, fb, stream);
-    else launch_gemm3_q_f<kEpiFp8Seed, kE5M2>(g, fa, fb, stream);
+    launch_fp8out<kEpiAmax, kE4M3>(g, fa, fb, stream);
+    if (e4) launch_fp8out<kEpiFp8Seed, kE4M3>(g, fa, fb, stream);
+    else launch_fp8out<kEpiFp8Seed, kE5M2>(g, fa, fb, stream);
     ring_out->seeded = 1;
   } else if (e4) {
-    launch_gemm3_q_f<kEpiFp8Ring, kE4M3>(g, fa, fb, stream);
+    launch_fp8out<kEpiFp8Ring, kE4M3>(g, fa, fb, stream);
   } else {
-    launch_gemm3_q_f<kEpiFp8Ring, kE5M2>(g, fa, fb, stream);
+    launch_fp8out<kEpiFp8Ring, kE5M2>(g, fa, fb, stream);
   }
   return hip_status();
 }

@@ -567,23 +567,32 @@ enum { kEpiBF16 = 0, kEpiFp8Ring = 1, kEpiFp8Seed = 2, kEpiAmax = 3 };
 // last-block election, which folds it into the output ring as a quantize
 // launch does; kEpiAmax computes and elects max |y| only, leaving it for
 // the converting pass of a seeding call.  acc: the block's accumulators in
-// gemm3's fragment layout; sbias: the BiasStage area.
-template <int BM, int BN, int WTM, int WTN, int EPI, int OF, int FM, int FN>
+// the pipelined kernels' fragment layout; s: the output scale (out_scale);
+// sbias: the BiasStage area; NT: threads per block.
+// Scale of the FP8-output epilogue: the ring's, or (seeding) S of the max
+// the amax pass left in the header.  Kernels read it at their start, with
+// the other scales, so the epilogue does not wait for it; the previous
+// launch on the stream, which wrote it, has completed by then.
+template <int EPI, int OF>
+FP8L_DEV float out_scale(const GemmArgs& g) {
+  if constexpr (EPI == kEpiFp8Ring) {
+    return g.oring->scale;
+  } else if constexpr (EPI == kEpiFp8Seed) {
+    const float m = __uint_as_float(
+        __hip_atomic_load(&g.oring->top_amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    return scale_from_amax(m, FmtTraits<OF>::kMax, g.oring->scale);
+  } else {
+    return 0.0f;
+  }
+}
+
+template <int BM, int BN, int WTM, int WTN, int EPI, int OF, int NT, int FM, int FN>
 FP8L_DEV void fp8_out_epilogue(const GemmArgs& g, const v16f (&acc)[FM][FN], float dq,
-                               float inv_bs, const uint8_t* sbias, uint8_t* smem, int64_t i0,
-                               int64_t j0, int wm, int wn) {
+                               float inv_bs, float s, const uint8_t* sbias, uint8_t* smem,
+                               int64_t i0, int64_t j0, int wm, int wn) {
   constexpr int RSB = BN + 16;  // LDS bytes per staged row of codes
   const int tid = threadIdx.x, lane = tid & 63;
   const uint32_t bid = blockIdx.y * gridDim.x + blockIdx.x, total = gridDim.x * gridDim.y;
-  float s = 0.0f;
-  if constexpr (EPI == kEpiFp8Ring) {
-    s = g.oring->scale;
-  } else if constexpr (EPI == kEpiFp8Seed) {
-    // amax left in the header by the amax pass that ran just before
-    const float m = __uint_as_float(
-        __hip_atomic_load(&g.oring->top_amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    s = scale_from_amax(m, FmtTraits<OF>::kMax, g.oring->scale);
-  }
   const int64_t rows_left = g.Mc - i0, cols_left = g.Nc - j0;
   uint32_t mx = 0;
 #pragma unroll
@@ -613,12 +622,12 @@ FP8L_DEV void fp8_out_epilogue(const GemmArgs& g, const v16f (&acc)[FM][FN], flo
     }
   }
   if constexpr (EPI == kEpiAmax) {
-    amax_pass_finish(g.oring, mx, bid, total);
+    amax_pass_finish<NT>(g.oring, mx, bid, total);
   } else {
     lds_barrier();
     constexpr int kChunks = BN / 16;
 #pragma unroll 2
-    for (int q = tid; q < BM * kChunks; q += kQThreads) {
+    for (int q = tid; q < BM * kChunks; q += NT) {
       const int r = q / kChunks, ch = q % kChunks;
       if (r < rows_left && 16 * ch < cols_left) {
         uint8_t* dst = g.c8 + (i0 + r) * g.ldc + j0 + 16 * ch;
@@ -637,7 +646,7 @@ FP8L_DEV void fp8_out_epilogue(const GemmArgs& g, const v16f (&acc)[FM][FN], flo
     qa.hist_len = g.ohist_len;
     qa.scale_used = g.oscale_used;
     qa.amax_out = g.oamax;
-    finish_launch<OF, EPI == kEpiFp8Seed ? kScaleSeed : kScaleRing>(qa, mx, s, bid, total);
+    finish_launch<OF, EPI == kEpiFp8Seed ? kScaleSeed : kScaleRing, NT>(qa, mx, s, bid, total);
   }
 }
 
@@ -645,8 +654,6 @@ template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB, int 
           int OF = kE4M3>
 __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN <= 128 * 128) ? 2 : 1)
 void gemm3_kernel(GemmArgs g) {
-  static_assert(EPI == kEpiBF16 || WGM * WGN * 64 == kQThreads,
-                "the FP8-output epilogue's election takes 256-thread blocks");
   batch_slice(g);
   constexpr int NW = WGM * WGN;
   using OA = Op3<LA, BM, NW>;
@@ -690,6 +697,7 @@ void gemm3_kernel(GemmArgs g) {
   // prologue: DMA steps 0..3, then step 0's fragments
   BiasStage<BN>::load(g, j0, sbias, wv);  // ahead of the stages (see BiasStage)
   const EpiScales es = load_scales(g);
+  const float s_out = out_scale<EPI, OF>(g);
   for (int s = 0; s < kStages3 && s < nk; ++s) {
     oa.issue(ra, step_buf(s), s);
     ob.issue(rb, step_buf(s) + OA::kBytes, s);
@@ -846,7 +854,8 @@ void gemm3_kernel(GemmArgs g) {
   barrier_only();                  // every wave is done reading operand tiles
   const float dq = es.dq(), inv_bs = es.inv_bs();
   if constexpr (EPI != kEpiBF16) {
-    fp8_out_epilogue<BM, BN, WTM, WTN, EPI, OF>(g, acc, dq, inv_bs, sbias, smem3, i0, j0, wm, wn);
+    fp8_out_epilogue<BM, BN, WTM, WTN, EPI, OF, 64 * WGM * WGN>(g, acc, dq, inv_bs, s_out, sbias,
+                                                                smem3, i0, j0, wm, wn);
     return;
   }
 #pragma unroll

@@ -28,7 +28,7 @@ namespace fp8l {
 constexpr int kGemm4BiasOff =
     kStages3 * 512 * kBK3 > 256 * (256 * 2 + 16) ? kStages3 * 512 * kBK3 : 256 * (256 * 2 + 16);
 
-template <int LA, int LB, int FA, int FB>
+template <int LA, int LB, int FA, int FB, int EPI = kEpiBF16, int OF = kE4M3>
 __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   batch_slice(g);
   constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4, NW = WGM * WGN;
@@ -93,6 +93,7 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   // prologue: DMA steps 0..3, read step 0, issue its first two MFMAs
   BiasStage<BN>::load(g, j0, sbias, wv);  // ahead of the stages (see BiasStage)
   const EpiScales es = load_scales(g);
+  const float s_out = out_scale<EPI, OF>(g);
   for (int s = 0; s < kStages3 && s <= nk; ++s) issue_step(s);
   if (nk > 0) {
     const int later = min(3, nk);  // steps 1..min(3, nk) may still be in flight
@@ -111,9 +112,9 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   // A fragments, fb[CUR] its B fragments.
   // FAST: the refill of this step (step kt+4) lies wholly inside K, so its
   // loads take the whole-operand resources with the advance as scalar
-  // offset (issue_full), the refill is
-  // unconditional and the wait count is fixed; the last steps take the
-  // general form (partial step, the zero step past K, no refill).
+  // offset (issue_full), the refill is unconditional and the wait count is
+  // fixed; the last steps take the general form (partial step, the zero
+  // step past K, no refill).
   const __amdgpu_buffer_rsrc_t ra_all = make_rsrc(g.a, a_bytes);
   const __amdgpu_buffer_rsrc_t rb_all = make_rsrc(g.b, b_bytes);
   auto kstep_body = [&](int kt, auto cur_tag, auto fast_tag) {
@@ -214,6 +215,11 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   side_work<64 * NW>(g);  // after the drain: its VALU work may reuse fragment registers
   const float dq = es.dq(), inv_bs = es.inv_bs();
   barrier_only();
+  if constexpr (EPI != kEpiBF16) {
+    fp8_out_epilogue<BM, BN, WTM, WTN, EPI, OF, 64 * NW>(g, acc, dq, inv_bs, s_out, sbias, smem4,
+                                                         i0, j0, wm, wn);
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < FN; ++b) {
 #pragma unroll

@@ -149,13 +149,18 @@ FP8L_DEV uint32_t quant_scalar8(const void* x, uint8_t* q, int64_t e, int cnt, f
   return mx;
 }
 
-// Block-wide max of non-negative float bits (all 256 threads participate).
-FP8L_DEV uint32_t block_max_u32(uint32_t v, uint32_t* sh4) {
+// Block-wide max of non-negative float bits (all NT threads participate;
+// sh holds one word per wave).
+template <int NT = kQThreads>
+FP8L_DEV uint32_t block_max_u32(uint32_t v, uint32_t* sh) {
+  static_assert(NT % 64 == 0 && NT <= 1024, "whole waves");
   v = wave_max_u32(v);
   const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) sh4[wave] = v;
+  if ((threadIdx.x & 63) == 0) sh[wave] = v;
   __syncthreads();
-  const uint32_t r = max(max(sh4[0], sh4[1]), max(sh4[2], sh4[3]));
+  uint32_t r = sh[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) r = max(r, sh[w]);
   __syncthreads();
   return r;
 }
@@ -191,28 +196,31 @@ FP8L_DEV bool elect_top(RingHdr* h, uint32_t total) {
 // and that ticket before the top ticket that made this block the last.
 // consume: also take (and clear) the header max that the amax pass of a
 // seeding quantize leaves for the converting launch.
-FP8L_DEV uint32_t gather_amax(RingHdr* h, uint32_t total, bool consume, uint32_t* sh4) {
+template <int NT = kQThreads>
+FP8L_DEV uint32_t gather_amax(RingHdr* h, uint32_t total, bool consume, uint32_t* sh) {
   const uint32_t G = total < (uint32_t)kGroups ? total : (uint32_t)kGroups;
-  static_assert(kGroups < kQThreads, "one lane per group plus one");
+  static_assert(kGroups < NT, "one lane per group plus one");
   uint32_t m = 0;
   if (threadIdx.x < G) m = atom_xchg(&h->group[threadIdx.x].amax, 0u);
   else if (consume && threadIdx.x == G) m = atom_xchg(&h->top_amax, 0u);
-  return block_max_u32(m, sh4);
+  return block_max_u32<NT>(m, sh);
 }
 
 // End of an amax pass (the first pass of a seeding quantize, or of a
 // seeding FP8-output GEMM): the launch's last block leaves max |x| in the
 // ring header's top_amax, the counters back at zero, for the converting
-// launch that follows.  mx: this thread's max |x| bits.
+// launch that follows.  mx: this thread's max |x| bits; NT: threads per
+// block.
+template <int NT = kQThreads>
 FP8L_DEV void amax_pass_finish(RingHdr* h, uint32_t mx, uint32_t bid, uint32_t total) {
-  __shared__ uint32_t sh4[4];
+  __shared__ uint32_t sh[NT / 64];
   __shared__ uint32_t sh_flag;
-  const uint32_t bm = block_max_u32(mx, sh4);
+  const uint32_t bm = block_max_u32<NT>(mx, sh);
   if (threadIdx.x == 0)
     sh_flag = (elect_group(h, bid, total, bm) && elect_top(h, total)) ? 1u : 0u;
   __syncthreads();
   if (!sh_flag) return;
-  const uint32_t amax_bits = gather_amax(h, total, false, sh4);
+  const uint32_t amax_bits = gather_amax<NT>(h, total, false, sh);
   if (threadIdx.x == 0) atom_xchg(&h->top_amax, amax_bits);
 }
 
@@ -237,15 +245,16 @@ FP8L_DEV float launch_scale(const QArgs& a) {
 // End of a converting launch: dynamic -> block 0 writes scale_used; ring ->
 // elect the last block, which folds amax into the window and publishes the
 // next scale.  s is the scale this launch used (the snapshot in scale_used).
-template <int FMT, int SMODE>
+// NT: threads per block.
+template <int FMT, int SMODE, int NT = kQThreads>
 FP8L_DEV void finish_launch(const QArgs& a, uint32_t mx, float s, uint32_t bid, uint32_t total) {
-  __shared__ uint32_t sh4[4];
+  __shared__ uint32_t sh4[NT / 64];
   __shared__ uint32_t sh_flag;
   if constexpr (SMODE == kScaleDyn) {
     if (bid == 0 && threadIdx.x == 0) *a.scale_used = s;
     return;
   } else {
-    const uint32_t bm = block_max_u32(mx, sh4);
+    const uint32_t bm = block_max_u32<NT>(mx, sh4);
     if (threadIdx.x == 0) sh_flag = elect_group(a.ring, bid, total, bm) ? 1u : 0u;
     __syncthreads();
     if (!sh_flag) return;
@@ -254,10 +263,10 @@ FP8L_DEV void finish_launch(const QArgs& a, uint32_t mx, float s, uint32_t bid, 
     // block writes them, and only after it has won, so what a winner reads
     // here is the state the previous launch left.
     const int H = a.hist_len;
-    uint32_t hv[FP8_RING_MAX_HIST / kQThreads];
+    uint32_t hv[FP8_RING_MAX_HIST / NT];
 #pragma unroll
-    for (int k = 0; k < FP8_RING_MAX_HIST / kQThreads; ++k) {
-      const int j = threadIdx.x + k * kQThreads;
+    for (int k = 0; k < FP8_RING_MAX_HIST / NT; ++k) {
+      const int j = threadIdx.x + k * NT;
       hv[k] = j < H ? __float_as_uint(a.hist[j]) : 0u;
     }
     const uint32_t idx = a.ring->idx % (uint32_t)H;  // in range even for a corrupted header
@@ -265,14 +274,14 @@ FP8L_DEV void finish_launch(const QArgs& a, uint32_t mx, float s, uint32_t bid, 
     if (threadIdx.x == 0) sh_flag = elect_top(a.ring, total) ? 1u : 0u;
     __syncthreads();
     if (!sh_flag) return;
-    const uint32_t amax_bits = gather_amax(a.ring, total, true, sh4);
+    const uint32_t amax_bits = gather_amax<NT>(a.ring, total, true, sh4);
     uint32_t m = 0;
 #pragma unroll
-    for (int k = 0; k < FP8_RING_MAX_HIST / kQThreads; ++k) {
-      const int j = threadIdx.x + k * kQThreads;
+    for (int k = 0; k < FP8_RING_MAX_HIST / NT; ++k) {
+      const int j = threadIdx.x + k * NT;
       if (j < H) m = max(m, (uint32_t)j == idx ? amax_bits : hv[k]);
     }
-    m = block_max_u32(m, sh4);
+    m = block_max_u32<NT>(m, sh4);
     if (threadIdx.x == 0) {
       a.hist[idx] = __uint_as_float(amax_bits);
       a.ring->idx = (idx + 1 == (uint32_t)H) ? 0u : idx + 1;

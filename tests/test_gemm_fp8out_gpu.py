@@ -59,10 +59,13 @@ def _run(a8, fa, b8, fb, sa, sb, bias_t, fmt_out, ring):
 
 
 # (160, 384, 272): a ragged block row (160 = 128 + 32), three block columns;
-# (1024, 256, 1536): 96 blocks, more than the 64 election groups
+# (1024, 256, 1536): 96 blocks, more than the 64 election groups;
+# (2000, 256, 4096): 128 tiles of 256x256 (the 8-wave kernel), a ragged last
+# tile row (2000 = 7 x 256 + 208)
 @pytest.mark.parametrize("fa,fb,M,K,N", [(O.E4M3, O.E4M3, 160, 384, 272),
                                          (O.E5M2, O.E4M3, 160, 384, 272),
-                                         (O.E4M3, O.E4M3, 1024, 256, 1536)])
+                                         (O.E4M3, O.E4M3, 1024, 256, 1536),
+                                         (O.E4M3, O.E5M2, 2000, 256, 4096)])
 @pytest.mark.parametrize("fmt_out", [O.E4M3, O.E5M2])
 def test_fp8out_exact_steps(fa, fb, M, K, N, fmt_out):
     rng = np.random.default_rng(7 + 3 * fa + fmt_out + M)
