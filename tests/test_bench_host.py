@@ -1,0 +1,118 @@
+"""Host logic of the benchmark, on the CPU: which kernel a profiled
+dispatch counts for, the algorithmic bytes of the quantize launches, and
+the HBM bytes per launch from rocprofv3 counter CSVs scaled by the copy
+calibration.  No GPU and no kernel call."""
+
+import csv
+
+import pytest
+
+import bench
+
+GEMM3 = "void fp8l::gemm3_kernel<128, 128, 2, 2, {}>(fp8l::GemmArgs)"
+GEMM4 = "void fp8l::gemm4_kernel<{}, 0, 0>(fp8l::GemmArgs)"
+GEMM5 = "void fp8l::gemm5_kernel<{}>(fp8l::GemmArgs)"
+
+
+@pytest.mark.parametrize("ops,kind", [("0, 0, 0, 0", "fwd"), ("0, 1, 1, 0", "dx"),
+                                      ("1, 1, 1, 0", "dw"), ("1, 0, 0, 1", None)])
+def test_gemm_kind_of_operand_args(ops, kind):
+    assert bench.gemm_kind_of(GEMM4.format(ops)) == kind
+    assert bench.gemm_kind_of(GEMM5.format(ops)) == kind
+    # gemm3: the operand arguments follow BM, BN, WGM, WGN; with and without
+    # the trailing epilogue mode and output format (bf16 epilogue = 0)
+    assert bench.gemm_kind_of(GEMM3.format(ops)) == kind
+    assert bench.gemm_kind_of(GEMM3.format(ops + ", 0, 0")) == kind
+
+
+def test_gemm_kind_of_excludes_other_kernels():
+    # an FP8-output epilogue (mode 1..3) is not one of the three linear GEMMs
+    for epi in (1, 2, 3):
+        assert bench.gemm_kind_of(GEMM3.format(f"0, 0, 0, 0, {epi}, 0")) is None
+    for name in ("void fp8l::quantize_flat_kernel<2, 0, 0>(fp8l::QArgs)",
+                 "void fp8l::amax_ring_kernel<2>(void const*, long, int, fp8l::RingHdr*)",
+                 "__amd_rocclr_copyBuffer", "void fp8l::gemm6_kernel<0, 0, 0, 0>(x)"):
+        assert bench.gemm_kind_of(name) is None
+
+
+# (K, N) of the dim1536 layer's five linears: qkv, out, up, gate, down
+_DIM1536 = [(1536, 4608), (1536, 1536), (1536, 6912), (1536, 6912), (6912, 1536)]
+
+
+def test_quant_launch_bytes_counts_whole_steps():
+    M = 2048
+    xw = sum(3 * (M * K + N * K) for K, N in _DIM1536)   # bf16 in, one fp8 byte out
+    g = sum(3 * M * N for K, N in _DIM1536)
+    # 3 steps of 15 launches after the seeding step's 10 (its G is quantized
+    # by the column-sum kernel, which is not a flat-quantize dispatch)
+    assert bench.quant_launch_bytes("dim1536_m2048", 55) == pytest.approx(
+        (3 * (xw + g) + xw) / 55, rel=1e-12)
+    for bad in (54, 10, 9):
+        with pytest.raises(SystemExit):
+            bench.quant_launch_bytes("dim1536_m2048", bad)
+
+
+_FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Kernel_Name", "Counter_Name",
+           "Counter_Value"]
+
+
+def _pmc_csv(path, counter, dispatches):
+    """A rocprofv3 --pmc CSV: one row per (dispatch, per-XCD part) of the
+    counter, plus a row of another counter that must be ignored."""
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=_FIELDS)
+        w.writeheader()
+        for d, (name, parts) in enumerate(dispatches, start=1):
+            for v in parts:
+                w.writerow({"Correlation_Id": d, "Dispatch_Id": d, "Agent_Id": "Agent 1",
+                            "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v})
+            w.writerow({"Correlation_Id": d, "Dispatch_Id": d, "Agent_Id": "Agent 1",
+                        "Kernel_Name": name, "Counter_Name": "GRBM_COUNT", "Counter_Value": 1e9})
+    return str(path)
+
+
+def test_traffic_record_scales_by_copy_calibration(tmp_path):
+    fwd = GEMM4.format("0, 0, 0, 0")
+    dx = GEMM5.format("0, 1, 1, 0")
+    copy = "__amd_rocclr_copyBuffer"
+    fill = "void at::native::vectorized_elementwise_kernel<4>(int)"
+    # the forward kernel: two dispatches, values split over rows and summed
+    fetch = _pmc_csv(tmp_path / "f.csv", "FETCH_SIZE",
+                     [(fwd, [1000.0, 2000.0]), (dx, [9e9]), (fwd, [5000.0]), (fill, [1.0])])
+    write = _pmc_csv(tmp_path / "w.csv", "WRITE_SIZE",
+                     [(fwd, [300.0]), (dx, [9e9]), (fwd, [100.0, 100.0])])
+    cb = bench.COPY_BYTES
+    # the copy reads 2x what it moves by this counter and writes it 1x; the
+    # largest dispatch is the calibration copy
+    cfetch = _pmc_csv(tmp_path / "cf.csv", "FETCH_SIZE",
+                      [(fill, [4.0]), (copy, [2 * cb / 1024 / 2] * 2), (copy, [7.0])])
+    cwrite = _pmc_csv(tmp_path / "cw.csv", "WRITE_SIZE", [(copy, [cb / 1024]), (fill, [3.0])])
+    rec = bench.traffic_record("fwd", fetch, write, cfetch, cwrite, "dim1536_m2048")
+    assert rec["dispatches"] == [2, 2]
+    assert rec["fetch_kib_raw"] == 4000.0 and rec["write_kib_raw"] == 250.0
+    assert rec["fetch_scale"] == pytest.approx(0.5) and rec["write_scale"] == pytest.approx(1.0)
+    assert rec["hbm_read_bytes_per_launch"] == pytest.approx(4000.0 * 1024 * 0.5)
+    assert rec["hbm_write_bytes_per_launch"] == pytest.approx(250.0 * 1024)
+    assert rec["hbm_bytes_per_launch"] == pytest.approx((2000.0 + 250.0) * 1024)
+    assert rec["kernel_source_hash"] == bench.kernel_source_hash()
+    assert "algorithmic_bytes_per_launch" not in rec
+    assert all("rocprofv3 --pmc" in c for c in rec["commands"][1:5])
+
+
+def test_traffic_record_quant_and_missing_kernel(tmp_path):
+    q = "void fp8l::quantize_flat_kernel<2, 0, 1>(fp8l::QArgs)"
+    pair = "void fp8l::quantize_flat2_kernel<2, 0>(fp8l::QArgs, fp8l::QArgs, unsigned int)"
+    copy = "__amd_rocclr_copyBuffer"
+    cb = bench.COPY_BYTES
+    fetch = _pmc_csv(tmp_path / "f.csv", "FETCH_SIZE", [(q, [10.0])] * 55 + [(pair, [1e6])])
+    write = _pmc_csv(tmp_path / "w.csv", "WRITE_SIZE", [(q, [5.0])] * 55)
+    cf = _pmc_csv(tmp_path / "cf.csv", "FETCH_SIZE", [(copy, [cb / 1024])])
+    cw = _pmc_csv(tmp_path / "cw.csv", "WRITE_SIZE", [(copy, [cb / 1024])])
+    rec = bench.traffic_record("quant", fetch, write, cf, cw, "dim1536_m2048")
+    assert rec["dispatches"] == [55, 55]
+    assert rec["hbm_bytes_per_launch"] == pytest.approx(15.0 * 1024)
+    assert rec["algorithmic_bytes_per_launch"] == pytest.approx(
+        bench.quant_launch_bytes("dim1536_m2048", 55))
+    # a CSV without the kernel is an error, not a zero
+    with pytest.raises(SystemExit):
+        bench.traffic_record("dx", fetch, write, cf, cw, "dim1536_m2048")
