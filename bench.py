@@ -8,13 +8,15 @@ dW = G8^T X8 / (sg sx), db) and the input gradient (dX = G8 W8 / (sg sw)):
 15 FP8 GEMMs and 15 quantizes.  Inputs are seeded synthetic bf16 tensors,
 resident in HBM before the timed region.
 
-Each linear is issued as fp8_quantize_pair(X, W) (one launch quantizing X
-and W with their rings), fp8_linear_fwd(X8, W8) (the GEMM), then
-fp8_linear_bwd_dw(G) (quantize G with column partials, then the dW GEMM
-with db) and fp8_linear_bwd_dx(G8) (the dX GEMM): the kernels the one-call
-fp8_linear_fwd(X, W) launches, with each GEMM a call of its own so that a
-forward or dX GEMM launch can be bracketed with events in the timed region
-for the roofline entry (one launch per step, rotating over the linears).
+The step runs in a training step's order: every forward, as
+fp8_quantize_pair(X, W) (one launch quantizing X and W with their rings) and
+fp8_linear_fwd(X8, W8) (the GEMM, a call of its own so that its launch can be
+bracketed with events in the timed region for the roofline entry, one launch
+per step rotating over the linears); then every backward in reverse order,
+each one fp8_linear_bwd(G): G quantized once (with db's column partials),
+the dX GEMM on the main stream, and the dW GEMM with db on a second stream
+after the quantize, so that the weight gradients fill the CUs the dX chain
+leaves idle.  The step ends with the main stream waiting for the second.
 
 Beside the headline (warm: the same buffers every step) the line carries a
 cold-cache step (the same step with its inputs rotated over enough copies of
@@ -82,7 +84,7 @@ class Layer:
     scales (made once here) and quantizes only X in the forward.  inputs:
     CPU tensors (X, W, b, G) to copy instead of generating them."""
 
-    def __init__(self, F, WL, wl, li, dev, stream, inputs=None):
+    def __init__(self, F, WL, wl, li, dev, stream, side, inputs=None):
         import torch
 
         X, W, b, G = WL.layer_inputs(wl, li) if inputs is None else inputs
@@ -116,7 +118,14 @@ class Layer:
             F.fp8_quantize(self.W, F.FP8_E4M3, self.w8, None, self.sw, self.aw, stream=stream)
             F.fp8_quantize(self.b, F.FP8_E4M3, self.b8, None, self.sb, ab, stream=stream)
             bias = F.Quantized(self.b8, F.FP8_E4M3, self.sb)
-        # the calls of a training step (the forward as quantize pair + GEMM)
+        # the calls of a training step: the forward as quantize pair + GEMM,
+        # the backward as one fp8_linear_bwd (G quantized once; dX on stream,
+        # dW and db on side after the quantize)
+        self.bwd = F.bind_fp8_linear_bwd(self.G, F.FP8_E5M2, x8q, w8q, self.dx, self.dw, self.db,
+                                         self.ws, self.rg, self.g8, self.sg, self.ag,
+                                         stream=stream, stream_dw=side)
+        # the same backward as two one-stream calls (the dW call quantizes G),
+        # for a step that brackets the dX GEMM alone
         self.bwd_dw = F.bind_fp8_linear_bwd_dw(self.G, F.FP8_E5M2, x8q, self.dw, self.db, self.ws,
                                                self.rg, self.g8, self.sg, self.ag, stream=stream)
         self.bwd_dx = F.bind_fp8_linear_bwd_dx(g8q, F.FP8_E5M2, w8q, self.dx, stream=stream)
@@ -402,16 +411,28 @@ def cpu_baseline(layers_cpu, budget_s, min_s=10.0):
                       f"GEMMs + db, fp64 accumulation; {dt:.1f} s on {os.cpu_count()} host cpus"}
 
 
-def layer_step(layers):
-    """One training step over the linears: the forward's quantize launch and
-    GEMM, the weight gradient (G quantized there, with db), the input
-    gradient from G8."""
-    def step():
-        for L in layers:
+def layer_step(layers, stream, side):
+    """One training step over the linears in a training step's order: every
+    forward (the quantize launch, then the GEMM), then every backward in
+    reverse order, each one fp8_linear_bwd (G quantized once, with db's
+    column partials; the dX GEMM on stream; the dW GEMM and db on side after
+    the quantize, overlapping the dX chain).  The step ends with stream
+    waiting for side, so the next step's forward meets no dW GEMM and no
+    buffer is rewritten while a dW GEMM still reads it.
+
+    launch(kind, li, fn) issues call fn of kind "fwd" or "bwd" of linear li
+    (the timed region brackets one of them with events); by default it just
+    calls fn."""
+    def plain(kind, li, fn):
+        fn()
+
+    def step(launch=plain):
+        for li, L in enumerate(layers):
             L.quant_xw()
-            L.gemm_fwd()
-            L.bwd_dw()
-            L.bwd_dx()
+            launch("fwd", li, L.gemm_fwd)
+        for li in reversed(range(len(layers))):
+            launch("bwd", li, layers[li].bwd)
+        stream.wait_stream(side)
     return step
 
 
@@ -467,7 +488,7 @@ def workload_label(wl):
     return f"{wl.name}: {dims}; M={wl.M} tokens; {names} fwd+dW(+db)+dX; {mode}{pre}"
 
 
-def other_configs(torch, F, WL, dev, stream, skip, steps, reps):
+def other_configs(torch, F, WL, dev, stream, side, skip, steps, reps):
     """The step of every other full-size workload on its own: ms per step,
     TFLOP/s and % of the FP8 peak over its GEMMs, quantize GB/s as the step
     issues it, and the isolated GEMM totals per kind."""
@@ -476,8 +497,8 @@ def other_configs(torch, F, WL, dev, stream, skip, steps, reps):
         if name == skip:
             continue
         wl = WL.WORKLOADS[name]
-        layers = [Layer(F, WL, wl, li, dev, stream) for li in range(len(wl.linears))]
-        step = layer_step(layers)
+        layers = [Layer(F, WL, wl, li, dev, stream, side) for li in range(len(wl.linears))]
+        step = layer_step(layers, stream, side)
         for _ in range(2):  # the first step seeds the rings
             step()
         per, tot, q_us, q_gbps = isolated_timings(torch, layers, reps, stream)
@@ -503,15 +524,15 @@ def other_configs(torch, F, WL, dev, stream, skip, steps, reps):
     return res
 
 
-def cold_steps(torch, F, WL, wl, dev, stream, steps, min_bytes=1 << 30):
+def cold_steps(torch, F, WL, wl, dev, stream, side, steps, min_bytes=1 << 30):
     """ms per step with the step's inputs rotated over copies of the layer
     (at least 1 GiB of bf16 inputs in all, past the 256 MB MALL and the
     4 MB L2s), so that a step finds none of its inputs or weights in cache."""
     cpu = [WL.layer_inputs(wl, li) for li in range(len(wl.linears))]
     per_set = sum(t.numel() * t.element_size() for inp in cpu for t in inp)
     R = max(2, -(-min_bytes // per_set))
-    sets = [layer_step([Layer(F, WL, wl, li, dev, stream, inputs=cpu[li])
-                        for li in range(len(cpu))]) for _ in range(R)]
+    sets = [layer_step([Layer(F, WL, wl, li, dev, stream, side, inputs=cpu[li])
+                        for li in range(len(cpu))], stream, side) for _ in range(R)]
     for st in sets:  # seed every copy's rings
         st()
     calls = [0]
@@ -650,8 +671,9 @@ def main():
     F.lib()  # fails loudly if the HIP library is missing
     wl = WL.WORKLOADS[args.workload]
     stream = torch.cuda.Stream()
-    layers = [Layer(F, WL, wl, li, dev, stream) for li in range(len(wl.linears))]
-    step = layer_step(layers)
+    side = torch.cuda.Stream()  # the backward's dW GEMMs (default priority, like stream)
+    layers = [Layer(F, WL, wl, li, dev, stream, side) for li in range(len(wl.linears))]
+    step = layer_step(layers, stream, side)
 
     if args.sweep_tiles:
         step()  # seed the rings and fill the quantized operands
@@ -705,25 +727,36 @@ def main():
 
     # ---- timed region: exactly args.steps eager steps.  In step s the launch
     # of the GEMM kind that dominates the isolated timings (forward or dX:
-    # each a one-kernel call) of linear s mod 5 is bracketed with events on
-    # the stream it runs on, so over the steps every linear's launch is timed
+    # each a one-kernel call on stream) of linear s mod n is bracketed with
+    # events on stream, so over the steps every linear's launch is timed
     # live while each step carries one event pair (an event record costs a
-    # few microseconds of the stream's time).  The event pairs are created up
-    # front, outside the timed region.
+    # few microseconds of the stream's time).  A bracketed dX GEMM needs the
+    # backward as two calls on stream (fp8_linear_bwd_dw, then the dX alone);
+    # a bracketed forward GEMM runs while side is idle (the previous step
+    # ended with the join).  The event pairs are created up front, outside
+    # the timed region.
     dom = "fwd" if tot["fwd"] >= tot["dx"] else "dx"
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     ev_layer = []
 
-    def run(kind, fn, step_i, li):
-        if kind != dom or li != step_i % len(layers):
-            fn()
-            return
-        a, b_ = ev[step_i]
-        ev_layer.append(li)
-        a.record(stream)
-        fn()
-        b_.record(stream)
+    def bracketing(step_i):
+        def launch(kind, li, fn):
+            if li != step_i % len(layers) or kind != ("fwd" if dom == "fwd" else "bwd"):
+                fn()
+                return
+            a, b_ = ev[step_i]
+            ev_layer.append(li)
+            if dom == "fwd":
+                a.record(stream)
+                fn()
+                b_.record(stream)
+            else:
+                layers[li].bwd_dw()
+                a.record(stream)
+                layers[li].bwd_dx()
+                b_.record(stream)
+        return launch
 
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -732,11 +765,7 @@ def main():
     with torch.cuda.stream(stream):
         t_start.record(stream)
         for si in range(args.steps):
-            for li, L in enumerate(layers):
-                L.quant_xw()
-                run("fwd", L.gemm_fwd, si, li)
-                L.bwd_dw()
-                run("dx", L.bwd_dx, si, li)
+            step(bracketing(si))
         t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -836,8 +865,8 @@ def main():
     if not args.no_widened:
         out["widened"] = widened_rows(torch, F, WL, wl, layers, stream, args.kernel_reps)
     if not args.no_other_configs:
-        out["cold"] = cold_steps(torch, F, WL, wl, dev, stream, args.steps)
-        out["other_configs"] = other_configs(torch, F, WL, dev, stream, wl.name, args.steps,
+        out["cold"] = cold_steps(torch, F, WL, wl, dev, stream, side, args.steps)
+        out["other_configs"] = other_configs(torch, F, WL, dev, stream, side, wl.name, args.steps,
                                              args.kernel_reps)
     if not args.no_cpu_baseline:
         layers_cpu = [WL.layer_inputs(wl, li) for li in range(len(wl.linears))]

@@ -2,7 +2,8 @@
  * fp8linear.h -- C ABI of the MI355X (gfx950) FP8 linear-layer hot path.
  *
  * One library, libfp8linear.so, hand-written HIP for CDNA4.  Four entry
- * points do the work of one FP8 linear layer in training:
+ * points do the work of one FP8 linear layer in training (fp8_linear_bwd
+ * below runs the two backward ones from one quantized G on two streams):
  *
  *   fp8_quantize        per-tensor quantize with on-device amax and the
  *                       delayed-scaling ring finalize in the same launch
@@ -31,8 +32,10 @@
  * - Every pointer except the fp8_ring_t / fp8_operand_t structs themselves
  *   is a DEVICE pointer.  The caller allocates and owns every buffer; the
  *   library never allocates, frees or synchronizes, and enqueues all work on
- *   the given stream.  A NULL optional pointer means "absent" ([P2] entry on
- *   null defaults for optional pointer members).
+ *   the given stream (fp8_linear_bwd: on its two streams, ordered by one
+ *   HIP event per device that the library keeps).  A NULL optional pointer
+ *   means "absent" ([P2] entry on null defaults for optional pointer
+ *   members).
  * - Outputs must not alias inputs.  Scale outputs must not alias a ring's
  *   own scale slot (the snapshot rule of [P3]: the GEMM dequantizes with the
  *   scale the quantize used, not with the one the ring publishes next).
@@ -54,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FP8_ABI_VERSION 3
+#define FP8_ABI_VERSION 4
 #define FP8_RING_MAX_HIST 1024
 
 typedef enum {
@@ -102,7 +105,7 @@ typedef struct {
  * the scale snapshot).  Host struct owned by the caller.
  *   dev       device buffer of fp8_ring_bytes(hist_len) bytes, 256-byte
  *             aligned: a 128-byte header {float scale; u32 top_count;
- *             u32 top_amax; u32 idx; u32 hist_len; u32 seeded; ...}, 16
+ *             u32 top_amax; u32 idx; u32 hist_len; u32 seeded; ...}, 64
  *             election groups of 128 bytes {u32 count; ...; u32 amax; ...}
  *             used by the last-block election of each launch (all zero
  *             between launches), then float hist[hist_len].
@@ -284,6 +287,41 @@ size_t fp8_db_workspace_bytes(int64_t M, int64_t N);
 int fp8_linear_bwd_dw(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
                       fp8_ring_t* ring_g, fp8_operand_t x8, void* dw, void* db, float* db_ws,
                       uint8_t* g8_out, float* sg_used, float* amax_g, hipStream_t stream);
+
+/*
+ * Both gradients of one linear from one quantized G, the weight gradient on
+ * a second stream ([P3] entries on the backward's bf16 grad outputs and on
+ * the forward's scales reused there; [P4] entry on the bias column sum).
+ * The results are those of fp8_linear_bwd_dw(g, ...) followed by
+ * fp8_linear_bwd_dx(g8, ...), bit for bit; only the streams differ:
+ *
+ *   on stream:     the quantize of g (with db's column partials when db is
+ *                  wanted), then the dX GEMM;
+ *   on stream_dw:  after the quantize (an event recorded on stream and
+ *                  waited on by stream_dw), the dW GEMM and db.
+ *
+ * The dX chain of a backward (the critical path: dX feeds the layer below)
+ * then never waits for a dW GEMM, which fills the CUs the dX work leaves
+ * idle.  stream_dw == stream runs everything in order on stream.
+ *
+ *   g, ring_g, g8_out, sg_used, amax_g: as in fp8_linear_bwd_dw.
+ *   x8, dw, db, db_ws: as in fp8_linear_bwd_dw (dw, db written on stream_dw;
+ *            db_ws read there).
+ *   w8, dx:  as in fp8_linear_bwd_dx (dx written on stream).
+ *
+ * The caller orders later uses of dw and db, and the next reuse of db_ws,
+ * after stream_dw (for example with an event recorded on stream_dw), and
+ * under graph capture joins stream_dw back to the capturing stream before
+ * the capture ends.  The library keeps one event per device for the fork
+ * (created on first use, held until the process ends); record and wait run
+ * under one lock, so calls from several host threads stay correct.
+ * Errors as for the other entry points; FP8_ERR_HIP also covers a failed
+ * event record or wait.
+ */
+int fp8_linear_bwd(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
+                   fp8_ring_t* ring_g, fp8_operand_t x8, fp8_operand_t w8, void* dx, void* dw,
+                   void* db, float* db_ws, uint8_t* g8_out, float* sg_used, float* amax_g,
+                   hipStream_t stream, hipStream_t stream_dw);
 
 /* Storage of a GEMM operand, with its contraction index k ([P4] entry on 3D
  * operands and transposed views folding into the layout tag):

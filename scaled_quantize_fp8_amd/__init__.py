@@ -32,7 +32,7 @@ _FMT_DT = {FP8_E4M3: FP8_DT_E4M3, FP8_E5M2: FP8_DT_E5M2}
 C_SYMBOLS = (
     "fp8_abi_version", "fp8_status_str", "fp8_ring_bytes", "fp8_ring_init", "fp8_quantize",
     "fp8_quantize_pair", "fp8_linear_fwd", "fp8_linear_bwd_dx", "fp8_db_workspace_bytes",
-    "fp8_linear_bwd_dw", "fp8_gemm", "fp8_quantize_2d", "fp8_gemm_fp8out",
+    "fp8_linear_bwd_dw", "fp8_gemm", "fp8_quantize_2d", "fp8_gemm_fp8out", "fp8_linear_bwd",
 )
 
 
@@ -77,13 +77,15 @@ def lib() -> ctypes.CDLL:
                                      vp, vp]
         L.fp8_linear_bwd_dx.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp]
         L.fp8_linear_bwd_dw.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp, vp, vp]
+        L.fp8_linear_bwd.argtypes = [i64, i64, i64, op, i32, rp, op, op, vp, vp, vp, vp, vp, vp, vp,
+                                     vp, vp]
         L.fp8_quantize_2d.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, rp, vp, vp, vp]
         L.fp8_gemm.argtypes = [i64, i64, i64, i64, op, i32, i64, i64, op, i32, i64, i64, op, vp,
                                i64, i64, vp]
         L.fp8_gemm_fp8out.argtypes = [i64, i64, i64, op, op, op, i32, rp, vp, vp, vp, vp]
         for name in ("fp8_ring_init", "fp8_quantize", "fp8_quantize_pair", "fp8_quantize_2d",
                      "fp8_linear_fwd", "fp8_gemm", "fp8_linear_bwd_dx",
-                     "fp8_linear_bwd_dw", "fp8_gemm_fp8out"):
+                     "fp8_linear_bwd_dw", "fp8_gemm_fp8out", "fp8_linear_bwd"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -304,6 +306,33 @@ def bind_fp8_linear_bwd_dw(g, fmt_g, x8, dw, db=None, db_ws=None, ring_g=None, g
                            sg_used=None, amax_g=None, stream=None):
     return _bind("fp8_linear_bwd_dw", _dw_args(g, fmt_g, x8, dw, db, db_ws, ring_g, g8_out,
                                                sg_used, amax_g, stream))
+
+
+def _bwd_args(g, fmt_g, x8, w8, dx, dw, db, db_ws, ring_g, g8_out, sg_used, amax_g, stream,
+              stream_dw):
+    gd = g.codes if isinstance(g, Quantized) else g
+    M, N = gd.shape
+    K = x8.codes.shape[1]
+    st = _stream(stream)
+    st_dw = st if stream_dw is None else stream_dw.cuda_stream
+    return (ctypes.c_int64(M), ctypes.c_int64(N), ctypes.c_int64(K), _operand(g),
+            ctypes.c_int32(fmt_g), _ring(ring_g), _operand(x8), _operand(w8), _vp(dx), _vp(dw),
+            _vp(db), _vp(db_ws), _vp(g8_out), _vp(sg_used), _vp(amax_g), ctypes.c_void_p(st),
+            ctypes.c_void_p(st_dw))
+
+
+def fp8_linear_bwd(g, fmt_g, x8, w8, dx, dw, db=None, db_ws=None, ring_g=None, g8_out=None,
+                   sg_used=None, amax_g=None, stream=None, stream_dw=None):
+    """Both gradients from one quantize of g: dX on stream, dW (and db) on
+    stream_dw after the quantize (stream_dw None: the same stream)."""
+    _check(lib().fp8_linear_bwd(*_bwd_args(g, fmt_g, x8, w8, dx, dw, db, db_ws, ring_g, g8_out,
+                                           sg_used, amax_g, stream, stream_dw)), "fp8_linear_bwd")
+
+
+def bind_fp8_linear_bwd(g, fmt_g, x8, w8, dx, dw, db=None, db_ws=None, ring_g=None, g8_out=None,
+                        sg_used=None, amax_g=None, stream=None, stream_dw=None):
+    return _bind("fp8_linear_bwd", _bwd_args(g, fmt_g, x8, w8, dx, dw, db, db_ws, ring_g, g8_out,
+                                             sg_used, amax_g, stream, stream_dw))
 
 
 def _matrix_view(t, what):

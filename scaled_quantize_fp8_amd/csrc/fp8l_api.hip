@@ -1,5 +1,6 @@
 // C ABI of libfp8linear.so: argument validation, then launches on the
-// caller's stream.  No allocation, no synchronization.
+// caller's streams.  No device allocation, no host synchronization (the
+// two-stream backward creates one event per device on first use).
 //
 // The four entry points follow the two-primitive API of [P3] (quantize, and
 // a GEMM that consumes quantized operands and their scales) with the
@@ -11,6 +12,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "../../include/fp8linear.h"
 #include "fp8l_device.hpp"
@@ -632,22 +635,12 @@ static int bwd_prepare(int64_t M, int64_t N, fp8_operand_t g, int32_t fmt_g, fp8
   return FP8_OK;
 }
 
-int fp8_linear_bwd_dx(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
-                      fp8_ring_t* ring_g, fp8_operand_t w8, void* dx, uint8_t* g8_out,
-                      float* sg_used, float* amax_g, hipStream_t stream) {
-  if (M < 0 || N < 0 || K < 0) return FP8_ERR_SHAPE;
-  if (!mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return FP8_ERR_SHAPE;
-  const uint8_t* g8 = nullptr;
-  const float* sg = nullptr;
-  bool pre = false;
-  int st = bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, true, nullptr, stream, &g8,
-                       &sg, &pre);
-  if (st) return st;
-  if (!is_f8(w8.dtype)) return FP8_ERR_DTYPE;
-  if ((N * K > 0 && !w8.data) || !w8.scale) return FP8_ERR_NULL;
-  if (M * K > 0 && !dx) return FP8_ERR_NULL;
-  bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, nullptr, stream, &g8, &sg, &pre);
-
+// The dX GEMM of a backward: dX = G8 W8 / (sg sw).  pre: g was given
+// pre-quantized, so this launch's block 0 also snapshots its scale into
+// sg_used and clears amax_g.
+static void enqueue_dx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* g8, const float* sg,
+                            int32_t fmt_g, fp8_operand_t w8, void* dx, bool pre, const float* g_scale,
+                            float* sg_used, float* amax_g, hipStream_t stream) {
   GemmArgs a = {};
   a.a = g8;  // [M, N], contraction n contiguous
   a.lda = N;
@@ -662,43 +655,33 @@ int fp8_linear_bwd_dx(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t 
   a.scale_b = w8.scale;
   if (pre) {
     a.aux_scale_dst0 = sg_used;
-    a.aux_scale_src0 = g.scale;
+    a.aux_scale_src0 = g_scale;
     a.aux_amax_dst0 = amax_g;
   }
   finish_gemm_args(a);
   launch_gemm_l<kKContig, kCross>(a, fmt_g, dtype_fmt(w8.dtype), stream);
-  return hip_status();
 }
 
-int fp8_linear_bwd_dw(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
-                      fp8_ring_t* ring_g, fp8_operand_t x8, void* dw, void* db, float* db_ws,
-                      uint8_t* g8_out, float* sg_used, float* amax_g, hipStream_t stream) {
-  if (M < 0 || N < 0 || K < 0) return FP8_ERR_SHAPE;
-  if (!mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return FP8_ERR_SHAPE;
-  const uint8_t* g8 = nullptr;
-  const float* sg = nullptr;
-  bool pre = false;
-  int st = bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, true, nullptr, stream, &g8,
-                       &sg, &pre);
-  if (st) return st;
-  if (!is_f8(x8.dtype)) return FP8_ERR_DTYPE;
-  if ((M * K > 0 && !x8.data) || !x8.scale) return FP8_ERR_NULL;
-  if (N * K > 0 && !dw) return FP8_ERR_NULL;
-  if (db && M > 0 && !db_ws) return FP8_ERR_NULL;
+// The column partials of a pre-quantized g for db (dec(g8) / sg is summed
+// by the finalize); a high-precision g gets them from its quantize.
+static void enqueue_db_colsum_pre(int64_t M, int64_t N, const uint8_t* g8, int32_t fmt_g,
+                                  float* db_ws, hipStream_t stream) {
+  if (N <= 0) return;
+  dim3 grid((unsigned)((N + kColStrip - 1) / kColStrip),
+            (unsigned)((M + kColRowsPerChunk - 1) / kColRowsPerChunk));
+  if (fmt_g == FP8_E4M3)
+    hipLaunchKernelGGL(colsum_fp8_kernel<kE4M3>, grid, dim3(kQThreads), 0, stream, g8, M, N, db_ws);
+  else
+    hipLaunchKernelGGL(colsum_fp8_kernel<kE5M2>, grid, dim3(kQThreads), 0, stream, g8, M, N, db_ws);
+}
 
-  ColsumSpec cs = {M, N, db_ws};
-  const bool want_db = db != nullptr && M > 0;
-  bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, want_db ? &cs : nullptr,
-              stream, &g8, &sg, &pre);
-  if (want_db && pre && N > 0) {
-    dim3 grid((unsigned)((N + kColStrip - 1) / kColStrip),
-              (unsigned)((M + kColRowsPerChunk - 1) / kColRowsPerChunk));
-    if (fmt_g == FP8_E4M3)
-      hipLaunchKernelGGL(colsum_fp8_kernel<kE4M3>, grid, dim3(kQThreads), 0, stream, g8, M, N, db_ws);
-    else
-      hipLaunchKernelGGL(colsum_fp8_kernel<kE5M2>, grid, dim3(kQThreads), 0, stream, g8, M, N, db_ws);
-  }
-
+// The dW GEMM of a backward: dW = G8^T X8 / (sg sx), and db from the column
+// partials in db_ws.  aux: snapshot a pre-quantized g's scale (see
+// enqueue_dx_gemm).
+static void enqueue_dw_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* g8, const float* sg,
+                            int32_t fmt_g, fp8_operand_t x8, void* dw, void* db, float* db_ws,
+                            bool pre, bool aux, const float* g_scale, float* sg_used,
+                            float* amax_g, hipStream_t stream) {
   GemmArgs a = {};
   a.a = g8;  // G8 [M, N] as A(i = n, k = m): crosswise
   a.lda = N;
@@ -717,13 +700,117 @@ int fp8_linear_bwd_dw(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t 
     a.db_R = (int32_t)((M + kColRowsPerChunk - 1) / kColRowsPerChunk);
     a.db_scale = pre ? sg : nullptr;
   }
-  if (pre) {
+  if (pre && aux) {
     a.aux_scale_dst0 = sg_used;
-    a.aux_scale_src0 = g.scale;
+    a.aux_scale_src0 = g_scale;
     a.aux_amax_dst0 = amax_g;
   }
   finish_gemm_args(a);
   launch_gemm_l<kCross, kCross>(a, fmt_g, dtype_fmt(x8.dtype), stream);
+}
+
+static int check_dx_operands(int64_t M, int64_t N, int64_t K, fp8_operand_t w8, const void* dx) {
+  if (!is_f8(w8.dtype)) return FP8_ERR_DTYPE;
+  if ((N * K > 0 && !w8.data) || !w8.scale) return FP8_ERR_NULL;
+  if (M * K > 0 && !dx) return FP8_ERR_NULL;
+  return FP8_OK;
+}
+
+static int check_dw_operands(int64_t M, int64_t N, int64_t K, fp8_operand_t x8, const void* dw,
+                             const void* db, const float* db_ws) {
+  if (!is_f8(x8.dtype)) return FP8_ERR_DTYPE;
+  if ((M * K > 0 && !x8.data) || !x8.scale) return FP8_ERR_NULL;
+  if (N * K > 0 && !dw) return FP8_ERR_NULL;
+  if (db && M > 0 && !db_ws) return FP8_ERR_NULL;
+  return FP8_OK;
+}
+
+// One event per device for the fork of fp8_linear_bwd, created on first
+// use.  Record and wait happen under one lock, so a wait always refers to
+// the record made just before it by the same call.
+static std::mutex g_fork_mu;
+static hipEvent_t g_fork_ev[64];
+
+static int fork_after(hipStream_t from, hipStream_t to) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FP8_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_fork_mu);
+  if (!g_fork_ev[dev] && hipEventCreateWithFlags(&g_fork_ev[dev], hipEventDisableTiming) != hipSuccess) {
+    g_fork_ev[dev] = nullptr;
+    return FP8_ERR_HIP;
+  }
+  if (hipEventRecord(g_fork_ev[dev], from) != hipSuccess) return FP8_ERR_HIP;
+  if (hipStreamWaitEvent(to, g_fork_ev[dev], 0) != hipSuccess) return FP8_ERR_HIP;
+  return FP8_OK;
+}
+
+int fp8_linear_bwd_dx(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
+                      fp8_ring_t* ring_g, fp8_operand_t w8, void* dx, uint8_t* g8_out,
+                      float* sg_used, float* amax_g, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return FP8_ERR_SHAPE;
+  if (!mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return FP8_ERR_SHAPE;
+  const uint8_t* g8 = nullptr;
+  const float* sg = nullptr;
+  bool pre = false;
+  int st = bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, true, nullptr, stream, &g8,
+                       &sg, &pre);
+  if (st) return st;
+  if ((st = check_dx_operands(M, N, K, w8, dx))) return st;
+  bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, nullptr, stream, &g8, &sg, &pre);
+  enqueue_dx_gemm(M, N, K, g8, sg, fmt_g, w8, dx, pre, g.scale, sg_used, amax_g, stream);
+  return hip_status();
+}
+
+int fp8_linear_bwd_dw(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
+                      fp8_ring_t* ring_g, fp8_operand_t x8, void* dw, void* db, float* db_ws,
+                      uint8_t* g8_out, float* sg_used, float* amax_g, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return FP8_ERR_SHAPE;
+  if (!mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return FP8_ERR_SHAPE;
+  const uint8_t* g8 = nullptr;
+  const float* sg = nullptr;
+  bool pre = false;
+  int st = bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, true, nullptr, stream, &g8,
+                       &sg, &pre);
+  if (st) return st;
+  if ((st = check_dw_operands(M, N, K, x8, dw, db, db_ws))) return st;
+
+  ColsumSpec cs = {M, N, db_ws};
+  const bool want_db = db != nullptr && M > 0;
+  bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, want_db ? &cs : nullptr,
+              stream, &g8, &sg, &pre);
+  if (want_db && pre) enqueue_db_colsum_pre(M, N, g8, fmt_g, db_ws, stream);
+  enqueue_dw_gemm(M, N, K, g8, sg, fmt_g, x8, dw, db, db_ws, pre, true, g.scale, sg_used, amax_g,
+                  stream);
+  return hip_status();
+}
+
+int fp8_linear_bwd(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
+                   fp8_ring_t* ring_g, fp8_operand_t x8, fp8_operand_t w8, void* dx, void* dw,
+                   void* db, float* db_ws, uint8_t* g8_out, float* sg_used, float* amax_g,
+                   hipStream_t stream, hipStream_t stream_dw) {
+  if (M < 0 || N < 0 || K < 0) return FP8_ERR_SHAPE;
+  if (!mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return FP8_ERR_SHAPE;
+  const uint8_t* g8 = nullptr;
+  const float* sg = nullptr;
+  bool pre = false;
+  int st = bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, true, nullptr, stream, &g8,
+                       &sg, &pre);
+  if (st) return st;
+  if ((st = check_dx_operands(M, N, K, w8, dx))) return st;
+  if ((st = check_dw_operands(M, N, K, x8, dw, db, db_ws))) return st;
+
+  ColsumSpec cs = {M, N, db_ws};
+  const bool want_db = db != nullptr && M > 0;
+  bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, want_db ? &cs : nullptr,
+              stream, &g8, &sg, &pre);
+  if (want_db && pre) enqueue_db_colsum_pre(M, N, g8, fmt_g, db_ws, stream);
+  if ((st = hip_status())) return st;
+  if (stream_dw != stream && (st = fork_after(stream, stream_dw))) return st;
+  // the dX GEMM snapshots a pre-quantized g's scale; the dW GEMM reads
+  // g's own scale, so the two streams touch no common output
+  enqueue_dw_gemm(M, N, K, g8, sg, fmt_g, x8, dw, db, db_ws, pre, false, g.scale, sg_used, amax_g,
+                  stream_dw);
+  enqueue_dx_gemm(M, N, K, g8, sg, fmt_g, w8, dx, pre, g.scale, sg_used, amax_g, stream);
   return hip_status();
 }
 

@@ -227,8 +227,14 @@ FP8L_DEV void db_finalize(const GemmArgs& g) {
   }
 }
 
+// Tile of linear index pid: pids walk down groups of G tile rows, column by
+// column, so that a run of consecutive pids (one XCD's share, see
+// tile_coords_xcd) covers a block G rows tall.  G = 4 gives the 2048 x 1536
+// outputs of the 128x128 kernels 4 x 6 blocks per XCD, 10 operand panels
+// where G = 8 gives 8 x 3, 11 panels; measured, it is 0.5-1% faster over the
+// layer's GEMMs.
 FP8L_DEV void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int G = 8;
+  constexpr int G = 4;
   const int per_group = G * tiles_n;
   const int group = pid / per_group;
   const int first = group * G;

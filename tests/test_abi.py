@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8_abi_version() == 3
+    assert F.fp8_abi_version() == 4
     for st in range(6):
         assert F.status_str(st)
     assert F.status_str(99) == "unknown status"
@@ -130,6 +130,37 @@ def test_linear_validation(lib):
     dw = lib.fp8_linear_bwd_dw
     assert dw(8, 8, 8, hp, F.FP8_E5M2, None, f8, P, P, None, P, P, P, None) == F.FP8_ERR_NULL
     assert dw(8, 8, 8, hp, 9, None, f8, P, None, None, P, P, P, None) == F.FP8_ERR_DTYPE
+
+
+def test_two_stream_backward_validation(lib):
+    """fp8_linear_bwd checks the union of the dX and dW arguments before it
+    enqueues anything (or records its fork event)."""
+    hp = F._Operand(P, F.FP8_DT_BF16, None)
+    f8 = F._Operand(P, F.FP8_DT_E4M3, P)
+    g8 = F._Operand(P, F.FP8_DT_E5M2, P)
+    S2 = ctypes.c_void_p(0x300000)
+    bwd = lib.fp8_linear_bwd
+
+    def call(M=8, N=8, K=8, g=hp, fmt=F.FP8_E5M2, x8=f8, w8=f8, dx=P, dw=P, db=None, ws=None,
+             g8_out=P, su=P, am=P):
+        return bwd(M, N, K, g, fmt, None, x8, w8, dx, dw, db, ws, g8_out, su, am, None, S2)
+
+    assert call(M=-1) == F.FP8_ERR_SHAPE
+    assert call(M=2**40, N=2**40) == F.FP8_ERR_SHAPE
+    assert call(fmt=7) == F.FP8_ERR_DTYPE
+    assert call(g=F._Operand(P, F.FP8_DT_E4M3, P)) == F.FP8_ERR_DTYPE  # fp8 g of the other format
+    assert call(g=F._Operand(P, F.FP8_DT_E5M2, None)) == F.FP8_ERR_NULL  # pre-quantized, no scale
+    assert call(g8_out=None) == F.FP8_ERR_NULL                         # hp g needs g8_out
+    assert call(su=None) == F.FP8_ERR_NULL
+    assert call(am=None) == F.FP8_ERR_NULL                             # dynamic: amax required
+    assert call(w8=hp) == F.FP8_ERR_DTYPE                              # dX operand
+    assert call(w8=F._Operand(P, F.FP8_DT_E4M3, None)) == F.FP8_ERR_NULL
+    assert call(dx=None) == F.FP8_ERR_NULL
+    assert call(x8=hp) == F.FP8_ERR_DTYPE                              # dW operand
+    assert call(x8=F._Operand(None, F.FP8_DT_E4M3, P)) == F.FP8_ERR_NULL
+    assert call(dw=None) == F.FP8_ERR_NULL
+    assert call(db=P, ws=None) == F.FP8_ERR_NULL                       # db needs its workspace
+    assert call(g=g8, g8_out=None, su=None, am=None, dx=None) == F.FP8_ERR_NULL
 
 
 def test_ring_init_validation(lib):

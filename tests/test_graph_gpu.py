@@ -9,7 +9,9 @@ program does its own eager work (it rescales X in both copies, so that the
 rings see a changing amax) and synchronizes; every replay must give the
 eager step's bytes exactly: codes, scales, amax, ring state and the bf16
 outputs (the GEMMs are deterministic).  The calls record no memset nodes:
-the library issues only kernels.
+the library issues only kernels.  In the two-stream variant the backward is
+fp8_linear_bwd with the dW GEMM on a second stream, which the capture takes
+as a fork after the G quantize and a join at the end of the step.
 """
 
 import numpy as np
@@ -27,7 +29,7 @@ FX, FG = F.FP8_E4M3, F.FP8_E5M2
 class Linear:
     """Buffers, rings and the bound calls of one linear's step on a stream."""
 
-    def __init__(self, X, W, b, G, stream, hist_len=4):
+    def __init__(self, X, W, b, G, stream, hist_len=4, side=None):
         M, K = X.shape
         N = W.shape[0]
         e = lambda *s, dt=torch.uint8: torch.empty(*s, dtype=dt, device=DEV)
@@ -47,10 +49,21 @@ class Linear:
             F.bind_fp8_quantize_pair(self.X, self.x8, self.rx, self.sx, self.ax, self.W, self.w8,
                                      self.rw, self.sw, self.aw, FX, stream=stream),
             F.bind_fp8_linear_fwd(x8q, w8q, self.b, FX, self.y, stream=stream),
-            F.bind_fp8_linear_bwd_dw(self.G, FG, x8q, self.dw, self.db, self.ws, self.rg, self.g8,
-                                     self.sg, self.ag, stream=stream),
-            F.bind_fp8_linear_bwd_dx(g8q, FG, w8q, self.dx, stream=stream),
         ]
+        if side is None:
+            self.calls += [
+                F.bind_fp8_linear_bwd_dw(self.G, FG, x8q, self.dw, self.db, self.ws, self.rg,
+                                         self.g8, self.sg, self.ag, stream=stream),
+                F.bind_fp8_linear_bwd_dx(g8q, FG, w8q, self.dx, stream=stream),
+            ]
+        else:
+            # the two-stream backward: dW on side, joined back at the end
+            self.calls += [
+                F.bind_fp8_linear_bwd(self.G, FG, x8q, w8q, self.dx, self.dw, self.db, self.ws,
+                                      self.rg, self.g8, self.sg, self.ag, stream=stream,
+                                      stream_dw=side),
+                lambda: stream.wait_stream(side),
+            ]
 
     def step(self):
         for c in self.calls:
@@ -73,13 +86,17 @@ def _inputs(M, K, N, seed):
             bf(rng.standard_normal(N) * 0.01), bf(rng.standard_normal((M, N)) * 1e-3))
 
 
-# (384, 320, 640): 128x128 tiles; (2048, 256, 4096): the 256x256 8-wave kernel
+# (384, 320, 640): 128x128 tiles; (2048, 256, 4096): the 256x256 8-wave kernel.
+# two_stream: the backward through fp8_linear_bwd with dW on a second stream
+# (captured as a fork and a join of the graph).
+@pytest.mark.parametrize("two_stream", [False, True])
 @pytest.mark.parametrize("M,K,N", [(384, 320, 640), (2048, 256, 4096)])
-def test_graph_replays_match_eager(M, K, N):
+def test_graph_replays_match_eager(M, K, N, two_stream):
     stream = torch.cuda.Stream()
+    side = torch.cuda.Stream() if two_stream else None
     X0, W, b, G = _inputs(M, K, N, seed=M + N)
-    eager = Linear(X0, W, b, G, stream)
-    graphed = Linear(X0, W, b, G, stream)
+    eager = Linear(X0, W, b, G, stream, side=side)
+    graphed = Linear(X0, W, b, G, stream, side=side)
     with torch.cuda.stream(stream):
         eager.step()  # seeding step: the first call through each ring
         graphed.step()
