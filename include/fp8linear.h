@@ -309,10 +309,13 @@ int fp8_linear_bwd_dw(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t 
  *            db_ws read there).
  *   w8, dx:  as in fp8_linear_bwd_dx (dx written on stream).
  *
- * The caller orders later uses of dw and db, and the next reuse of db_ws,
- * after stream_dw (for example with an event recorded on stream_dw), and
- * under graph capture joins stream_dw back to the capturing stream before
- * the capture ends.  The library keeps one event per device for the fork
+ * The dW GEMM, running on stream_dw, reads g8_out (or a pre-quantized g),
+ * sg_used, x8 with its scale and db_ws whenever stream_dw reaches it.  The
+ * caller orders later uses of dw and db, and any rewrite of those inputs
+ * (say g8_out or db_ws reused by the next layer's backward on stream),
+ * after stream_dw, for example with an event recorded on stream_dw; under
+ * graph capture it joins stream_dw back to the capturing stream before the
+ * capture ends.  The library keeps one event per device for the fork
  * (created on first use, held until the process ends); record and wait run
  * under one lock, so calls from several host threads stay correct.
  * Errors as for the other entry points; FP8_ERR_HIP also covers a failed
