@@ -116,3 +116,36 @@ def test_traffic_record_quant_and_missing_kernel(tmp_path):
     # a CSV without the kernel is an error, not a zero
     with pytest.raises(SystemExit):
         bench.traffic_record("dx", fetch, write, cf, cw, "dim1536_m2048")
+
+
+def test_layer_step_order_forwards_then_backwards_then_join():
+    """The step issues every forward (quantize launch, then GEMM) in order,
+    then every backward in reverse order, then makes the main stream wait for
+    the dW stream; the launch hook sees each GEMM call with its kind."""
+    log = []
+
+    class FakeLayer:
+        def __init__(self, i):
+            self.quant_xw = lambda: log.append(("q", i))
+            self.gemm_fwd = lambda: log.append(("fwd", i))
+            self.bwd = lambda: log.append(("bwd", i))
+
+    class FakeStream:
+        def wait_stream(self, other):
+            log.append(("join", other))
+
+    main, side = FakeStream(), "side"
+    layers = [FakeLayer(i) for i in range(3)]
+    step = bench.layer_step(layers, main, side)
+    step()
+    assert log == [("q", 0), ("fwd", 0), ("q", 1), ("fwd", 1), ("q", 2), ("fwd", 2),
+                   ("bwd", 2), ("bwd", 1), ("bwd", 0), ("join", "side")]
+    log.clear()
+    seen = []
+
+    def hook(kind, li, fn):
+        seen.append((kind, li))
+        fn()
+    step(hook)
+    assert seen == [("fwd", 0), ("fwd", 1), ("fwd", 2), ("bwd", 2), ("bwd", 1), ("bwd", 0)]
+    assert log[-1] == ("join", "side")
