@@ -1,7 +1,8 @@
 """Host logic of the benchmark, on the CPU: which kernel a profiled
-dispatch counts for, the algorithmic bytes of the quantize launches, and
-the HBM bytes per launch from rocprofv3 counter CSVs scaled by the copy
-calibration.  No GPU and no kernel call."""
+dispatch counts for, the algorithmic bytes of the quantize launches, the
+HBM bytes per launch from rocprofv3 counter CSVs scaled by the copy
+calibration, and the order in which a step issues its calls.  No GPU and
+no kernel call."""
 
 import csv
 
