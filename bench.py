@@ -849,6 +849,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": workload_label(wl), "global_batch": wl.M,
                    "gemms_per_step": 3 * len(layers)},
+        "step_schedule": "every forward in order, then every backward in reverse order as "
+                         "fp8_linear_bwd (dX on the main stream, dW and db on a second stream "
+                         "after the G quantize); one join of the two streams per step",
         "pct_fp8_peak": round(100 * tflops / MI355X_FP8_DENSE_TFLOPS, 2),
         "quantize_GBps": round(quant_gbps, 1),
         "quantize_pct_hbm": round(100 * quant_gbps / MI355X_HBM_GBPS, 2),
