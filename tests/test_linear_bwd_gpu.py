@@ -130,6 +130,31 @@ def test_two_stream_matches_pair(M, N, K, mode):
         _assert_same(a.snapshot(), b.snapshot(), f"step {step}")
 
 
+# empty problems: no G rows (dW and db are zeros), no G columns (dX is
+# zeros), no features (only db has elements)
+@pytest.mark.parametrize("M,N,K", [(0, 64, 32), (48, 0, 32), (48, 64, 0)])
+@pytest.mark.parametrize("mode", ["ring", "prequantized"])
+def test_two_stream_degenerate_sizes(M, N, K, mode):
+    G, x8, w8, rng = _inputs(M, N, K, seed=17 + M + N + K)
+    g_pre = None
+    if mode == "prequantized":
+        g_pre = (np.full((M, N), 0x3C, np.uint8), 2.0)  # e5m2 1.0
+    side = torch.cuda.Stream()
+    a = Bwd(G, x8, 1.0, w8, 1.0, F.ScaleRing(4) if mode == "ring" else None, g_pre)
+    b = Bwd(G, x8, 1.0, w8, 1.0, F.ScaleRing(4) if mode == "ring" else None, g_pre)
+    for step in range(2):
+        a.run_pair()
+        b.run_two_stream(side)
+        _assert_same(a.snapshot(), b.snapshot(), f"step {step}")
+    if M == 0 or K == 0:
+        assert not torch.any(b.dw.float() != 0) and not torch.any(b.dx.float() != 0)
+    if M == 0:
+        assert not torch.any(b.db.float() != 0)
+    if mode == "prequantized" and N > 0 and K == 0:
+        # db = sum over rows of dec(g8) / sg = M * 1.0 / 2.0
+        assert torch.all(b.db.float() == M / 2.0)
+
+
 def test_same_stream_and_no_db():
     M, N, K = 384, 512, 256
     G, x8, w8, _ = _inputs(M, N, K, seed=5)
