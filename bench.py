@@ -553,7 +553,9 @@ def widened_rows(torch, F, WL, wl, layers, stream, reps):
     """Isolated timings of the entry points beyond the layer step (not part of
     the step or its value): the transposed and dual quantize, the weight
     gradient run k-contiguous from transposed operands next to the crosswise
-    one, a batched fp8_gemm, and the FP8-output forward next to the bf16 one."""
+    one, a batched fp8_gemm, the FP8-output forward next to the bf16 one, and
+    the flat quantize of a 2^28-element tensor (its streaming rate once the
+    fixed costs of a launch no longer count)."""
     dev = "cuda:0"
     up = next(L for L in layers if L.name == "up")
     M, N, K = up.M, up.N, up.K
@@ -612,6 +614,26 @@ def widened_rows(torch, F, WL, wl, layers, stream, reps):
     res["gemm_fp8out_up_fwd_us"] = round(us_q, 2)
     res["gemm_fp8out_up_fwd_TFLOPs"] = round(flops / (us_q * 1e-6) / 1e12, 1)
     res["gemm_bf16out_up_fwd_us"] = round(us_b, 2)
+    # the flat quantize where its fixed costs vanish: 2^28 seeded-normal bf16
+    # elements (512 MiB in, 256 MiB of codes out) through a seeded ring
+    n = 1 << 28
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(28)
+    big = torch.randn(n, device=dev, generator=gen).to(torch.bfloat16)
+    qbig = torch.empty(n, dtype=torch.uint8, device=dev)
+    rbig = F.ScaleRing(wl.hist_len, stream=stream)
+    s3, a3 = (torch.zeros(1, dtype=torch.float32, device=dev) for _ in range(2))
+    qf = F.bind_fp8_quantize(big, F.FP8_E4M3, qbig, rbig, s3, a3, stream=stream)
+    qf()  # seeds the ring
+    us = 1e3 * event_time_ms(torch, qf, reps, stream)
+    res["quantize_flat_2p28_bf16_us"] = round(us, 2)
+    res["quantize_flat_2p28_bf16_GBps"] = round(3.0 * n / (us * 1e-6) / 1e9, 1)
+    # beside it, torch's device copy of the same tensor (read + write 2 B per
+    # element): the streaming rate a plain copy reaches at this size
+    cbig = torch.empty_like(big)
+    us = 1e3 * event_time_ms(torch, lambda: cbig.copy_(big), reps, stream)
+    res["copy_2p28_bf16_GBps"] = round(4.0 * n / (us * 1e-6) / 1e9, 1)
+    del big, qbig, cbig
     res["e2e_train_step"] = e2e_train_step(torch, dev)
     return res
 
