@@ -18,10 +18,11 @@ the dX GEMM on the main stream, and the dW GEMM with db on a second stream
 after the quantize, so that the weight gradients fill the CUs the dX chain
 leaves idle.  The step ends with the main stream waiting for the second.
 
-Beside the headline (warm: the same buffers every step) the line carries a
-cold-cache step (the same step with its inputs rotated over enough copies of
-the layer, >= 1 GiB of bf16 inputs, that none is found in L2 or the MALL) and
-the step of every other full-size workload: the dim1024 layer at M = 2048,
+The timed steps walk enough copies of the layer (>= 1 GiB of bf16 inputs,
+each copy with its own buffers and rings) that no step finds its inputs in
+L2 or the MALL: the headline is this cold step.  Beside it the line carries
+the warm step (one copy every step), the same step replayed from a HIP graph
+(one copy), and the step of every other full-size workload: the dim1024 layer at M = 2048,
 the dim1536 layer at M = 512, the generic 4096 <-> 11008 pair at M = 4096
 with dynamic scaling, and the dim1536 layer with W and bias pre-quantized.
 
@@ -55,7 +56,7 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=20, help="repeats of each isolated kernel timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-other-configs", action="store_true",
-                   help="skip the cold-cache step and the other workloads' steps")
+                   help="skip the other workloads' steps")
     p.add_argument("--no-widened", action="store_true",
                    help="skip the isolated timings of the entry points beyond the layer step "
                         "(for a profile of the step alone)")
@@ -524,31 +525,6 @@ def other_configs(torch, F, WL, dev, stream, side, skip, steps, reps):
     return res
 
 
-def cold_steps(torch, F, WL, wl, dev, stream, side, steps, min_bytes=1 << 30):
-    """ms per step with the step's inputs rotated over copies of the layer
-    (at least 1 GiB of bf16 inputs in all, past the 256 MB MALL and the
-    4 MB L2s), so that a step finds none of its inputs or weights in cache."""
-    cpu = [WL.layer_inputs(wl, li) for li in range(len(wl.linears))]
-    per_set = sum(t.numel() * t.element_size() for inp in cpu for t in inp)
-    R = max(2, -(-min_bytes // per_set))
-    sets = [layer_step([Layer(F, WL, wl, li, dev, stream, side, inputs=cpu[li])
-                        for li in range(len(cpu))], stream, side) for _ in range(R)]
-    for st in sets:  # seed every copy's rings
-        st()
-    calls = [0]
-
-    def step():
-        sets[calls[0] % R]()
-        calls[0] += 1
-    ms = timed_steps_ms(torch, step, steps, stream)
-    flops = sum(3 * 2.0 * wl.M * L.N * L.K for L in wl.linears)
-    del sets
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    return {"ms_per_step": round(ms, 4), "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
-            "rotated_copies": R, "rotated_input_MB": round(R * per_set / 1e6, 1)}
-
-
 def widened_rows(torch, F, WL, wl, layers, stream, reps):
     """Isolated timings of the entry points beyond the layer step (not part of
     the step or its value): the transposed and dual quantize, the weight
@@ -743,11 +719,28 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # ---- the rotation the timed region walks: R copies of the layer (set 0 is
+    # `layers`, the others made from the same host inputs, each with its own
+    # buffers and rings), >= 1 GiB of bf16 inputs in all, past the 256 MB MALL
+    # and the 4 MB L2s, so that a timed step finds none of its inputs in a
+    # cache (the headline is this cold step; the warm one is reported beside)
+    cpu_in = [WL.layer_inputs(wl, li) for li in range(len(wl.linears))]
+    per_set = sum(t.numel() * t.element_size() for inp in cpu_in for t in inp)
+    R = max(2, -(-(1 << 30) // per_set))
+    sets = [layers] + [[Layer(F, WL, wl, li, dev, stream, side, inputs=cpu_in[li])
+                        for li in range(len(cpu_in))] for _ in range(R - 1)]
+    steps_of = [step] + [layer_step(ls, stream, side) for ls in sets[1:]]
+    for st_ in steps_of[1:]:
+        for _ in range(max(1, args.warmup)):
+            st_()
+    torch.cuda.synchronize()
+
     # ---- isolated per-kernel timings (events behind a GPU sleep), before the
     # timed region: they decide which GEMM kind the live events follow
     per, tot, q_us, quant_gbps = isolated_timings(torch, layers, args.kernel_reps, stream)
 
-    # ---- timed region: exactly args.steps eager steps.  In step s the launch
+    # ---- timed region: exactly args.steps eager steps, step s on copy s mod R
+    # of the layer.  In step s the launch
     # of the GEMM kind that dominates the isolated timings (forward or dX:
     # each a one-kernel call on stream) of linear s mod n is bracketed with
     # events on stream, so over the steps every linear's launch is timed
@@ -763,8 +756,10 @@ def main():
     ev_layer = []
 
     def bracketing(step_i):
+        ls = sets[step_i % R]
+
         def launch(kind, li, fn):
-            if li != step_i % len(layers) or kind != ("fwd" if dom == "fwd" else "bwd"):
+            if li != step_i % len(ls) or kind != ("fwd" if dom == "fwd" else "bwd"):
                 fn()
                 return
             a, b_ = ev[step_i]
@@ -774,9 +769,9 @@ def main():
                 fn()
                 b_.record(stream)
             else:
-                layers[li].bwd_dw()
+                ls[li].bwd_dw()
                 a.record(stream)
-                layers[li].bwd_dx()
+                ls[li].bwd_dx()
                 b_.record(stream)
         return launch
 
@@ -787,7 +782,7 @@ def main():
     with torch.cuda.stream(stream):
         t_start.record(stream)
         for si in range(args.steps):
-            step(bracketing(si))
+            steps_of[si % R](bracketing(si))
         t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -827,6 +822,14 @@ def main():
         graph_ms_per_step = gs.elapsed_time(ge) / args.steps
     except Exception as exc:  # graph capture is an extra measurement only
         print(f"graph capture skipped: {exc}", file=sys.stderr)
+
+    # ---- the warm step beside it: copy 0 of the layer every step, so its
+    # inputs stay in the MALL from one step to the next
+    warm_ms = timed_steps_ms(torch, step, args.steps, stream)
+    rotation = {"copies": R, "input_MB": round(R * per_set / 1e6, 1)}
+    del steps_of, sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
     # the roofline entry: the dominant GEMM kind of the forward and dX (the
     # two issued as one-kernel calls), timed live; all three isolated totals
@@ -879,6 +882,9 @@ def main():
         "quantize_pct_hbm": round(100 * quant_gbps / MI355X_HBM_GBPS, 2),
         "quantize_traffic": load_quant_traffic(args.workload),
         "wall_s_timed": round(wall, 4),
+        "cold_rotation": rotation,
+        "warm": {"ms_per_step": round(warm_ms, 4),
+                 "TFLOPs": round(step_flops / (warm_ms * 1e-3) / 1e12, 2)},
         "graph_ms_per_step": None if graph_ms_per_step is None else round(graph_ms_per_step, 4),
         "graph_TFLOPs": None if graph_ms_per_step is None else
         round(step_flops / (graph_ms_per_step * 1e-3) / 1e12, 2),
@@ -890,7 +896,6 @@ def main():
     if not args.no_widened:
         out["widened"] = widened_rows(torch, F, WL, wl, layers, stream, args.kernel_reps)
     if not args.no_other_configs:
-        out["cold"] = cold_steps(torch, F, WL, wl, dev, stream, side, args.steps)
         out["other_configs"] = other_configs(torch, F, WL, dev, stream, side, wl.name, args.steps,
                                              args.kernel_reps)
     if not args.no_cpu_baseline:
