@@ -176,6 +176,9 @@ def bf16_ulp(r) -> np.ndarray:
     """Spacing of bf16 numbers at magnitude |r| (2^-133 at and near zero)."""
     a = np.abs(np.asarray(r, dtype=np.float64))
     _, e = np.frexp(a)
+    # frexp gives exponent 0 for zero; zero lies in the subnormal range,
+    # whose spacing is the smallest subnormal 2^-133
+    e = np.where(a == 0.0, -125, e)
     return np.ldexp(1.0, np.maximum(e - 8, -133))
 
 

@@ -189,14 +189,123 @@ def test_bias_grad_closed_form_and_brute_force():
     assert np.array_equal(deq, O.decode_array(g8, O.E5M2) / 4096.0)
 
 
-def test_tolerance_contract_shape():
+# ---------------------------------------------------------------- bf16 spacing
+# bfloat16 as a format (sign, 8 exponent bits with bias 127, 7 fraction
+# bits; the fp32 exponent range): the value of every positive finite bit
+# pattern written out from its fields with exact rationals, independent of
+# the frexp/ldexp arithmetic of O.bf16_ulp.
+
+def _bf16_field_value(p: int) -> Fraction:
+    e, t = (p >> 7) & 0xFF, p & 0x7F
+    if e == 0:
+        return Fraction(t, 128) * Fraction(1, 2 ** 126)
+    return (1 + Fraction(t, 128)) * Fraction(2) ** (e - 127)
+
+
+_BF16_POS = None
+
+
+def _bf16_table():
+    """float64 values of the positive finite patterns 0x0000 .. 0x7F7F (each
+    exact in float64), ascending."""
+    global _BF16_POS
+    if _BF16_POS is None:
+        _BF16_POS = np.array([float(_bf16_field_value(p)) for p in range(0x7F80)], np.float64)
+    return _BF16_POS
+
+
+def _ulp_exact(r):
+    """Spacing of bf16 at |r|: v(p+1) - v(p) for the pattern p with
+    v(p) <= |r| < v(p+1); in the top binade (|r| >= v(0x7F7F)) the spacing
+    of that binade."""
+    tab = _bf16_table()
+    a = np.abs(np.asarray(r, np.float64))
+    p = np.searchsorted(tab, a, side="right") - 1
+    p = np.clip(p, 0, len(tab) - 2)
+    return tab[p + 1] - tab[p]
+
+
+def test_bf16_ulp_matches_format_spacing():
+    tab = _bf16_table()
+    # every pattern's own value, the midpoint of its interval, the largest
+    # float64 below the next pattern, and their negatives
+    lo = tab[:-1]
+    hi = tab[1:]
+    pts = np.concatenate([lo, (lo + hi) / 2, np.nextafter(hi, 0.0), [tab[-1]]])
+    pts = np.concatenate([pts, -pts])
+    got = O.bf16_ulp(pts)
+    want = _ulp_exact(pts)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(pts[i]), float(got[i]), float(want[i])) for i in bad[:6]]
+    # closed values the format fixes: spacing 2^-7 on [1, 2), 2^-133 at and
+    # near zero (the smallest subnormal), 2^120 in the top binade
+    assert O.bf16_ulp(1.0) == 2.0 ** -7 and O.bf16_ulp(1.99) == 2.0 ** -7
+    assert O.bf16_ulp(0.0) == 2.0 ** -133 and O.bf16_ulp(2.0 ** -140) == 2.0 ** -133
+    assert O.bf16_ulp(2.0 ** -126) == 2.0 ** -133 and O.bf16_ulp(2.0 ** -125) == 2.0 ** -132
+    assert O.bf16_ulp(3.0e38) == 2.0 ** 120
+
+
+def test_tolerance_contract_exact():
+    """gemm_tolerance = 2^-7 * sum_k |a_k b_k| / (sa sb) + ulp_bf16(r) (up to
+    float64 rounding), with
+    the sum of magnitudes written out term by term in exact rationals and the
+    ulp from the format's bit fields; also for the tighter rel the GPU tests
+    apply, and for dX / dW orientation (a transposed operand in the sum
+    would fail)."""
     rng = np.random.default_rng(1)
-    x8 = _codes((8, 32), O.E4M3, rng)
-    w8 = _codes((4, 32), O.E4M3, rng)
-    ref = O.linear_fwd(x8, w8, O.E4M3, 2.0, 4.0)
-    tol = O.gemm_tolerance(ref)
-    X, W = O.decode_array(x8, O.E4M3), O.decode_array(w8, O.E4M3)
-    assert np.allclose(tol, 2.0 ** -7 * (np.abs(X) @ np.abs(W).T) / 8.0 + O.bf16_ulp(ref.r))
+    x8 = _codes((6, 16), O.E4M3, rng)
+    w8 = _codes((4, 16), O.E4M3, rng)
+    g8 = _codes((6, 4), O.E5M2, rng)
+    sx, sw, sg = np.float32(2.0), np.float32(0.375), np.float32(1536.0)
+    cases = [
+        (O.linear_fwd(x8, w8, O.E4M3, sx, sw),
+         lambda i, j: sum(abs(_frac(x8[i, k], O.E4M3) * _frac(w8[j, k], O.E4M3))
+                          for k in range(16)), Fraction(1) / (Fraction(float(sx)) * Fraction(float(sw)))),
+        (O.linear_bwd_dx(g8, O.E5M2, w8, O.E4M3, sg, sw),
+         lambda i, j: sum(abs(_frac(g8[i, n], O.E5M2) * _frac(w8[n, j], O.E4M3))
+                          for n in range(4)), Fraction(1) / (Fraction(float(sg)) * Fraction(float(sw)))),
+        (O.linear_bwd_dw(g8, O.E5M2, x8, O.E4M3, sg, sx),
+         lambda i, j: sum(abs(_frac(g8[m, i], O.E5M2) * _frac(x8[m, j], O.E4M3))
+                          for m in range(6)), Fraction(1) / (Fraction(float(sg)) * Fraction(float(sx)))),
+    ]
+    for ref, abs_sum, dq in cases:
+        for rel in (2.0 ** -7, 2.0 ** -10):
+            tol = O.gemm_tolerance(ref, rel)
+            ulp = _ulp_exact(ref.r)
+            for i in range(ref.r.shape[0]):
+                for j in range(ref.r.shape[1]):
+                    want = Fraction(rel) * abs_sum(i, j) * dq + Fraction(float(ulp[i, j]))
+                    # the oracle sums in float64: equal up to its rounding
+                    err = abs(Fraction(float(tol[i, j])) - want)
+                    assert err <= want * Fraction(1, 2 ** 40), (i, j, rel)
+
+
+def test_quantized_gradient_direction_sanity():
+    """The pages' regression signature of a wrong scale (the amax of already
+    quantized values): the fp8 input gradient's direction collapsed to a
+    cosine of about 0.05 with the bf16 one.  With the oracle's quantize and
+    GEMM, the cosine of dX = G8 W8 / (sg sw) with the unquantized G W is
+    close to 1, for the delayed scale of a first step and for a window that
+    has seen 16x larger values; a scale that leaked the wrong ratio (G
+    quantized with 2^-32 of its scale, most codes flushed to zero) is far
+    from it."""
+    rng = np.random.default_rng(5)
+    M, N, K = 96, 64, 80
+    W = O.bf16_value(O.bf16_bits(rng.standard_normal((N, K)) * 0.02))
+    G = O.bf16_value(O.bf16_bits(rng.standard_normal((M, N)) * 1e-3))
+    exact = G @ W
+    cos = lambda a, b: float(np.sum(a * b) / np.sqrt(np.sum(a * a) * np.sum(b * b)))
+    rw, rg = O.ScaleRing(16), O.ScaleRing(16)
+    w8, sw, _ = O.quantize_step(W, O.E4M3, rw)
+    g8, sg, _ = O.quantize_step(G, O.E5M2, rg)
+    assert cos(O.linear_bwd_dx(g8, O.E5M2, w8, O.E4M3, sg, sw).r, exact) > 0.995
+    O.quantize_step(G * 16.0, O.E5M2, rg)  # a larger step enters the window
+    g8b, sgb, _ = O.quantize_step(G, O.E5M2, rg)
+    assert sgb == sg / 16
+    assert cos(O.linear_bwd_dx(g8b, O.E5M2, w8, O.E4M3, sgb, sw).r, exact) > 0.98
+    bad_s = np.float32(sg * 2.0 ** -32)
+    g8c = O.quantize_with_scale(G, bad_s, O.E5M2)
+    assert cos(O.linear_bwd_dx(g8c, O.E5M2, w8, O.E4M3, bad_s, sw).r, exact) < 0.9
 
 
 def test_fp8out_hand_worked_steps():
