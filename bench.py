@@ -88,6 +88,16 @@ class Layer:
     def __init__(self, F, WL, wl, li, dev, stream, side, inputs=None):
         import torch
 
+        # every buffer is made, filled and first written on `stream`, the
+        # stream the library calls run on, so that no zero fill or copy on
+        # another stream can land after a library write to the same scalar
+        with torch.cuda.stream(stream):
+            self._build(F, WL, wl, li, dev, stream, side, inputs)
+        stream.synchronize()
+
+    def _build(self, F, WL, wl, li, dev, stream, side, inputs):
+        import torch
+
         X, W, b, G = WL.layer_inputs(wl, li) if inputs is None else inputs
         self.delayed = wl.delayed
         self.prequant = wl.name.startswith("prequant")

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FP8_ABI_VERSION 4
+#define FP8_ABI_VERSION 5
 #define FP8_RING_MAX_HIST 1024
 
 typedef enum {
@@ -69,7 +69,8 @@ typedef enum {
                          validating the fmt enum; [P1] pre-quantized operands
                          must match fmt) */
   FP8_ERR_RING = 4,   /* ring hist_len outside [1, 1024], dev NULL or not
-                         256-byte aligned, or a scale output aliasing it */
+                         256-byte aligned, a scale output aliasing it, or an
+                         unseeded ring used on a stream under graph capture */
   FP8_ERR_HIP = 5     /* a kernel launch failed */
 } fp8_status_t;
 
@@ -116,6 +117,10 @@ typedef struct {
  *             with the scale published by the previous step.
  * Byte-copying dev plus seeded resumes the scale sequence exactly.  A ring
  * must not be used by two calls that may run concurrently.
+ * Graph capture: whether a call seeds is decided on the host when it is
+ * issued, so a ring must be seeded (one call through it enqueued) before any
+ * call on it is captured; a call that would seed a ring on a capturing
+ * stream returns FP8_ERR_RING with nothing enqueued.
  */
 typedef struct {
   void* dev;
@@ -125,6 +130,11 @@ typedef struct {
 
 /* Library ABI version (FP8_ABI_VERSION). */
 int fp8_abi_version(void);
+
+/* Identity of the sources the library was built from: the SHA-256 (hex) of
+ * its HIP sources and this header, fixed at build time ("unknown" when the
+ * build did not supply it).  Static string, never NULL. */
+const char* fp8_source_hash(void);
 
 /* Static description of a status code. */
 const char* fp8_status_str(int status);

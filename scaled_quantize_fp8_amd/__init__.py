@@ -30,7 +30,7 @@ _TORCH_DT = {torch.float32: FP8_DT_F32, torch.float16: FP8_DT_F16, torch.bfloat1
 _FMT_DT = {FP8_E4M3: FP8_DT_E4M3, FP8_E5M2: FP8_DT_E5M2}
 
 C_SYMBOLS = (
-    "fp8_abi_version", "fp8_status_str", "fp8_ring_bytes", "fp8_ring_init", "fp8_quantize",
+    "fp8_abi_version", "fp8_source_hash", "fp8_status_str", "fp8_ring_bytes", "fp8_ring_init", "fp8_quantize",
     "fp8_quantize_pair", "fp8_linear_fwd", "fp8_linear_bwd_dx", "fp8_db_workspace_bytes",
     "fp8_linear_bwd_dw", "fp8_gemm", "fp8_quantize_2d", "fp8_gemm_fp8out", "fp8_linear_bwd",
 )
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         op, rp = _Operand, ctypes.POINTER(_Ring)
         L.fp8_abi_version.restype = ctypes.c_int
+        L.fp8_source_hash.restype = ctypes.c_char_p
+        L.fp8_source_hash.argtypes = []
         L.fp8_status_str.restype = ctypes.c_char_p
         L.fp8_status_str.argtypes = [ctypes.c_int]
         L.fp8_ring_bytes.restype = sz
@@ -99,6 +101,10 @@ def fp8_abi_version() -> int:
     return lib().fp8_abi_version()
 
 
+def fp8_source_hash() -> str:
+    return lib().fp8_source_hash().decode()
+
+
 def fp8_ring_bytes(hist_len: int) -> int:
     return lib().fp8_ring_bytes(hist_len)
 
@@ -122,6 +128,66 @@ def _stream(stream) -> int | None:
 def _check(status: int, where: str) -> None:
     if status != FP8_OK:
         raise Fp8Error(status, where)
+
+
+_HP = (torch.float32, torch.float16, torch.bfloat16)
+
+
+def _need(t, what, dtypes=None, shape=None, numel=None, optional=True):
+    """Validate a tensor argument before its pointer crosses the boundary:
+    contiguous (the C ABI takes dense row-major buffers: a transposed or
+    strided view would be read as the wrong elements), of an allowed dtype,
+    of the expected shape or element count, on the GPU.  None passes when
+    the argument is optional (the library decides whether it is needed)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{what} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor, got {type(t).__name__}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous (shape {tuple(t.shape)}, "
+                         f"strides {t.stride()}); pass .contiguous()")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{what}: dtype {t.dtype} not in {[str(d) for d in dtypes]}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{what}: {t.numel()} elements, at least {numel} needed")
+
+
+def _on_gpu(**named):
+    """Second phase of the checks, after every argument's structure: each
+    tensor (or Quantized operand) given lives on the GPU."""
+    for what, t in named.items():
+        for name, x in ((what, t.codes), (what + ".scale", t.scale)) if isinstance(t, Quantized) \
+                else ((what, t),):
+            if isinstance(x, torch.Tensor) and x.device.type != "cuda":
+                raise ValueError(f"{name}: must be a GPU tensor (got {x.device})")
+
+
+def _need_scalar(t, what, optional=True):
+    _need(t, what, (torch.float32,), numel=1, optional=optional)
+
+
+def _need_operand(t, what, shape, hp_ok=True):
+    """A high-precision tensor or a Quantized (uint8 codes + float32 scale)."""
+    if isinstance(t, Quantized):
+        _need(t.codes, f"{what}.codes", (torch.uint8,), shape=shape, optional=False)
+        _need_scalar(t.scale, f"{what}.scale", optional=False)
+        if t.fmt not in _FMT_DT:
+            raise ValueError(f"{what}: unknown fp8 format {t.fmt}")
+    elif hp_ok:
+        _need(t, what, _HP, shape=shape, optional=False)
+    else:
+        raise TypeError(f"{what}: expected a Quantized operand")
+
+
+def _dims2(t, what):
+    d = t.codes if isinstance(t, Quantized) else t
+    if not isinstance(d, torch.Tensor) or d.dim() != 2:
+        raise ValueError(f"{what}: expected a 2-D matrix")
+    return d.shape
 
 
 @dataclass
@@ -175,12 +241,23 @@ def _vp(t):
 
 
 def _quantize_args(x, fmt, q, ring, scale_used, amax_out, stream):
+    _need(x, "x", _HP, optional=False)
+    _need(q, "q", (torch.uint8,), numel=x.numel(), optional=x.numel() == 0)
+    _need_scalar(scale_used, "scale_used")
+    _need_scalar(amax_out, "amax_out")
+    _on_gpu(x=x, q=q, scale_used=scale_used, amax_out=amax_out)
     return (_vp(x), ctypes.c_int32(_TORCH_DT[x.dtype]), ctypes.c_int64(x.numel()),
             ctypes.c_int32(fmt), _vp(q), _ring(ring), _vp(scale_used), _vp(amax_out),
             ctypes.c_void_p(_stream(stream)))
 
 
 def _quantize_pair_args(x0, q0, ring0, su0, am0, x1, q1, ring1, su1, am1, fmt, stream):
+    for i, (x, q, su, am) in enumerate(((x0, q0, su0, am0), (x1, q1, su1, am1))):
+        _need(x, f"x{i}", _HP, optional=False)
+        _need(q, f"q{i}", (torch.uint8,), numel=x.numel(), optional=x.numel() == 0)
+        _need_scalar(su, f"scale_used{i}")
+        _need_scalar(am, f"amax_out{i}")
+    _on_gpu(x0=x0, q0=q0, su0=su0, am0=am0, x1=x1, q1=q1, su1=su1, am1=am1)
     return (_vp(x0), ctypes.c_int32(_TORCH_DT[x0.dtype]), ctypes.c_int64(x0.numel()), _vp(q0),
             _ring(ring0), _vp(su0), _vp(am0), _vp(x1), ctypes.c_int32(_TORCH_DT[x1.dtype]),
             ctypes.c_int64(x1.numel()), _vp(q1), _ring(ring1), _vp(su1), _vp(am1),
@@ -189,10 +266,23 @@ def _quantize_pair_args(x0, q0, ring0, su0, am0, x1, q1, ring1, su1, am1, fmt, s
 
 def _fwd_args(x, w, bias, fmt, y, ring_x, ring_w, x8_out, w8_out, sx_used, sw_used, amax_x,
               amax_w, stream):
-    xd = x.codes if isinstance(x, Quantized) else x
-    wd = w.codes if isinstance(w, Quantized) else w
-    M, K = xd.shape
-    N = wd.shape[0]
+    M, K = _dims2(x, "x")
+    N = _dims2(w, "w")[0]
+    _need_operand(x, "x", (M, K))
+    _need_operand(w, "w", (N, K))
+    if bias is not None:
+        if isinstance(bias, Quantized):
+            _need_operand(bias, "bias", (N,), hp_ok=False)
+        else:
+            _need(bias, "bias", (torch.bfloat16,), shape=(N,))
+    _need(y, "y", (torch.bfloat16,), shape=(M, N), optional=M * N == 0)
+    _need(x8_out, "x8_out", (torch.uint8,), shape=(M, K))
+    _need(w8_out, "w8_out", (torch.uint8,), shape=(N, K))
+    for t, n in ((sx_used, "sx_used"), (sw_used, "sw_used"), (amax_x, "amax_x"),
+                 (amax_w, "amax_w")):
+        _need_scalar(t, n)
+    _on_gpu(x=x, w=w, bias=bias, y=y, x8_out=x8_out, w8_out=w8_out, sx_used=sx_used,
+            sw_used=sw_used, amax_x=amax_x, amax_w=amax_w)
     return (ctypes.c_int64(M), ctypes.c_int64(N), ctypes.c_int64(K), _operand(x), _operand(w),
             _operand(bias), ctypes.c_int32(fmt), _ring(ring_x), _ring(ring_w), _vp(y), _vp(x8_out),
             _vp(w8_out), _vp(sx_used), _vp(sw_used), _vp(amax_x), _vp(amax_w),
@@ -200,18 +290,32 @@ def _fwd_args(x, w, bias, fmt, y, ring_x, ring_w, x8_out, w8_out, sx_used, sw_us
 
 
 def _dx_args(g, fmt_g, w8, dx, ring_g, g8_out, sg_used, amax_g, stream):
-    gd = g.codes if isinstance(g, Quantized) else g
-    M, N = gd.shape
-    K = w8.codes.shape[1]
+    M, N = _dims2(g, "g")
+    K = _dims2(w8, "w8")[1]
+    _need_operand(g, "g", (M, N))
+    _need_operand(w8, "w8", (N, K), hp_ok=False)
+    _need(dx, "dx", (torch.bfloat16,), shape=(M, K), optional=M * K == 0)
+    _need(g8_out, "g8_out", (torch.uint8,), shape=(M, N))
+    _need_scalar(sg_used, "sg_used")
+    _need_scalar(amax_g, "amax_g")
+    _on_gpu(g=g, w8=w8, dx=dx, g8_out=g8_out, sg_used=sg_used, amax_g=amax_g)
     return (ctypes.c_int64(M), ctypes.c_int64(N), ctypes.c_int64(K), _operand(g),
             ctypes.c_int32(fmt_g), _ring(ring_g), _operand(w8), _vp(dx), _vp(g8_out),
             _vp(sg_used), _vp(amax_g), ctypes.c_void_p(_stream(stream)))
 
 
 def _dw_args(g, fmt_g, x8, dw, db, db_ws, ring_g, g8_out, sg_used, amax_g, stream):
-    gd = g.codes if isinstance(g, Quantized) else g
-    M, N = gd.shape
-    K = x8.codes.shape[1]
+    M, N = _dims2(g, "g")
+    K = _dims2(x8, "x8")[1]
+    _need_operand(g, "g", (M, N))
+    _need_operand(x8, "x8", (M, K), hp_ok=False)
+    _need(dw, "dw", (torch.bfloat16,), shape=(N, K), optional=N * K == 0)
+    _need(db, "db", (torch.bfloat16,), shape=(N,))
+    _need(db_ws, "db_ws", (torch.float32,), numel=fp8_db_workspace_bytes(M, N) // 4)
+    _need(g8_out, "g8_out", (torch.uint8,), shape=(M, N))
+    _need_scalar(sg_used, "sg_used")
+    _need_scalar(amax_g, "amax_g")
+    _on_gpu(g=g, x8=x8, dw=dw, db=db, db_ws=db_ws, g8_out=g8_out, sg_used=sg_used, amax_g=amax_g)
     return (ctypes.c_int64(M), ctypes.c_int64(N), ctypes.c_int64(K), _operand(g),
             ctypes.c_int32(fmt_g), _ring(ring_g), _operand(x8), _vp(dw), _vp(db), _vp(db_ws),
             _vp(g8_out), _vp(sg_used), _vp(amax_g), ctypes.c_void_p(_stream(stream)))
@@ -237,7 +341,15 @@ def bind_fp8_quantize(x, fmt, q, ring=None, scale_used=None, amax_out=None, stre
 
 
 def _quantize_2d_args(x, fmt, layout, q, qt, ring, scale_used, amax_out, stream):
+    _need(x, "x", _HP, optional=False)
+    if x.dim() != 2:
+        raise ValueError("x: expected a 2-D matrix")
     rows, cols = x.shape
+    _need(q, "q", (torch.uint8,), shape=(rows, cols))
+    _need(qt, "qt", (torch.uint8,), shape=(cols, rows))
+    _need_scalar(scale_used, "scale_used")
+    _need_scalar(amax_out, "amax_out")
+    _on_gpu(x=x, q=q, qt=qt, scale_used=scale_used, amax_out=amax_out)
     return (_vp(x), ctypes.c_int32(_TORCH_DT[x.dtype]), ctypes.c_int64(rows), ctypes.c_int64(cols),
             ctypes.c_int32(fmt), ctypes.c_int32(layout), _vp(q), _vp(qt), _ring(ring),
             _vp(scale_used), _vp(amax_out), ctypes.c_void_p(_stream(stream)))
@@ -310,9 +422,20 @@ def bind_fp8_linear_bwd_dw(g, fmt_g, x8, dw, db=None, db_ws=None, ring_g=None, g
 
 def _bwd_args(g, fmt_g, x8, w8, dx, dw, db, db_ws, ring_g, g8_out, sg_used, amax_g, stream,
               stream_dw):
-    gd = g.codes if isinstance(g, Quantized) else g
-    M, N = gd.shape
-    K = x8.codes.shape[1]
+    M, N = _dims2(g, "g")
+    K = _dims2(x8, "x8")[1]
+    _need_operand(g, "g", (M, N))
+    _need_operand(x8, "x8", (M, K), hp_ok=False)
+    _need_operand(w8, "w8", (N, K), hp_ok=False)
+    _need(dx, "dx", (torch.bfloat16,), shape=(M, K), optional=M * K == 0)
+    _need(dw, "dw", (torch.bfloat16,), shape=(N, K), optional=N * K == 0)
+    _need(db, "db", (torch.bfloat16,), shape=(N,))
+    _need(db_ws, "db_ws", (torch.float32,), numel=fp8_db_workspace_bytes(M, N) // 4)
+    _need(g8_out, "g8_out", (torch.uint8,), shape=(M, N))
+    _need_scalar(sg_used, "sg_used")
+    _need_scalar(amax_g, "amax_g")
+    _on_gpu(g=g, x8=x8, w8=w8, dx=dx, dw=dw, db=db, db_ws=db_ws, g8_out=g8_out, sg_used=sg_used,
+            amax_g=amax_g)
     st = _stream(stream)
     st_dw = st if stream_dw is None else stream_dw.cuda_stream
     return (ctypes.c_int64(M), ctypes.c_int64(N), ctypes.c_int64(K), _operand(g),
@@ -386,10 +509,19 @@ def bind_fp8_gemm(a, b, c, bias=None, stream=None):
 
 
 def _gemm_fp8out_args(a, b, c8, fmt_out, ring_out, scale_used, amax_out, bias, stream):
-    M, K = a.codes.shape
-    N = b.codes.shape[0]
-    if b.codes.shape[1] != K or tuple(c8.shape) != (M, N):
-        raise ValueError("fp8_gemm_fp8out: a [M,K], b [N,K], c8 [M,N]")
+    M, K = _dims2(a, "a")
+    N = _dims2(b, "b")[0]
+    _need_operand(a, "a", (M, K), hp_ok=False)
+    _need_operand(b, "b", (N, K), hp_ok=False)
+    _need(c8, "c8", (torch.uint8,), shape=(M, N), optional=False)
+    _need_scalar(scale_used, "scale_used")
+    _need_scalar(amax_out, "amax_out")
+    if bias is not None:
+        if isinstance(bias, Quantized):
+            _need_operand(bias, "bias", (N,), hp_ok=False)
+        else:
+            _need(bias, "bias", (torch.bfloat16,), shape=(N,))
+    _on_gpu(a=a, b=b, c8=c8, scale_used=scale_used, amax_out=amax_out, bias=bias)
     return (ctypes.c_int64(M), ctypes.c_int64(N), ctypes.c_int64(K), _operand(a), _operand(b),
             _operand(bias), ctypes.c_int32(fmt_out), _ring(ring_out), _vp(c8), _vp(scale_used),
             _vp(amax_out), ctypes.c_void_p(_stream(stream)))

@@ -2,6 +2,7 @@
 
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -18,6 +19,21 @@ HEADERS = [os.path.join(CSRC, f) for f in ("fp8l_device.hpp", "fp8l_quantize.hpp
 ]
 
 
+def source_hash() -> str:
+    """SHA-256 over the library's sources and its public header (file names
+    and bytes, in sorted order).  The build compiles it into the library
+    (fp8_source_hash), so a library built from other sources is detected."""
+    h = hashlib.sha256()
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                   if f.endswith((".hip", ".hpp", ".h")))
+    files.append(os.path.join(ROOT, "include", "fp8linear.h"))
+    for path in files:
+        h.update(os.path.relpath(path, ROOT).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -31,6 +47,7 @@ def build_command(out: str = LIB_PATH, extra: list[str] | None = None) -> list[s
         # packed fp32 VALU forms stay off (see the library's design notes)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(ROOT, "include"),
+        f'-DFP8L_SOURCE_HASH="{source_hash()}"',
         *(extra or []),
         *SOURCES, "-o", out,
     ]

@@ -65,9 +65,25 @@ int check_alias(const fp8_ring_t* r, const float* scale_out) {
   return FP8_OK;
 }
 
+// True while the stream is being captured into a graph.  A query that fails
+// counts as not capturing (a launch on such a stream fails on its own).
+bool capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
+}
+
+// A ring's first use seeds it with an extra amax pass, decided on the host
+// from ring->seeded.  Captured into a graph, that pass and the seeding
+// conversion would run again on every replay (dynamic scaling, while the
+// host flag says seeded), so an unseeded ring is refused under capture.
+int check_seed_capture(const fp8_ring_t* r, hipStream_t st) {
+  return (r && !r->seeded && capturing(st)) ? FP8_ERR_RING : FP8_OK;
+}
+
 // Checks for one quantize (shared by the four entry points).
 int check_quant(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, const uint8_t* q,
-                const fp8_ring_t* ring, const float* scale_used, const float* amax_out) {
+                const fp8_ring_t* ring, const float* scale_used, const float* amax_out,
+                hipStream_t stream) {
   if (n < 0) return FP8_ERR_SHAPE;
   if (!is_hp(in_dtype) || !valid_fmt(fmt)) return FP8_ERR_DTYPE;
   if (n > 0 && (!x || !q)) return FP8_ERR_NULL;
@@ -75,7 +91,8 @@ int check_quant(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, const u
   if (!ring && !amax_out) return FP8_ERR_NULL;
   int st = check_ring(ring);
   if (st) return st;
-  return check_alias(ring, scale_used);
+  if ((st = check_alias(ring, scale_used))) return st;
+  return check_seed_capture(ring, stream);
 }
 
 // 2-D shape of a quantize: the column-sum variant (ws != null) or the
@@ -437,6 +454,11 @@ extern "C" {
 
 int fp8_abi_version(void) { return FP8_ABI_VERSION; }
 
+#ifndef FP8L_SOURCE_HASH
+#define FP8L_SOURCE_HASH "unknown"
+#endif
+const char* fp8_source_hash(void) { return FP8L_SOURCE_HASH; }
+
 const char* fp8_status_str(int status) {
   switch (status) {
     case FP8_OK: return "ok";
@@ -478,9 +500,9 @@ int fp8_quantize_pair(const void* x0, int32_t dtype0, int64_t n0, uint8_t* q0, f
                       float* scale_used0, float* amax_out0, const void* x1, int32_t dtype1,
                       int64_t n1, uint8_t* q1, fp8_ring_t* ring1, float* scale_used1,
                       float* amax_out1, int32_t fmt, hipStream_t stream) {
-  int st = check_quant(x0, dtype0, n0, fmt, q0, ring0, scale_used0, amax_out0);
+  int st = check_quant(x0, dtype0, n0, fmt, q0, ring0, scale_used0, amax_out0, stream);
   if (st) return st;
-  st = check_quant(x1, dtype1, n1, fmt, q1, ring1, scale_used1, amax_out1);
+  st = check_quant(x1, dtype1, n1, fmt, q1, ring1, scale_used1, amax_out1, stream);
   if (st) return st;
   if (!mul_ok(n0, 4) || !mul_ok(n1, 4)) return FP8_ERR_SHAPE;
   if (ring0 && ring0 == ring1) return FP8_ERR_RING;
@@ -500,7 +522,7 @@ int fp8_quantize_2d(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
   const bool want_q = layout != FP8_QUANT_TRANSPOSED, want_qt = layout != FP8_QUANT_ROWS;
   if (n > 0 && ((want_q && !q) || (want_qt && !qt))) return FP8_ERR_NULL;
   // the rest as fp8_quantize (q stands for whichever output is given)
-  int st = check_quant(x, in_dtype, n, fmt, want_q ? q : qt, ring, scale_used, amax_out);
+  int st = check_quant(x, in_dtype, n, fmt, want_q ? q : qt, ring, scale_used, amax_out, stream);
   if (st) return st;
   if (layout == FP8_QUANT_ROWS) {
     enqueue_quant(x, in_dtype, n, fmt, q, ring, scale_used, amax_out, nullptr, stream);
@@ -519,7 +541,7 @@ int fp8_quantize_2d(const void* x, int32_t in_dtype, int64_t rows, int64_t cols,
 
 int fp8_quantize(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, uint8_t* q,
                  fp8_ring_t* ring, float* scale_used, float* amax_out, hipStream_t stream) {
-  int st = check_quant(x, in_dtype, n, fmt, q, ring, scale_used, amax_out);
+  int st = check_quant(x, in_dtype, n, fmt, q, ring, scale_used, amax_out, stream);
   if (st) return st;
   if (!mul_ok(n, 4)) return FP8_ERR_SHAPE;
   enqueue_quant(x, in_dtype, n, fmt, q, ring, scale_used, amax_out, nullptr, stream);
@@ -537,7 +559,7 @@ int fp8_linear_fwd(int64_t M, int64_t N, int64_t K, fp8_operand_t x, fp8_operand
   int st;
   // X
   if (is_hp(x.dtype)) {
-    st = check_quant(x.data, x.dtype, M * K, fmt, x8_out, ring_x, sx_used, amax_x);
+    st = check_quant(x.data, x.dtype, M * K, fmt, x8_out, ring_x, sx_used, amax_x, stream);
     if (st) return st;
   } else if (x.dtype == f8dt) {
     if ((M * K > 0 && !x.data) || !x.scale) return FP8_ERR_NULL;
@@ -546,7 +568,7 @@ int fp8_linear_fwd(int64_t M, int64_t N, int64_t K, fp8_operand_t x, fp8_operand
   }
   // W
   if (is_hp(w.dtype)) {
-    st = check_quant(w.data, w.dtype, N * K, fmt, w8_out, ring_w, sw_used, amax_w);
+    st = check_quant(w.data, w.dtype, N * K, fmt, w8_out, ring_w, sw_used, amax_w, stream);
     if (st) return st;
   } else if (w.dtype == f8dt) {
     if ((N * K > 0 && !w.data) || !w.scale) return FP8_ERR_NULL;
@@ -619,7 +641,7 @@ static int bwd_prepare(int64_t M, int64_t N, fp8_operand_t g, int32_t fmt_g, fp8
   if (!valid_fmt(fmt_g)) return FP8_ERR_DTYPE;
   if (is_hp(g.dtype)) {
     if (validate_only)
-      return check_quant(g.data, g.dtype, M * N, fmt_g, g8_out, ring_g, sg_used, amax_g);
+      return check_quant(g.data, g.dtype, M * N, fmt_g, g8_out, ring_g, sg_used, amax_g, stream);
     enqueue_quant(g.data, g.dtype, M * N, fmt_g, g8_out, ring_g, sg_used, amax_g, cs, stream);
     *g8 = g8_out;
     *sg = sg_used;
@@ -898,6 +920,7 @@ int fp8_gemm_fp8out(int64_t M, int64_t N, int64_t K, fp8_operand_t a, fp8_operan
   int st = check_ring(ring_out);
   if (st) return st;
   if (check_alias(ring_out, scale_used) || check_alias(ring_out, amax_out)) return FP8_ERR_RING;
+  if ((st = check_seed_capture(ring_out, stream))) return st;
   if (M == 0 || N == 0) return FP8_OK;
   if (K > 0 && (!a.data || !b.data)) return FP8_ERR_NULL;
   if (!c8) return FP8_ERR_NULL;

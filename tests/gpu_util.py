@@ -83,14 +83,19 @@ def assert_ring_matches(ring, oring: O.ScaleRing):
 
 
 def check_gemm(y_bits: np.ndarray, ref: O.GemmRef, what: str = ""):
-    """Assert the contract bound and the diagnostic bound elementwise."""
+    """Assert the contract bound and the diagnostic bound elementwise.  An
+    output that is NaN or infinite where the reference is finite fails (the
+    comparisons are written as "not within", so a NaN error never passes)."""
     y = O.bf16_value(y_bits)
+    fin = np.isfinite(ref.r)
+    nonfinite = fin & ~np.isfinite(y)
+    assert not nonfinite.any(), f"{what}: {nonfinite.sum()} non-finite outputs where the reference is finite"
     err = np.abs(y - ref.r)
     tol = O.gemm_tolerance(ref, CONTRACT_REL)
-    bad = err > tol
-    assert not bad.any(), f"{what}: {bad.sum()} elements outside the 2^-7 contract, max err {err.max()}"
+    bad = ~(err <= tol)
+    assert not bad.any(), f"{what}: {bad.sum()} elements outside the 2^-7 contract, max err {np.nanmax(err)}"
     tight = O.gemm_tolerance(ref, TIGHT_REL)
-    bad = err > tight
+    bad = ~(err <= tight)
     assert not bad.any(), (
         f"{what}: {bad.sum()} elements outside the 2^-10 diagnostic bound; "
         f"worst err/sum|ab| = {np.max((err - O.bf16_ulp(ref.r)) / np.maximum(ref.abs_sum, 1e-300))}")

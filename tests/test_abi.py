@@ -45,10 +45,18 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert F.fp8_abi_version() == 4
+    assert F.fp8_abi_version() == 5
     for st in range(6):
         assert F.status_str(st)
     assert F.status_str(99) == "unknown status"
+
+
+def test_library_built_from_tree_sources(lib):
+    """The library carries the hash of the sources it was built from; the
+    GPU tests refuse a library whose hash differs from the tree's."""
+    from scaled_quantize_fp8_amd import _build
+    h = F.fp8_source_hash()
+    assert len(h) == 64 and h == _build.source_hash()
 
 
 def test_sizes(lib):

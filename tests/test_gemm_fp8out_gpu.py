@@ -82,10 +82,13 @@ def test_fp8out_exact_steps(fa, fb, M, K, N, fmt_out):
         assert_ring_matches(ring, oring)
 
 
+# (200, 640, 528): 128x128 blocks (4 waves, two per CU), ragged rows;
+# (2048, 1536, 6912): the up projection's forward, 216 tiles of 256x256 (the
+# 8-wave kernel and its fp8 epilogue), every element compared
+@pytest.mark.parametrize("M,K,N", [(200, 640, 528), (2048, 1536, 6912)])
 @pytest.mark.parametrize("fmt_out", [O.E4M3, O.E5M2])
-def test_fp8out_random_within_tolerance(fmt_out):
-    rng = np.random.default_rng(11 + fmt_out)
-    M, K, N = 200, 640, 528
+def test_fp8out_random_within_tolerance(fmt_out, M, K, N):
+    rng = np.random.default_rng(11 + fmt_out + M)
     b8 = _rand_codes((N, K), O.E4M3, rng)
     bias_t, bias_bits = _bf16(rng.standard_normal(N))
     beta = O.bias_values(bias_bits, "bf16")

@@ -207,22 +207,28 @@ def test_repeat_runs_bit_identical(M, N, K, tile):
 
 
 def test_full_size_sampled_rows(tile):
-    """dim1536/ffn6912 shapes at M = 2048, full GPU outputs, oracle on a
-    seeded sample of rows plus the first and last rows."""
+    """dim1536/ffn6912 shapes at M = 2048, random codes over the whole finite
+    range.  Under the automatic tile choice (the configuration the step and
+    the benchmark run) every output element is compared with the oracle;
+    under each forced tile configuration a seeded sample of rows plus the
+    first and last."""
     rng = np.random.default_rng(99)
+    full = tile == "auto"
     for (K, N) in ((1536, 4608), (1536, 1536), (1536, 6912), (6912, 1536)):
         M = 2048
         x8 = _rand_codes((M, K), O.E4M3, rng)
         w8 = _rand_codes((N, K), O.E4M3, rng)
         g8 = _rand_codes((M, N), O.E5M2, rng)
-        rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 48, replace=False)]))
+        rows = np.arange(M) if full else \
+            np.unique(np.concatenate([[0, M - 1], rng.choice(M, 48, replace=False)]))
         y = run_fwd(x8, w8, O.E4M3, 100.0, 3000.0)
         check_gemm(y[rows], O.linear_fwd(x8[rows], w8, O.E4M3, 100.0, 3000.0), f"fwd {K}x{N}")
         dx = run_dx(g8, O.E5M2, w8, O.E4M3, 7.0e3, 3000.0)
         check_gemm(dx[rows], O.linear_bwd_dx(g8[rows], O.E5M2, w8, O.E4M3, 7.0e3, 3000.0),
                    f"dx {K}x{N}")
         dw, _ = run_dw(g8, O.E5M2, x8, O.E4M3, 7.0e3, 100.0)
-        nrows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 48, replace=False)]))
+        nrows = np.arange(N) if full else \
+            np.unique(np.concatenate([[0, N - 1], rng.choice(N, 48, replace=False)]))
         check_gemm(dw[nrows], O.linear_bwd_dw(g8[:, nrows], O.E5M2, x8, O.E4M3, 7.0e3, 100.0),
                    f"dw {K}x{N}")
 

@@ -119,3 +119,32 @@ def test_graph_replays_match_eager(M, K, N, two_stream):
         a, r = eager.snapshot(), graphed.snapshot()
         for k in a:
             assert np.array_equal(a[k], r[k]), f"replay {i}: {k} differs from the eager step"
+
+
+def test_unseeded_ring_refused_under_capture():
+    """Whether a call seeds its ring is decided when it is issued; captured,
+    the seeding pass would re-seed on every replay.  So a call that would
+    seed a ring on a capturing stream fails with FP8_ERR_RING and enqueues
+    nothing, and the same call succeeds eagerly afterwards."""
+    x = torch.randn(256, 64, device=DEV).to(torch.bfloat16)
+    q = torch.empty(256 * 64, dtype=torch.uint8, device=DEV)
+    su = torch.zeros(1, dtype=torch.float32, device=DEV)
+    stream = torch.cuda.Stream()
+    ring = F.ScaleRing(4, stream=stream)
+    stream.synchronize()
+    before = ring.buf.clone()
+    g = torch.cuda.CUDAGraph()
+    status = None
+    with torch.cuda.graph(g, stream=stream):
+        q.zero_()  # the graph holds one node of its own
+        try:
+            F.fp8_quantize(x, FX, q, ring, su, stream=stream)
+        except F.Fp8Error as exc:
+            status = exc.status
+    assert status == F.FP8_ERR_RING
+    assert not ring.seeded
+    torch.cuda.synchronize()
+    assert torch.equal(ring.buf, before)
+    F.fp8_quantize(x, FX, q, ring, su, stream=stream)  # eager: seeds
+    stream.synchronize()
+    assert ring.seeded and ring_state(ring)["idx"] == 1

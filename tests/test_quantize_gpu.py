@@ -78,6 +78,49 @@ def test_encoder_fp32_patterns(fmt):
     assert bad.size == 0, [(float(xs[i]), hex(int(ref[i])), hex(int(q[i]))) for i in bad[:8]]
 
 
+def _f32_bits(v: float) -> int:
+    return int(np.array([v], np.float32).view(np.uint32)[0])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_encoder_every_fp32_pattern_in_range(fmt):
+    """Every fp32 bit pattern whose magnitude lies between half the smallest
+    subnormal and twice the maximum of the format (both signs: 331M patterns
+    for e4m3, 566M for e5m2), through the GPU encoder (scale 1, so the codes
+    are enc(x) itself) against the oracle's encoder.  Outside that range
+    every value encodes to a signed zero or saturates; those values, with
+    NaN, infinities and fp32 subnormals, are covered by the seeded probes of
+    test_encoder_fp32_patterns.  The oracle runs in spawned worker processes
+    (numpy only) while the GPU encodes the same chunks."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import os
+
+    from tests.encode_sweep_worker import encode_bits
+
+    tab = O.decode_table(fmt)
+    fin = np.abs(tab[np.isfinite(tab)])
+    lo = _f32_bits(float(np.min(fin[fin > 0])) / 2)
+    hi = _f32_bits(float(np.max(fin)) * 2)
+    chunk = 1 << 24
+    jobs = [(a, min(chunk, hi + 1 - a), neg) for neg in (False, True)
+            for a in range(lo, hi + 1, chunk)]
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with cf.ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as pool:
+        futs = [pool.submit(encode_bits, a, n, neg, fmt) for a, n, neg in jobs]
+        for (a, n, neg), fut in zip(jobs, futs):
+            bits = torch.arange(a, a + n, dtype=torch.int64, device=DEV)
+            if neg:
+                bits -= 1 << 31  # int32 value whose bit pattern is that of a | 0x80000000
+            x = bits.to(torch.int32).view(torch.float32)
+            q, s, _ = _quant_gpu(x, fmt, _unit_ring())
+            assert s == 1.0
+            ref = fut.result()
+            bad = np.nonzero(q != ref)[0]
+            assert bad.size == 0, [(hex(a + int(i)), neg, hex(int(ref[i])), hex(int(q[i])))
+                                   for i in bad[:8]]
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n", [0, 1, 15, 16, 17, 4095, 4096, 4097, 1_000_003, 9 * 2 ** 20])
