@@ -298,6 +298,33 @@ int fp8_linear_bwd_dw(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t 
                       fp8_ring_t* ring_g, fp8_operand_t x8, void* dw, void* db, float* db_ws,
                       uint8_t* g8_out, float* sg_used, float* amax_g, hipStream_t stream);
 
+/* Bytes of the device array fp8_linear_bwd_dw_noalloc keeps per GPU. */
+#define FP8_NOALLOC_WS_MAX (8 << 20)
+
+/*
+ * fp8_linear_bwd_dw for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, results and kernels without db_ws.  The
+ * db column partials live in a static device array of FP8_NOALLOC_WS_MAX
+ * bytes (8 MiB) that the library holds on each GPU it runs on until the
+ * process ends; this entry point calls no hipMalloc, hipFree or allocating
+ * routine.  The array's device address is looked up once per GPU on the
+ * first call there (hipGetSymbolAddress, with that GPU current); the stream
+ * must belong to the current device.
+ *
+ *   all arguments   as fp8_linear_bwd_dw.
+ * The partials a call writes are all read by that call, so the array needs
+ * no clearing; every call on one GPU shares it, so two calls that may
+ * overlap on one GPU (two streams, or two host threads) race on it and must
+ * be ordered by the caller.
+ * Errors: as fp8_linear_bwd_dw; FP8_ERR_SHAPE when db is wanted and
+ * fp8_db_workspace_bytes(M, N) exceeds FP8_NOALLOC_WS_MAX; FP8_ERR_HIP when
+ * the array's address cannot be looked up (nothing is enqueued then).
+ */
+int fp8_linear_bwd_dw_noalloc(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
+                              fp8_ring_t* ring_g, fp8_operand_t x8, void* dw, void* db,
+                              uint8_t* g8_out, float* sg_used, float* amax_g, hipStream_t stream);
+
 /*
  * Both gradients of one linear from one quantized G, the weight gradient on
  * a second stream ([P3] entries on the backward's bf16 grad outputs and on

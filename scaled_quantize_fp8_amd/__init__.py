@@ -33,6 +33,7 @@ C_SYMBOLS = (
     "fp8_abi_version", "fp8_source_hash", "fp8_status_str", "fp8_ring_bytes", "fp8_ring_init", "fp8_quantize",
     "fp8_quantize_pair", "fp8_linear_fwd", "fp8_linear_bwd_dx", "fp8_db_workspace_bytes",
     "fp8_linear_bwd_dw", "fp8_gemm", "fp8_quantize_2d", "fp8_gemm_fp8out", "fp8_linear_bwd",
+    "fp8_linear_bwd_dw_noalloc",
 )
 
 
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
                                      vp, vp]
         L.fp8_linear_bwd_dx.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp]
         L.fp8_linear_bwd_dw.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp, vp, vp]
+        L.fp8_linear_bwd_dw_noalloc.argtypes = [i64, i64, i64, op, i32, rp, op, vp, vp, vp, vp, vp,
+                                                vp]
         L.fp8_linear_bwd.argtypes = [i64, i64, i64, op, i32, rp, op, op, vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp]
         L.fp8_quantize_2d.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, rp, vp, vp, vp]
@@ -87,7 +90,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_gemm_fp8out.argtypes = [i64, i64, i64, op, op, op, i32, rp, vp, vp, vp, vp]
         for name in ("fp8_ring_init", "fp8_quantize", "fp8_quantize_pair", "fp8_quantize_2d",
                      "fp8_linear_fwd", "fp8_gemm", "fp8_linear_bwd_dx",
-                     "fp8_linear_bwd_dw", "fp8_gemm_fp8out", "fp8_linear_bwd"):
+                     "fp8_linear_bwd_dw", "fp8_gemm_fp8out", "fp8_linear_bwd",
+                     "fp8_linear_bwd_dw_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -418,6 +422,27 @@ def bind_fp8_linear_bwd_dw(g, fmt_g, x8, dw, db=None, db_ws=None, ring_g=None, g
                            sg_used=None, amax_g=None, stream=None):
     return _bind("fp8_linear_bwd_dw", _dw_args(g, fmt_g, x8, dw, db, db_ws, ring_g, g8_out,
                                                sg_used, amax_g, stream))
+
+
+def _dw_noalloc_args(g, fmt_g, x8, dw, db, ring_g, g8_out, sg_used, amax_g, stream):
+    args = _dw_args(g, fmt_g, x8, dw, db, None, ring_g, g8_out, sg_used, amax_g, stream)
+    return args[:9] + args[10:]  # the same arguments without db_ws
+
+
+def fp8_linear_bwd_dw_noalloc(g, fmt_g, x8, dw, db=None, ring_g=None, g8_out=None, sg_used=None,
+                              amax_g=None, stream=None):
+    """fp8_linear_bwd_dw without a workspace: the db partials live in the
+    library's static per-GPU array (no allocation; calls that overlap on one
+    GPU race on it)."""
+    _check(lib().fp8_linear_bwd_dw_noalloc(*_dw_noalloc_args(g, fmt_g, x8, dw, db, ring_g, g8_out,
+                                                             sg_used, amax_g, stream)),
+           "fp8_linear_bwd_dw_noalloc")
+
+
+def bind_fp8_linear_bwd_dw_noalloc(g, fmt_g, x8, dw, db=None, ring_g=None, g8_out=None,
+                                   sg_used=None, amax_g=None, stream=None):
+    return _bind("fp8_linear_bwd_dw_noalloc", _dw_noalloc_args(g, fmt_g, x8, dw, db, ring_g,
+                                                               g8_out, sg_used, amax_g, stream))
 
 
 def _bwd_args(g, fmt_g, x8, w8, dx, dw, db, db_ws, ring_g, g8_out, sg_used, amax_g, stream,

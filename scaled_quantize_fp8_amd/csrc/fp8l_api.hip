@@ -446,6 +446,32 @@ void finish_gemm_args(GemmArgs& g) {
 int hip_status() { return hipGetLastError() == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
 
 }  // namespace
+
+// Library-owned device memory of fp8_linear_bwd_dw_noalloc: the db column
+// partials, FP8_NOALLOC_WS_MAX bytes, one copy per GPU for the life of the
+// process.  Host code never uses the array's name as an address (on the host
+// it is only a stand-in); it uses the address hipGetSymbolAddress returns on
+// each device, kept in scratch_dev.
+__device__ __align__(256) float scratch[FP8_NOALLOC_WS_MAX / 4];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64];
+
+// Device address of this GPU's scratch array (the current device's), looked
+// up once per device with that device current.  nullptr if the lookup fails.
+float* scratch_dev() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_dev[dev] = p;
+  }
+  return reinterpret_cast<float*>(g_scratch_dev[dev]);
+}
+}  // namespace
 }  // namespace fp8l
 
 using namespace fp8l;
@@ -802,6 +828,32 @@ int fp8_linear_bwd_dw(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t 
               stream, &g8, &sg, &pre);
   if (want_db && pre) enqueue_db_colsum_pre(M, N, g8, fmt_g, db_ws, stream);
   enqueue_dw_gemm(M, N, K, g8, sg, fmt_g, x8, dw, db, db_ws, pre, true, g.scale, sg_used, amax_g,
+                  stream);
+  return hip_status();
+}
+
+int fp8_linear_bwd_dw_noalloc(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt_g,
+                              fp8_ring_t* ring_g, fp8_operand_t x8, void* dw, void* db,
+                              uint8_t* g8_out, float* sg_used, float* amax_g, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return FP8_ERR_SHAPE;
+  if (!mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N)) return FP8_ERR_SHAPE;
+  const bool want_db = db != nullptr && M > 0;
+  if (want_db && fp8_db_workspace_bytes(M, N) > (size_t)FP8_NOALLOC_WS_MAX) return FP8_ERR_SHAPE;
+  const uint8_t* g8 = nullptr;
+  const float* sg = nullptr;
+  bool pre = false;
+  int st = bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, true, nullptr, stream, &g8,
+                       &sg, &pre);
+  if (st) return st;
+  float* ws = nullptr;
+  if (want_db && !(ws = scratch_dev())) return FP8_ERR_HIP;
+  if ((st = check_dw_operands(M, N, K, x8, dw, db, ws))) return st;
+  // from here on exactly fp8_linear_bwd_dw with ws as its workspace
+  ColsumSpec cs = {M, N, ws};
+  bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, want_db ? &cs : nullptr,
+              stream, &g8, &sg, &pre);
+  if (want_db && pre) enqueue_db_colsum_pre(M, N, g8, fmt_g, ws, stream);
+  enqueue_dw_gemm(M, N, K, g8, sg, fmt_g, x8, dw, db, ws, pre, true, g.scale, sg_used, amax_g,
                   stream);
   return hip_status();
 }
