@@ -130,7 +130,7 @@ void launch_convert(const QArgs& a, const ColsumSpec* cs, hipStream_t st) {
 
 template <int IN, int FMT>
 void enqueue_quant_t(const void* x, int64_t n, uint8_t* q, fp8_ring_t* ring, float* scale_used,
-                     float* amax_out, const ColsumSpec* cs, hipStream_t st) {
+                     float* amax_out, const ColsumSpec* cs, hipStream_t st, bool defer) {
   QArgs a = {};
   a.x = x;
   a.q = q;
@@ -151,7 +151,9 @@ void enqueue_quant_t(const void* x, int64_t n, uint8_t* q, fp8_ring_t* ring, flo
     a.ring = reinterpret_cast<RingHdr*>(ring->dev);
     a.hist = reinterpret_cast<float*>(reinterpret_cast<char*>(ring->dev) + sizeof(RingHdr));
     a.hist_len = ring->hist_len;
-    if (ring->seeded) {
+    if (ring->seeded && defer) {
+      launch_convert<IN, FMT, kScaleDefer>(a, cs, st);  // the consuming GEMM folds
+    } else if (ring->seeded) {
       launch_convert<IN, FMT, kScaleRing>(a, cs, st);
     } else {
       // first use: the amax pass leaves max |x| in the ring header, the
@@ -175,7 +177,7 @@ void enqueue_quant_t(const void* x, int64_t n, uint8_t* q, fp8_ring_t* ring, flo
 template <int IN, int FMT>
 void enqueue_quant2_t(const void* x0, int64_t n0, uint8_t* q0, fp8_ring_t* r0, float* su0,
                       float* am0, const void* x1, int64_t n1, uint8_t* q1, fp8_ring_t* r1,
-                      float* su1, float* am1, hipStream_t st) {
+                      float* su1, float* am1, hipStream_t st, bool defer) {
   auto args = [](const void* x, int64_t n, uint8_t* q, fp8_ring_t* r, float* su, float* am) {
     QArgs a = {};
     a.x = x;
@@ -197,57 +199,89 @@ void enqueue_quant2_t(const void* x0, int64_t n0, uint8_t* q0, fp8_ring_t* r0, f
     b0 = b0 < 1 ? 1 : (b0 > cap - 1 ? cap - 1 : b0);
     b1 = cap - b0;
   }
-  hipLaunchKernelGGL((quantize_flat2_kernel<IN, FMT>), dim3((unsigned)(b0 + b1)), dim3(kQThreads),
-                     0, st, a0, a1, (uint32_t)b0);
+  if (defer)
+    hipLaunchKernelGGL((quantize_flat2_kernel<IN, FMT, kScaleDefer>), dim3((unsigned)(b0 + b1)),
+                       dim3(kQThreads), 0, st, a0, a1, (uint32_t)b0);
+  else
+    hipLaunchKernelGGL((quantize_flat2_kernel<IN, FMT, kScaleRing>), dim3((unsigned)(b0 + b1)),
+                       dim3(kQThreads), 0, st, a0, a1, (uint32_t)b0);
 }
 
 template <int IN>
 void enqueue_quant2_in(int32_t fmt, const void* x0, int64_t n0, uint8_t* q0, fp8_ring_t* r0,
                        float* su0, float* am0, const void* x1, int64_t n1, uint8_t* q1,
-                       fp8_ring_t* r1, float* su1, float* am1, hipStream_t st) {
+                       fp8_ring_t* r1, float* su1, float* am1, hipStream_t st, bool defer) {
   if (fmt == FP8_E4M3)
-    enqueue_quant2_t<IN, kE4M3>(x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st);
+    enqueue_quant2_t<IN, kE4M3>(x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st, defer);
   else
-    enqueue_quant2_t<IN, kE5M2>(x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st);
+    enqueue_quant2_t<IN, kE5M2>(x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st, defer);
 }
 
 template <int IN>
 void enqueue_quant_in(const void* x, int64_t n, int32_t fmt, uint8_t* q, fp8_ring_t* ring,
-                      float* scale_used, float* amax_out, const ColsumSpec* cs, hipStream_t st) {
+                      float* scale_used, float* amax_out, const ColsumSpec* cs, hipStream_t st,
+                      bool defer) {
   if (fmt == FP8_E4M3)
-    enqueue_quant_t<IN, kE4M3>(x, n, q, ring, scale_used, amax_out, cs, st);
+    enqueue_quant_t<IN, kE4M3>(x, n, q, ring, scale_used, amax_out, cs, st, defer);
   else
-    enqueue_quant_t<IN, kE5M2>(x, n, q, ring, scale_used, amax_out, cs, st);
+    enqueue_quant_t<IN, kE5M2>(x, n, q, ring, scale_used, amax_out, cs, st, defer);
 }
 
-void enqueue_quant(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, uint8_t* q,
+// A quantize through this ring may leave its fold to the GEMM that consumes
+// the codes: the ring is seeded (one converting launch, no seeding pass) and
+// its window fits the one wave that folds it.
+bool can_defer(const fp8_ring_t* r) { return r && r->seeded && r->hist_len <= 64; }
+
+// The fold the consuming GEMM does for a deferred quantize through r.
+RingFold fold_of(const fp8_ring_t* r, int32_t fmt, float* amax_out) {
+  RingFold f = {};
+  f.ring = reinterpret_cast<RingHdr*>(r->dev);
+  f.hist = reinterpret_cast<float*>(reinterpret_cast<char*>(r->dev) + sizeof(RingHdr));
+  f.hist_len = r->hist_len;
+  f.fmt_max = fmt == FP8_E4M3 ? FmtTraits<kE4M3>::kMax : FmtTraits<kE5M2>::kMax;
+  f.amax_out = amax_out;
+  return f;
+}
+
+// One quantize.  may_defer: the caller launches a GEMM on the codes next,
+// on the same stream, which folds the ring when this returns true.
+bool enqueue_quant(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, uint8_t* q,
                    fp8_ring_t* ring, float* scale_used, float* amax_out, const ColsumSpec* cs,
-                   hipStream_t st) {
+                   hipStream_t st, bool may_defer = false) {
+  const bool defer = may_defer && can_defer(ring);
   if (in_dtype == FP8_DT_F32)
-    enqueue_quant_in<kInF32>(x, n, fmt, q, ring, scale_used, amax_out, cs, st);
+    enqueue_quant_in<kInF32>(x, n, fmt, q, ring, scale_used, amax_out, cs, st, defer);
   else if (in_dtype == FP8_DT_F16)
-    enqueue_quant_in<kInF16>(x, n, fmt, q, ring, scale_used, amax_out, cs, st);
+    enqueue_quant_in<kInF16>(x, n, fmt, q, ring, scale_used, amax_out, cs, st, defer);
   else
-    enqueue_quant_in<kInBF16>(x, n, fmt, q, ring, scale_used, amax_out, cs, st);
+    enqueue_quant_in<kInBF16>(x, n, fmt, q, ring, scale_used, amax_out, cs, st, defer);
+  return defer;
 }
 
 // Two quantizes: one launch when the input types match and both rings are
 // seeded (the steady state of delayed scaling), else one after the other.
+// may_defer as enqueue_quant; *d0 / *d1 say which folds were left.
 void enqueue_quant_pair(const void* x0, int32_t dt0, int64_t n0, uint8_t* q0, fp8_ring_t* r0,
                         float* su0, float* am0, const void* x1, int32_t dt1, int64_t n1,
                         uint8_t* q1, fp8_ring_t* r1, float* su1, float* am1, int32_t fmt,
-                        hipStream_t st) {
+                        hipStream_t st, bool may_defer = false, bool* d0 = nullptr,
+                        bool* d1 = nullptr) {
   const bool one = dt0 == dt1 && r0 && r1 && r0->seeded && r1->seeded && n0 > 0 && n1 > 0;
+  bool f0 = false, f1 = false;
   if (!one) {
-    enqueue_quant(x0, dt0, n0, fmt, q0, r0, su0, am0, nullptr, st);
-    enqueue_quant(x1, dt1, n1, fmt, q1, r1, su1, am1, nullptr, st);
-  } else if (dt0 == FP8_DT_F32) {
-    enqueue_quant2_in<kInF32>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st);
-  } else if (dt0 == FP8_DT_F16) {
-    enqueue_quant2_in<kInF16>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st);
+    f0 = enqueue_quant(x0, dt0, n0, fmt, q0, r0, su0, am0, nullptr, st, may_defer);
+    f1 = enqueue_quant(x1, dt1, n1, fmt, q1, r1, su1, am1, nullptr, st, may_defer);
   } else {
-    enqueue_quant2_in<kInBF16>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st);
+    f0 = f1 = may_defer && can_defer(r0) && can_defer(r1);
+    if (dt0 == FP8_DT_F32)
+      enqueue_quant2_in<kInF32>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st, f0);
+    else if (dt0 == FP8_DT_F16)
+      enqueue_quant2_in<kInF16>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st, f0);
+    else
+      enqueue_quant2_in<kInBF16>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st, f0);
   }
+  if (d0) *d0 = f0;
+  if (d1) *d1 = f1;
 }
 
 template <int LA, int LB, int FA, int FB>
@@ -613,14 +647,18 @@ int fp8_linear_fwd(int64_t M, int64_t N, int64_t K, fp8_operand_t x, fp8_operand
   }
   if (M * N > 0 && !y) return FP8_ERR_NULL;
 
+  // The quantizes leave their ring folds to the GEMM below (same stream),
+  // which folds them in its first block before any operand load.
   GemmArgs g = {};
+  bool fold_x = false, fold_w = false;
   if (is_hp(x.dtype) && is_hp(w.dtype))
     enqueue_quant_pair(x.data, x.dtype, M * K, x8_out, ring_x, sx_used, amax_x, w.data, w.dtype,
-                       N * K, w8_out, ring_w, sw_used, amax_w, fmt, stream);
+                       N * K, w8_out, ring_w, sw_used, amax_w, fmt, stream, true, &fold_x, &fold_w);
   const bool pair = is_hp(x.dtype) && is_hp(w.dtype);
   if (is_hp(x.dtype)) {
     if (!pair)
-      enqueue_quant(x.data, x.dtype, M * K, fmt, x8_out, ring_x, sx_used, amax_x, nullptr, stream);
+      fold_x = enqueue_quant(x.data, x.dtype, M * K, fmt, x8_out, ring_x, sx_used, amax_x, nullptr,
+                             stream, true);
     g.a = x8_out;
     g.scale_a = sx_used;
   } else {
@@ -632,7 +670,8 @@ int fp8_linear_fwd(int64_t M, int64_t N, int64_t K, fp8_operand_t x, fp8_operand
   }
   if (is_hp(w.dtype)) {
     if (!pair)
-      enqueue_quant(w.data, w.dtype, N * K, fmt, w8_out, ring_w, sw_used, amax_w, nullptr, stream);
+      fold_w = enqueue_quant(w.data, w.dtype, N * K, fmt, w8_out, ring_w, sw_used, amax_w, nullptr,
+                             stream, true);
     g.b = w8_out;
     g.scale_b = sw_used;
   } else {
@@ -652,6 +691,8 @@ int fp8_linear_fwd(int64_t M, int64_t N, int64_t K, fp8_operand_t x, fp8_operand
   g.bias = bias.data;
   g.bias_kind = bias_kind;
   g.bias_scale = bias.scale;
+  if (fold_x) g.fold[0] = fold_of(ring_x, fmt, amax_x);
+  if (fold_w) g.fold[1] = fold_of(ring_w, fmt, amax_w);
   finish_gemm_args(g);
   launch_gemm_l<kKContig, kKContig>(g, fmt, fmt, stream);
   return hip_status();
@@ -660,15 +701,20 @@ int fp8_linear_fwd(int64_t M, int64_t N, int64_t K, fp8_operand_t x, fp8_operand
 // Shared front half of the two backward entry points: validate g and
 // enqueue its quantize if it is high precision.  Outputs the fp8 pointer
 // and scale pointer the GEMM uses.
+// fold: when not null, the quantize may leave its ring fold to the GEMM the
+// caller launches next on the same stream, and *fold receives that fold
+// (ring null if the quantize folded in its own launch).
 static int bwd_prepare(int64_t M, int64_t N, fp8_operand_t g, int32_t fmt_g, fp8_ring_t* ring_g,
                        uint8_t* g8_out, float* sg_used, float* amax_g, bool validate_only,
                        const ColsumSpec* cs, hipStream_t stream, const uint8_t** g8,
-                       const float** sg, bool* pre) {
+                       const float** sg, bool* pre, RingFold* fold = nullptr) {
   if (!valid_fmt(fmt_g)) return FP8_ERR_DTYPE;
   if (is_hp(g.dtype)) {
     if (validate_only)
       return check_quant(g.data, g.dtype, M * N, fmt_g, g8_out, ring_g, sg_used, amax_g, stream);
-    enqueue_quant(g.data, g.dtype, M * N, fmt_g, g8_out, ring_g, sg_used, amax_g, cs, stream);
+    if (enqueue_quant(g.data, g.dtype, M * N, fmt_g, g8_out, ring_g, sg_used, amax_g, cs, stream,
+                      fold != nullptr))
+      *fold = fold_of(ring_g, fmt_g, amax_g);
     *g8 = g8_out;
     *sg = sg_used;
     *pre = false;
@@ -688,8 +734,10 @@ static int bwd_prepare(int64_t M, int64_t N, fp8_operand_t g, int32_t fmt_g, fp8
 // sg_used and clears amax_g.
 static void enqueue_dx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* g8, const float* sg,
                             int32_t fmt_g, fp8_operand_t w8, void* dx, bool pre, const float* g_scale,
-                            float* sg_used, float* amax_g, hipStream_t stream) {
+                            float* sg_used, float* amax_g, hipStream_t stream,
+                            const RingFold& fold = RingFold{}) {
   GemmArgs a = {};
+  a.fold[0] = fold;
   a.a = g8;  // [M, N], contraction n contiguous
   a.lda = N;
   a.b = reinterpret_cast<const uint8_t*>(w8.data);  // [N, K] read crosswise
@@ -729,8 +777,9 @@ static void enqueue_db_colsum_pre(int64_t M, int64_t N, const uint8_t* g8, int32
 static void enqueue_dw_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* g8, const float* sg,
                             int32_t fmt_g, fp8_operand_t x8, void* dw, void* db, float* db_ws,
                             bool pre, bool aux, const float* g_scale, float* sg_used,
-                            float* amax_g, hipStream_t stream) {
+                            float* amax_g, hipStream_t stream, const RingFold& fold = RingFold{}) {
   GemmArgs a = {};
+  a.fold[0] = fold;
   a.a = g8;  // G8 [M, N] as A(i = n, k = m): crosswise
   a.lda = N;
   a.b = reinterpret_cast<const uint8_t*>(x8.data);  // X8 [M, K] as B(j = k, k = m): crosswise
@@ -804,8 +853,10 @@ int fp8_linear_bwd_dx(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t 
                        &sg, &pre);
   if (st) return st;
   if ((st = check_dx_operands(M, N, K, w8, dx))) return st;
-  bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, nullptr, stream, &g8, &sg, &pre);
-  enqueue_dx_gemm(M, N, K, g8, sg, fmt_g, w8, dx, pre, g.scale, sg_used, amax_g, stream);
+  RingFold fold = {};
+  bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, nullptr, stream, &g8, &sg, &pre,
+              &fold);
+  enqueue_dx_gemm(M, N, K, g8, sg, fmt_g, w8, dx, pre, g.scale, sg_used, amax_g, stream, fold);
   return hip_status();
 }
 
@@ -824,11 +875,12 @@ int fp8_linear_bwd_dw(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t 
 
   ColsumSpec cs = {M, N, db_ws};
   const bool want_db = db != nullptr && M > 0;
+  RingFold fold = {};
   bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, want_db ? &cs : nullptr,
-              stream, &g8, &sg, &pre);
+              stream, &g8, &sg, &pre, &fold);
   if (want_db && pre) enqueue_db_colsum_pre(M, N, g8, fmt_g, db_ws, stream);
   enqueue_dw_gemm(M, N, K, g8, sg, fmt_g, x8, dw, db, db_ws, pre, true, g.scale, sg_used, amax_g,
-                  stream);
+                  stream, fold);
   return hip_status();
 }
 
@@ -850,11 +902,12 @@ int fp8_linear_bwd_dw_noalloc(int64_t M, int64_t N, int64_t K, fp8_operand_t g, 
   if ((st = check_dw_operands(M, N, K, x8, dw, db, ws))) return st;
   // from here on exactly fp8_linear_bwd_dw with ws as its workspace
   ColsumSpec cs = {M, N, ws};
+  RingFold fold = {};
   bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, want_db ? &cs : nullptr,
-              stream, &g8, &sg, &pre);
+              stream, &g8, &sg, &pre, &fold);
   if (want_db && pre) enqueue_db_colsum_pre(M, N, g8, fmt_g, ws, stream);
   enqueue_dw_gemm(M, N, K, g8, sg, fmt_g, x8, dw, db, ws, pre, true, g.scale, sg_used, amax_g,
-                  stream);
+                  stream, fold);
   return hip_status();
 }
 
@@ -875,8 +928,9 @@ int fp8_linear_bwd(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt
 
   ColsumSpec cs = {M, N, db_ws};
   const bool want_db = db != nullptr && M > 0;
+  RingFold fold = {};  // left to the dX GEMM, which runs on stream after the quantize
   bwd_prepare(M, N, g, fmt_g, ring_g, g8_out, sg_used, amax_g, false, want_db ? &cs : nullptr,
-              stream, &g8, &sg, &pre);
+              stream, &g8, &sg, &pre, &fold);
   if (want_db && pre) enqueue_db_colsum_pre(M, N, g8, fmt_g, db_ws, stream);
   if ((st = hip_status())) return st;
   if (stream_dw != stream && (st = fork_after(stream, stream_dw))) return st;
@@ -884,7 +938,7 @@ int fp8_linear_bwd(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt
   // g's own scale, so the two streams touch no common output
   enqueue_dw_gemm(M, N, K, g8, sg, fmt_g, x8, dw, db, db_ws, pre, false, g.scale, sg_used, amax_g,
                   stream_dw);
-  enqueue_dx_gemm(M, N, K, g8, sg, fmt_g, w8, dx, pre, g.scale, sg_used, amax_g, stream);
+  enqueue_dx_gemm(M, N, K, g8, sg, fmt_g, w8, dx, pre, g.scale, sg_used, amax_g, stream, fold);
   return hip_status();
 }
 

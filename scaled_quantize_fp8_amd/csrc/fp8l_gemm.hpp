@@ -43,6 +43,17 @@ constexpr int kTileBytes = 128 * 128;
 enum { kKContig = 0, kCross = 1 };
 enum { kBiasNone = 0, kBiasBF16 = 1, kBiasE4M3 = 2, kBiasE5M2 = 3 };
 
+// The ring fold of a quantize launch that ran in kScaleDefer mode (its
+// blocks left their maxima in the ring's election groups), done by the GEMM
+// that consumes the codes.  ring null: nothing to fold.
+struct RingFold {
+  RingHdr* ring;
+  float* hist;
+  int32_t hist_len;  // 1..64: one window slot per lane of the folding wave
+  float fmt_max;
+  float* amax_out;   // optional
+};
+
 struct GemmArgs {
   const uint8_t* a;
   int64_t lda;
@@ -82,7 +93,42 @@ struct GemmArgs {
   int32_t ohist_len;
   float* oscale_used;
   float* oamax;
+  // ring folds left by the quantizes of this GEMM's operands (block 0)
+  RingFold fold[2];
 };
+
+// The fold of one ring by one full wave: take the 64 group maxima (leaving
+// zeros), fold the launch amax into hist[idx], advance idx, publish
+// S(window max), mark the ring seeded, write amax_out.  The quantize launch
+// ran before this kernel on the same stream and has completed, so every
+// group max is in place; nothing else touches the ring while this kernel
+// runs.  The loads and the atomic exchange are waited for here, before the
+// caller issues any operand load.
+FP8L_DEV void ring_fold_wave(const RingFold& f) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t gm = atom_xchg(&f.ring->group[lane].amax, 0u);
+  const uint32_t H = (uint32_t)f.hist_len;
+  const uint32_t hv = (uint32_t)lane < H ? __float_as_uint(f.hist[lane]) : 0u;
+  const uint32_t idx = f.ring->idx % H;  // in range even for a corrupted header
+  const float prev = f.ring->scale;
+  const uint32_t amax = wave_max_u32(gm);
+  const uint32_t m = wave_max_u32((uint32_t)lane == idx ? amax : hv);
+  if (lane == 0) {
+    f.hist[idx] = __uint_as_float(amax);
+    f.ring->idx = idx + 1 == H ? 0u : idx + 1;
+    f.ring->scale = scale_from_amax(__uint_as_float(m), f.fmt_max, prev);
+    f.ring->seeded = 1u;
+    if (f.amax_out) *f.amax_out = __uint_as_float(amax);
+  }
+}
+
+// Block (0, 0)'s wave 0 folds the rings before its first operand load (one
+// device round trip on one wave of one block).
+FP8L_DEV void ring_folds(const GemmArgs& g) {
+  if (blockIdx.x != 0 || blockIdx.y != 0 || (threadIdx.x >> 6) != 0) return;
+  if (g.fold[0].ring) ring_fold_wave(g.fold[0]);
+  if (g.fold[1].ring) ring_fold_wave(g.fold[1]);
+}
 
 // Move the operand pointers to this block's batch slice (blockIdx.y).
 FP8L_DEV void batch_slice(GemmArgs& g) {
@@ -247,6 +293,7 @@ FP8L_DEV void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
 template <int LA, int LB, int FA, int FB>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_kernel(GemmArgs g) {
   batch_slice(g);
+  ring_folds(g);  // before any operand load of this block
   __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][kTileBytes];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;

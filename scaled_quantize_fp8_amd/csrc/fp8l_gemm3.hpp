@@ -655,6 +655,7 @@ template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB, int 
 __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN <= 128 * 128) ? 2 : 1)
 void gemm3_kernel(GemmArgs g) {
   batch_slice(g);
+  ring_folds(g);  // before any operand load of this block
   constexpr int NW = WGM * WGN;
   using OA = Op3<LA, BM, NW>;
   using OB = Op3<LB, BN, NW>;

@@ -31,7 +31,12 @@
 
 namespace fp8l {
 
-enum { kScaleRing = 0, kScaleSeed = 1, kScaleDyn = 2 };
+// Scale modes of a converting launch: the ring's scale with the ring fold
+// in the last block (Ring); the seed from the amax pass, then the fold
+// (Seed); dynamic, from the amax pass (Dyn); the ring's scale with the fold
+// left to the launch that consumes the codes (Defer: each block only folds
+// its max into its election group; see finish_launch and RingFold).
+enum { kScaleRing = 0, kScaleSeed = 1, kScaleDyn = 2, kScaleDefer = 3 };
 
 constexpr int kQThreads = 256;
 constexpr int kWaveChunk = 1024;            // elements per wave per step (flat kernel)
@@ -228,7 +233,7 @@ FP8L_DEV void amax_pass_finish(RingHdr* h, uint32_t mx, uint32_t bid, uint32_t t
 template <int FMT, int SMODE>
 FP8L_DEV float launch_scale(const QArgs& a) {
   constexpr float M = FmtTraits<FMT>::kMax;
-  if constexpr (SMODE == kScaleRing) {
+  if constexpr (SMODE == kScaleRing || SMODE == kScaleDefer) {
     return a.ring->scale;
   } else if constexpr (SMODE == kScaleSeed) {
     // amax left in the header by the amax pass that ran just before
@@ -252,6 +257,18 @@ FP8L_DEV void finish_launch(const QArgs& a, uint32_t mx, float s, uint32_t bid, 
   __shared__ uint32_t sh_flag;
   if constexpr (SMODE == kScaleDyn) {
     if (bid == 0 && threadIdx.x == 0) *a.scale_used = s;
+    return;
+  } else if constexpr (SMODE == kScaleDefer) {
+    // No election: the block's max goes into its group (no return value
+    // is awaited, so nothing here waits on a device round trip), and the
+    // launch that consumes the codes folds the groups into the ring when
+    // it starts (RingFold).  Block 0 writes the scale snapshot.
+    const uint32_t bm = block_max_u32<NT>(mx, sh4);
+    if (threadIdx.x == 0) {
+      if (bid == 0) *a.scale_used = s;
+      const uint32_t G = total < (uint32_t)kGroups ? total : (uint32_t)kGroups;
+      if (bm) atom_max(&a.ring->group[bid % G].amax, bm);
+    }
     return;
   } else {
     const uint32_t bm = block_max_u32<NT>(mx, sh4);
@@ -337,13 +354,13 @@ __global__ __launch_bounds__(kQThreads) void quantize_flat_kernel(QArgs a) {
 // in one launch: blocks [0, nblk0) quantize a0, the rest a1.  The forward of
 // a linear layer quantizes X and W this way, so that one tensor's fixed
 // latency (first loads, the election chain) overlaps the other's.
-template <int IN, int FMT>
+template <int IN, int FMT, int SMODE>
 __global__ __launch_bounds__(kQThreads) void quantize_flat2_kernel(QArgs a0, QArgs a1,
                                                                    uint32_t nblk0) {
   if (blockIdx.x < nblk0)
-    quantize_flat_body<IN, FMT, kScaleRing>(a0, blockIdx.x, nblk0);
+    quantize_flat_body<IN, FMT, SMODE>(a0, blockIdx.x, nblk0);
   else
-    quantize_flat_body<IN, FMT, kScaleRing>(a1, blockIdx.x - nblk0, gridDim.x - nblk0);
+    quantize_flat_body<IN, FMT, SMODE>(a1, blockIdx.x - nblk0, gridDim.x - nblk0);
 }
 
 // Quantize x [rows, cols] into q [rows, cols] and/or its transpose

@@ -120,15 +120,15 @@ def test_traffic_record_quant_and_missing_kernel(tmp_path):
 
 
 def test_layer_step_order_forwards_then_backwards_then_join():
-    """The step issues every forward (quantize launch, then GEMM) in order,
-    then every backward in reverse order, then makes the main stream wait for
-    the dW stream; the launch hook sees each GEMM call with its kind."""
+    """The step issues every forward (one fp8_linear_fwd call: quantize, then
+    the GEMM that folds the rings) in order, then every backward in reverse
+    order, then makes the main stream wait for the dW stream; the launch hook
+    sees each call with its kind."""
     log = []
 
     class FakeLayer:
         def __init__(self, i):
-            self.quant_xw = lambda: log.append(("q", i))
-            self.gemm_fwd = lambda: log.append(("fwd", i))
+            self.fwd = lambda: log.append(("fwd", i))
             self.bwd = lambda: log.append(("bwd", i))
 
     class FakeStream:
@@ -139,7 +139,7 @@ def test_layer_step_order_forwards_then_backwards_then_join():
     layers = [FakeLayer(i) for i in range(3)]
     step = bench.layer_step(layers, main, side)
     step()
-    assert log == [("q", 0), ("fwd", 0), ("q", 1), ("fwd", 1), ("q", 2), ("fwd", 2),
+    assert log == [("fwd", 0), ("fwd", 1), ("fwd", 2),
                    ("bwd", 2), ("bwd", 1), ("bwd", 0), ("join", "side")]
     log.clear()
     seen = []
