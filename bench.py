@@ -56,7 +56,10 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="dim1536_m2048")
-    p.add_argument("--kernel-reps", type=int, default=20, help="repeats of each isolated kernel timing")
+    p.add_argument("--kernel-reps", type=int, default=200,
+                   help="timed launches of each isolated kernel timing (in batches of 20)")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the MFMA-only and HBM-stream probes")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-other-configs", action="store_true",
                    help="skip the other workloads' steps")
@@ -72,6 +75,10 @@ def parse():
                    help="no GPU: turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of "
                         "'--only KIND' and '--only copy' runs into the HBM-traffic record that "
                         "the roofline entry reads, and exit")
+    p.add_argument("--trace-from", default=None, metavar="KERNEL_TRACE_CSV",
+                   help="no GPU: turn the rocprofv3 --kernel-trace CSV of a profiled run of this "
+                        "benchmark into the per-kind GEMM duration record under profiles/, and "
+                        "exit")
     p.add_argument("--mfma-from", default=None, metavar="MFMAUTIL_CSV",
                    help="no GPU: turn a rocprofv3 --pmc MfmaUtil CSV of an '--only gemm' run "
                         "into the per-kind MFMA-utilisation record under profiles/, and exit")
@@ -199,6 +206,38 @@ def event_time_ms(torch, fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
+def _pct(vals, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(vals, dtype=np.float64), q))
+
+
+def batched_stats_us(torch, fns, stream, reps=200, warm=20, batch=20):
+    """Per-launch device time in µs: `warm` untimed launches, then `reps`
+    launches in batches of `batch` back-to-back launches, each batch inside
+    one event pair (all queued behind a GPU sleep, so the device runs them
+    back to back); median, p10 and p90 of the per-launch time over the
+    batches.  fns: one callable, or a list the launches cycle through."""
+    fns = fns if isinstance(fns, (list, tuple)) else [fns]
+    for i in range(warm):
+        fns[i % len(fns)]()
+    nb = max(1, reps // batch)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nb)]
+    k = 0
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(5_000_000)
+        for a, b in evs:
+            a.record(stream)
+            for _ in range(batch):
+                fns[k % len(fns)]()
+                k += 1
+            b.record(stream)
+    evs[-1][1].synchronize()
+    per = [1e3 * a.elapsed_time(b) / batch for a, b in evs]
+    return {"median": round(_pct(per, 50), 3), "p10": round(_pct(per, 10), 3),
+            "p90": round(_pct(per, 90), 3), "launches": nb * batch}
+
+
 def bracket_overhead_us(torch, fn, reps, stream):
     """How much longer a launch measures when an event pair brackets it on
     its own (as the live roofline figures do) than its share of one pair
@@ -218,9 +257,13 @@ def bracket_overhead_us(torch, fn, reps, stream):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the FP8 path's kernel sources (the measurement probes'
+    source excluded): records taken on other sources are not used."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "scaled_quantize_fp8_amd", "csrc")
     for fn in sorted(os.listdir(csrc)):
+        if fn == "fp8l_probe.hip":
+            continue
         with open(os.path.join(csrc, fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -350,6 +393,57 @@ def mfma_record(csv_path, workload):
             "dispatches": {k: len(v) for k, v in sorted(by.items())}}
 
 
+def trace_record(trace_csv, workload):
+    """Per-kind GEMM durations from the rocprofv3 --kernel-trace CSV of a
+    profiled run of this benchmark (--no-widened --no-other-configs, so
+    every GEMM launch in it is one of this workload's linears, and every
+    linear's GEMM of a kind is launched equally often): launches, average
+    duration, and the frac of the FP8 peak that the average flops per
+    launch over the average duration give."""
+    import csv
+    from scaled_quantize_fp8_amd import workloads as WL
+    wl = WL.WORKLOADS[workload]
+    by = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            kind = gemm_kind_of(r["Kernel_Name"])
+            if kind:
+                by.setdefault(kind, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    if not by:
+        raise SystemExit(f"{trace_csv}: no GEMM dispatch")
+    flops = sum(2.0 * wl.M * L.N * L.K for L in wl.linears) / len(wl.linears)
+    kinds = {}
+    for k, v in sorted(by.items()):
+        avg_us = sum(v) / len(v) / 1e3
+        kinds[k] = {"launches": len(v), "avg_us": round(avg_us, 3),
+                    "frac": round(flops / (avg_us * 1e-6) / 1e12 / MI355X_FP8_DENSE_TFLOPS, 4)}
+    cmds = ["cd /tmp && export TMPDIR=/tmp",
+            "rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_step "
+            "-o step -- python3 $REPO/bench.py --steps 20 --warmup 5 --no-widened "
+            "--no-other-configs --no-cpu-baseline --no-ceilings",
+            f"python3 bench.py --workload {workload} --trace-from "
+            "gpurun_out/prof_step/step_kernel_trace.csv"]
+    return {"workload": workload, "kernel_source_hash": kernel_source_hash(), "commands": cmds,
+            "flops_per_launch_avg": flops, "kinds": kinds}
+
+
+def trace_record_path(workload):
+    return os.path.join(PROFILE_DIR, f"gemm_trace_{workload}.txt")
+
+
+def load_trace_record(kind, workload):
+    """The kind's trace figures from the committed record, or None if absent
+    or taken on different kernel sources."""
+    path = trace_record_path(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec["kinds"].get(kind)
+
+
 def load_mfma(workload):
     """Per-kind MFMA utilisation (percent) from the committed record, or None
     if absent or taken on different kernel sources."""
@@ -394,44 +488,104 @@ def load_traffic(kernel_key: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(layers_cpu, budget_s, min_s=10.0):
-    """The oracle (untuned) on a bounded row sample of the same layer: the
-    quantizes of X/W/G and the three GEMMs per linear.  Rate in TFLOP/s."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_oracle_rate(layers_cpu, budget_s, rows, threads=None, min_s=5.0):
+    """The oracle (untuned) on the host: per linear, the dynamic quantizes of
+    X, W, G and the three GEMMs plus db, on the first `rows` rows of X and
+    G (full W), repeated over the layer's linears until min_s has passed at
+    a layer boundary or budget_s at any linear.  threads: BLAS threads for
+    the oracle's float64 matmuls (None = all).  Rate in TFLOP/s of the
+    GEMMs' 2MNK flops."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import fp8_oracle as O
 
-    rows = layers_cpu[0][0].shape[0]  # every row: full layer steps, repeated to >= min_s
     flops = 0.0
-    t0 = time.perf_counter()
     done = 0
-    order = [layers_cpu[i % len(layers_cpu)] for i in range(64 * len(layers_cpu))]
-    for (X, W, b, G) in order:
-        xs = X[:rows].float().numpy()
-        gs = G[:rows].float().numpy()
-        ws = W.float().numpy()
-        x8, sx, _ = O.quantize_step(xs, O.E4M3, None)
-        w8, sw, _ = O.quantize_step(ws, O.E4M3, None)
-        g8, sg, _ = O.quantize_step(gs, O.E5M2, None)
-        beta = O.bias_values(b.view(__import__("torch").int16).numpy().view(np.uint16), "bf16")
-        O.linear_fwd(x8, w8, O.E4M3, sx, sw, beta)
-        O.linear_bwd_dx(g8, O.E5M2, w8, O.E4M3, sg, sw)
-        O.linear_bwd_dw(g8, O.E5M2, x8, O.E4M3, sg, sx)
-        O.bias_grad(gs.astype(np.float64))
-        K, N = X.shape[1], W.shape[0]
-        flops += 3 * 2.0 * rows * N * K
-        done += 1
-        el = time.perf_counter() - t0
-        if el > budget_s or (el >= min_s and done % len(layers_cpu) == 0):
-            break
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    with threadpool_limits(limits=threads):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        t0 = time.perf_counter()
+        order = [layers_cpu[i % len(layers_cpu)] for i in range(64 * len(layers_cpu))]
+        for (X, W, b, G) in order:
+            xs = X[:rows].float().numpy()
+            gs = G[:rows].float().numpy()
+            ws = W.float().numpy()
+            x8, sx, _ = O.quantize_step(xs, O.E4M3, None)
+            w8, sw, _ = O.quantize_step(ws, O.E4M3, None)
+            g8, sg, _ = O.quantize_step(gs, O.E5M2, None)
+            beta = O.bias_values(b.view(__import__("torch").int16).numpy().view(np.uint16), "bf16")
+            O.linear_fwd(x8, w8, O.E4M3, sx, sw, beta)
+            O.linear_bwd_dx(g8, O.E5M2, w8, O.E4M3, sg, sw)
+            O.linear_bwd_dw(g8, O.E5M2, x8, O.E4M3, sg, sx)
+            O.bias_grad(gs.astype(np.float64))
+            K, N = X.shape[1], W.shape[0]
+            flops += 3 * 2.0 * rows * N * K
+            done += 1
+            el = time.perf_counter() - t0
+            if el > budget_s or (el >= min_s and done % len(layers_cpu) == 0):
+                break
+        dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used,
             "sample": f"{rows} of {layers_cpu[0][0].shape[0]} rows of X and G, full W; "
                       f"{done} linear passes over the layer's {len(layers_cpu)} linears: "
-                      f"quantize X/W/G (dynamic) + fwd/dX/dW "
-                      f"GEMMs + db, fp64 accumulation; {dt:.1f} s on {os.cpu_count()} host cpus"}
+                      f"quantize X/W/G (dynamic) + fwd/dX/dW GEMMs + db, fp64 accumulation; "
+                      f"{dt:.1f} s with {used} BLAS thread(s)"}
+
+
+def cpu_baseline(layers_cpu, budget_s):
+    """The oracle on the host's cores at all threads (value) and at one
+    thread (on a smaller row sample), with the CPU model."""
+    all_t = cpu_oracle_rate(layers_cpu, 0.55 * budget_s, rows=layers_cpu[0][0].shape[0])
+    one_t = cpu_oracle_rate(layers_cpu, 0.45 * budget_s, rows=256, threads=1, min_s=3.0)
+    return {**all_t, "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_thread": one_t}
+
+
+def ceilings(torch, stream):
+    """The machine's own ceilings, from the measurement kernels of
+    libfp8probe.so: the MFMA-only rate (v_mfma_f32_32x32x64_f8f6f4, 8 waves
+    per CU, one block per CU) on random e4m3 operands and on zeros, with all
+    CUs busy and with the tile counts of the layer's GEMMs; and a plain HBM
+    stream (copy, read, write) of 512 MiB at 4 and 8 blocks per CU."""
+    from scaled_quantize_fp8_amd import probe as P
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {"cus": cus, "mfma_TFLOPs": {}, "hbm_GBps": {}}
+    out = torch.empty(65536 * 8, dtype=torch.float32, device="cuda")
+    iters = 2000
+    for label, rnd in (("random", True), ("zeros", False)):
+        codes = P.mfma_codes(rnd)
+        for blocks in sorted({cus, 216, 192, 144, 48}):
+            if blocks > cus:
+                continue
+            st = batched_stats_us(torch, lambda: P.mfma(blocks, iters, codes, out, stream), stream,
+                                  reps=20, warm=3, batch=5)
+            res["mfma_TFLOPs"][f"{label}_{blocks}cu"] = round(
+                P.mfma_flops(blocks, iters) / (st["median"] * 1e-6) / 1e12, 1)
+    nbytes = 512 << 20
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for mode, name, moved in ((0, "copy", 2 * nbytes), (1, "read", nbytes), (2, "write", nbytes)):
+        best = 0.0
+        for bpc in (4, 8):
+            st = batched_stats_us(torch, lambda: P.stream(src, dst, nbytes, mode, bpc, sink, stream),
+                                  stream, reps=20, warm=3, batch=5)
+            best = max(best, moved / (st["median"] * 1e-6) / 1e9)
+        res["hbm_GBps"][name] = round(best, 1)
+    del src, dst
+    return res
 
 
 def layer_step(layers, stream, side):
@@ -459,32 +613,92 @@ def layer_step(layers, stream, side):
 
 
 def isolated_timings(torch, layers, reps, stream):
-    """Per-linear isolated kernel times (events behind a GPU sleep); the
-    per-kind GEMM totals of a step; the step's quantize time as it issues
-    it (the forward's quantize launch and the G quantize) and its rate."""
+    """Per-linear isolated kernel times, warm (the same buffers at every
+    launch), as batched medians with p10/p90 (batched_stats_us):
+
+      fwd_gemm, dx_gemm, dw_gemm   the three GEMMs as one-kernel calls on
+                                   pre-quantized operands (dW without db)
+      quant_X, quant_W, quant_G    the standalone fp8_quantize of each tensor
+                                   (ring election in its last block)
+      quant_fwd_pair               fp8_quantize_pair(X, W): one launch
+      fwd_call                     fp8_linear_fwd(X, W): the pair quantize
+                                   without election, then the GEMM that folds
+                                   the rings
+      bwd_dw_call                  fp8_linear_bwd_dw(G): the G quantize with
+                                   db's column partials, no election, then
+                                   the dW GEMM (with db) that folds the ring
+
+    The quantize inside the fused calls costs what a call takes beyond its
+    GEMM: fwd_call - fwd_gemm and bwd_dw_call - dw_gemm (the latter also
+    holds the db finalize)."""
     per = {}
     for L in layers:
-        per[L.name] = {
-            "fwd_gemm_us": 1e3 * event_time_ms(torch, L.gemm_fwd, reps, stream),
-            "dx_gemm_us": 1e3 * event_time_ms(torch, L.bwd_dx, reps, stream),
-            "dw_gemm_us": 1e3 * event_time_ms(torch, L.gemm_dw, reps, stream),
-        }
+        p = {"fwd_gemm": batched_stats_us(torch, L.gemm_fwd, stream, reps),
+             "dx_gemm": batched_stats_us(torch, L.bwd_dx, stream, reps),
+             "dw_gemm": batched_stats_us(torch, L.gemm_dw, stream, reps)}
         for w in ("X", "W", "G"):
-            us = 1e3 * event_time_ms(torch, L.quant[w], reps, stream)
-            per[L.name][f"quant_{w}_us"] = us
-            per[L.name][f"quant_{w}_GBps"] = L.quant_bytes(w) / (us * 1e-6) / 1e9
-        us = 1e3 * event_time_ms(torch, L.quant_xw, reps, stream)
-        fwd_bytes = L.quant_bytes("X") + (0.0 if L.prequant else L.quant_bytes("W"))
-        per[L.name]["quant_fwd_us"] = us
-        per[L.name]["quant_fwd_GBps"] = fwd_bytes / (us * 1e-6) / 1e9
-    for L in layers:
-        p = per[L.name]
+            p[f"quant_{w}"] = batched_stats_us(torch, L.quant[w], stream, reps)
+        p["quant_fwd_pair"] = batched_stats_us(torch, L.quant_xw, stream, reps)
+        p["fwd_call"] = batched_stats_us(torch, L.fwd, stream, reps)
+        p["bwd_dw_call"] = batched_stats_us(torch, L.bwd_dw, stream, reps)
+        med = lambda k: p[k]["median"]
+        fq_bytes = L.quant_bytes("X") + (0.0 if L.prequant else L.quant_bytes("W"))
+        derived = {
+            "quant_in_fwd_call_us": round(med("fwd_call") - med("fwd_gemm"), 3),
+            "quant_in_bwd_dw_call_us": round(med("bwd_dw_call") - med("dw_gemm"), 3),
+        }
+        derived["quant_in_fwd_call_GBps"] = round(
+            fq_bytes / max(derived["quant_in_fwd_call_us"], 1e-3) / 1e3, 1)
+        derived["quant_in_bwd_dw_call_GBps"] = round(
+            L.quant_bytes("G") / max(derived["quant_in_bwd_dw_call_us"], 1e-3) / 1e3, 1)
+        for w in ("X", "W", "G"):
+            derived[f"quant_{w}_GBps"] = round(L.quant_bytes(w) / (med(f"quant_{w}") * 1e3), 1)
         for g_ in ("fwd", "dx", "dw"):
-            p[f"{g_}_TFLOPs"] = L.flops / (p[f"{g_}_gemm_us"] * 1e-6) / 1e12
-    tot = {g_: sum(per[L.name][f"{g_}_gemm_us"] for L in layers) for g_ in ("fwd", "dx", "dw")}
-    q_us = sum(per[L.name]["quant_fwd_us"] + per[L.name]["quant_G_us"] for L in layers)
+            derived[f"{g_}_TFLOPs"] = round(L.flops / (med(f"{g_}_gemm") * 1e-6) / 1e12, 1)
+        p["derived"] = derived
+        per[L.name] = p
+    tot = {g_: sum(per[L.name][f"{g_}_gemm"]["median"] for L in layers) for g_ in ("fwd", "dx", "dw")}
+    # the quantizes as the step runs them, inside the fused calls
+    q_us = sum(per[L.name]["derived"]["quant_in_fwd_call_us"] +
+               per[L.name]["derived"]["quant_in_bwd_dw_call_us"] for L in layers)
     q_bytes = sum(L.step_quant_bytes() for L in layers)
     return per, tot, q_us, q_bytes / (q_us * 1e-6) / 1e9
+
+
+def cold_quant_sweep(torch, sets, stream, reps=100):
+    """The standalone quantizes of one step over the cold rotation: a batch
+    is one copy's paired X/W launch and G launch for every linear, and
+    consecutive batches take consecutive copies, so every input was last
+    read ~1 GB of other inputs ago (past the 256 MB MALL).  Beside it the
+    same batch on one copy, warm.  Aggregate GB/s of the algorithmic bytes
+    (median, p10, p90 over batches)."""
+    R = len(sets)
+    sweeps = [[fn for L in ls for fn in (L.quant_xw, L.quant["G"])] for ls in sets]
+    nbytes = sum(L.step_quant_bytes() for L in sets[0])
+    out = {}
+    for label, order in (("cold", list(range(R))), ("warm", [0])):
+        for i in range(2 * R):  # warm-up batches
+            for fn in sweeps[order[i % len(order)]]:
+                fn()
+        nb = max(len(order), reps // len(sweeps[0]))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(nb)]
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(5_000_000)
+            for bi, (a, b) in enumerate(evs):
+                a.record(stream)
+                for fn in sweeps[order[bi % len(order)]]:
+                    fn()
+                b.record(stream)
+        evs[-1][1].synchronize()
+        us = [1e3 * a.elapsed_time(b) for a, b in evs]
+        gbps = [nbytes / (u * 1e-6) / 1e9 for u in us]
+        out[label] = {"us_per_step": round(_pct(us, 50), 2), "GBps": round(_pct(gbps, 50), 1),
+                      "GBps_p10": round(_pct(gbps, 10), 1), "GBps_p90": round(_pct(gbps, 90), 1),
+                      "batches": nb}
+    out["bytes_per_step"] = nbytes
+    out["launches_per_step"] = len(sweeps[0])
+    return out
 
 
 def timed_steps_ms(torch, step, steps, stream):
@@ -665,6 +879,14 @@ def main():
             f.write("\n")
         print(json.dumps(rec))
         return
+    if args.trace_from:
+        rec = trace_record(args.trace_from, args.workload)
+        os.makedirs(PROFILE_DIR, exist_ok=True)
+        with open(trace_record_path(args.workload), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
     if args.mfma_from:
         rec = mfma_record(args.mfma_from, args.workload)
         os.makedirs(PROFILE_DIR, exist_ok=True)
@@ -756,35 +978,40 @@ def main():
             st_()
     torch.cuda.synchronize()
 
-    # ---- isolated per-kernel timings (events behind a GPU sleep), before the
-    # timed region: they decide which GEMM kind the live events follow
+    # ---- isolated per-kernel timings (batched medians with p10/p90, warm),
+    # before the timed region: they decide which GEMM kind the live events
+    # follow; then the step's standalone quantizes over the cold rotation
     per, tot, q_us, quant_gbps = isolated_timings(torch, layers, args.kernel_reps, stream)
+    qsweep = cold_quant_sweep(torch, sets, stream)
 
     # ---- timed region: exactly args.steps eager steps, step s on copy s mod R
-    # of the layer.  In step s the launch
-    # of the GEMM kind that dominates the isolated timings (forward or dX:
-    # each a one-kernel call on stream) of linear s mod n is bracketed with
-    # events on stream, so over the steps every linear's launch is timed
-    # live while each step carries one event pair (an event record costs a
-    # few microseconds of the stream's time).  A bracketed dX GEMM needs the
-    # backward as two calls on stream (fp8_linear_bwd_dw, then the dX alone);
-    # a bracketed forward GEMM runs while side is idle (the previous step
-    # ended with the join).  The event pairs are created up front, outside
-    # the timed region.
+    # of the layer.  In every other step (s even) one launch of the GEMM
+    # kind that dominates the isolated timings (forward or dX) is bracketed
+    # with events on stream, of linear (s / 2) mod n, so that every linear's
+    # launch is timed live at least once while only half the steps carry an
+    # event pair (an event record costs the stream a few microseconds).  A
+    # bracketed forward runs as fp8_quantize_pair + fp8_linear_fwd(X8, W8);
+    # a bracketed dX GEMM needs the backward as two calls on stream
+    # (fp8_linear_bwd_dw, then the dX alone).  The event pairs are created up
+    # front, outside the timed region.
     dom = "fwd" if tot["fwd"] >= tot["dx"] else "dx"
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    ev_layer = []
+    brack = [si for si in range(args.steps) if si % 2 == 0]
+    if len(brack) < len(layers):
+        brack = list(range(args.steps))
+    ev = {si: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for si in brack}
+    ev_layer = {}
 
     def bracketing(step_i):
         ls = sets[step_i % R]
+        target = (brack.index(step_i) % len(ls)) if step_i in ev else -1
 
         def launch(kind, li, fn):
-            if li != step_i % len(ls) or kind != ("fwd" if dom == "fwd" else "bwd"):
+            if li != target or kind != ("fwd" if dom == "fwd" else "bwd"):
                 fn()
                 return
             a, b_ = ev[step_i]
-            ev_layer.append(li)
+            ev_layer[step_i] = li
             if dom == "fwd":
                 # the same forward as two calls, so the GEMM launch can be
                 # bracketed alone: the quantize (with its ring election),
@@ -819,14 +1046,14 @@ def main():
     # live launch durations of the dominant kind: average over the bracketed
     # launches, with the average flops of the same launches; per step, the
     # sum over the linears of each one's average live duration
-    live_ms = [a.elapsed_time(b_) for a, b_ in ev]
+    live_ms = [ev[si][0].elapsed_time(ev[si][1]) for si in brack]
     by_layer = {}
-    for li, ms in zip(ev_layer, live_ms):
-        by_layer.setdefault(li, []).append(ms)
+    for si, ms in zip(brack, live_ms):
+        by_layer.setdefault(ev_layer[si], []).append(ms)
     live = {"avg_ms": sum(live_ms) / len(live_ms),
             "total_ms": (sum(sum(v) / len(v) for v in by_layer.values())
                          if len(by_layer) == len(layers) else None),
-            "flops": sum(layers[li].flops for li in ev_layer) / len(ev_layer),
+            "flops": sum(layers[ev_layer[si]].flops for si in brack) / len(brack),
             "launches": len(live_ms)}
 
     # ---- the same step captured as one HIP graph and replayed
@@ -858,7 +1085,10 @@ def main():
 
     # the roofline entry: the dominant GEMM kind of the forward and dX (the
     # two issued as one-kernel calls), timed live; all three isolated totals
-    # are reported beside it
+    # are reported beside it.  An event pair around a single launch adds a
+    # fixed overhead (measured here on the same launches); `achieved` takes
+    # it out, `achieved_raw` keeps it, and the kernel trace of a profiled
+    # run of this benchmark gives the third figure (`trace`).
     dominant_isolated = max(tot, key=tot.get)
     kernel_names = {
         "fwd": "gemm4/gemm5/gemm3_kernel <.., kKContig, kKContig, E4M3, E4M3> "
@@ -866,18 +1096,24 @@ def main():
         "dx": "gemm4/gemm5/gemm3_kernel <.., kKContig, kCross, E5M2, E4M3> "
               "(dX = G8 W8, W8 read crosswise; tile chosen per shape)",
     }
-    achieved = live["flops"] / (live["avg_ms"] * 1e-3) / 1e12
+    overhead_us = sum(bracket_overhead_us(torch, getattr(L, {"fwd": "gemm_fwd", "dx": "bwd_dx"}[dom]),
+                                          20, stream) for L in layers) / len(layers)
+    raw = live["flops"] / (live["avg_ms"] * 1e-3) / 1e12
+    corrected_us = live["avg_ms"] * 1e3 - overhead_us
+    achieved = live["flops"] / (corrected_us * 1e-6) / 1e12
     traffic = load_traffic(traffic_key(dom, args.workload))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_FP8_DENSE_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP8_DENSE_TFLOPS, 4),
                 "traffic": traffic,
                 "kernel": kernel_names[dom],
-                "launch_avg_us": round(live["avg_ms"] * 1e3, 2),
+                "launch_avg_us": round(corrected_us, 2),
+                "launch_avg_us_raw": round(live["avg_ms"] * 1e3, 2),
+                "live_bracket_overhead_us": round(overhead_us, 2),
+                "achieved_raw": round(raw, 2),
+                "frac_raw": round(raw / MI355X_FP8_DENSE_TFLOPS, 4),
+                "trace": load_trace_record(dom, args.workload),
                 "flops_per_launch": live["flops"],
                 "live_launches": live["launches"],
-                "live_bracket_overhead_us": round(sum(
-                    bracket_overhead_us(torch, getattr(L, {"fwd": "gemm_fwd", "dx": "bwd_dx"}[dom]),
-                                        args.kernel_reps, stream) for L in layers) / len(layers), 2),
                 "live_us_per_step": (None if live["total_ms"] is None
                                      else round(live["total_ms"] * 1e3, 1)),
                 "isolated_gemm_us_per_step": {k: round(v, 1) for k, v in tot.items()},
@@ -900,14 +1136,23 @@ def main():
         "config": {"workload": workload_label(wl), "global_batch": wl.M,
                    "gemms_per_step": 3 * len(layers)},
         "step_schedule": "every forward in order as fp8_linear_fwd(X, W) (quantize without "
-                         "election; the GEMM folds the rings), one per step split into "
-                         "fp8_quantize_pair + fp8_linear_fwd(X8, W8) for the event bracket; "
-                         "then every backward in reverse order as fp8_linear_bwd (dX on the "
-                         "main stream, dW and db on a second stream after the G quantize); one "
-                         "join of the two streams per step",
+                         "election; the GEMM folds the rings), in every other step one of them "
+                         "split into fp8_quantize_pair + fp8_linear_fwd(X8, W8) for the event "
+                         "bracket; then every backward in reverse order as fp8_linear_bwd (dX on "
+                         "the main stream, dW and db on a second stream after the G quantize); "
+                         "one join of the two streams per step",
         "pct_fp8_peak": round(100 * tflops / MI355X_FP8_DENSE_TFLOPS, 2),
-        "quantize_GBps": round(quant_gbps, 1),
-        "quantize_pct_hbm": round(100 * quant_gbps / MI355X_HBM_GBPS, 2),
+        "quantize_GBps": qsweep["cold"]["GBps"],
+        "quantize_pct_hbm": round(100 * qsweep["cold"]["GBps"] / MI355X_HBM_GBPS, 2),
+        "quantize": {
+            "standalone_cold": qsweep["cold"], "standalone_warm": qsweep["warm"],
+            "standalone_note": "fp8_quantize_pair(X, W) and fp8_quantize(G) of every linear, "
+                               "ring election in each launch's last block",
+            "in_fused_calls_warm_GBps": round(quant_gbps, 1),
+            "in_fused_calls_warm_us_per_step": round(q_us, 1),
+            "in_fused_calls_note": "the step's quantizes as it runs them (no election; the GEMM "
+                                   "folds the ring): fused call minus its GEMM, warm medians",
+            "bytes_per_step": qsweep["bytes_per_step"]},
         "quantize_traffic": load_quant_traffic(args.workload),
         "wall_s_timed": round(wall, 4),
         "cold_rotation": rotation,
@@ -917,10 +1162,14 @@ def main():
         "graph_TFLOPs": None if graph_ms_per_step is None else
         round(step_flops / (graph_ms_per_step * 1e-3) / 1e12, 2),
         "gemm_us_per_step": {g: round(v, 1) for g, v in tot.items()},
-        "quant_us_per_step": round(q_us, 1),
-        "per_linear": {k: {kk: round(vv, 2) for kk, vv in v.items()} for k, v in per.items()},
+        "per_linear": per,
+        "timing_method": "isolated kernels: 20 warm-up launches, then 200 launches in batches of "
+                         "20 back-to-back launches, one event pair per batch; median, p10, p90 "
+                         "of the per-launch time over the batches (warm: the same buffers)",
         "roofline": roofline,
     }
+    if not args.no_ceilings:
+        out["ceilings"] = ceilings(torch, stream)
     if not args.no_widened:
         out["widened"] = widened_rows(torch, F, WL, wl, layers, stream, args.kernel_reps)
     if not args.no_other_configs:

@@ -1,4 +1,5 @@
-"""Build libfp8linear.so in-tree with hipcc for gfx950."""
+"""Build libfp8linear.so (the FP8 linear path) and libfp8probe.so (its
+measurement kernels) in-tree with hipcc for gfx950."""
 
 from __future__ import annotations
 
@@ -13,6 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libfp8linear.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "fp8l_api.hip")]
+PROBE_LIB_PATH = os.path.join(HERE, "libfp8probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "fp8l_probe.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("fp8l_device.hpp", "fp8l_quantize.hpp", "fp8l_gemm.hpp",
                                                      "fp8l_gemm3.hpp", "fp8l_gemm4.hpp", "fp8l_gemm5.hpp")] + [
     os.path.join(ROOT, "include", "fp8linear.h")
@@ -41,7 +44,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build_command(out: str = LIB_PATH, extra: list[str] | None = None) -> list[str]:
+def build_command(out: str = LIB_PATH, extra: list[str] | None = None,
+                  sources: list[str] | None = None) -> list[str]:
     return [
         hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
         # packed fp32 VALU forms stay off (see the library's design notes)
@@ -49,22 +53,29 @@ def build_command(out: str = LIB_PATH, extra: list[str] | None = None) -> list[s
         "-I", os.path.join(ROOT, "include"),
         f'-DFP8L_SOURCE_HASH="{source_hash()}"',
         *(extra or []),
-        *SOURCES, "-o", out,
+        *(SOURCES if sources is None else sources), "-o", out,
     ]
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the HIP library; always recompiles.  Returns the .so path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = build_command(tmp)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
-            if "packed-fp32-ops" not in ln and ln.strip()]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs))
-    os.replace(tmp, LIB_PATH)
+    """Compile both libraries (always recompiles; the two hipcc runs go in
+    parallel).  Returns the path of libfp8linear.so."""
+    jobs = [(LIB_PATH, build_command(LIB_PATH + ".tmp")),
+            (PROBE_LIB_PATH, build_command(PROBE_LIB_PATH + ".tmp", sources=PROBE_SOURCES))]
+    procs = [(out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                    text=True)) for out, cmd in jobs]
+    failed = []
+    for out, proc in procs:
+        text, _ = proc.communicate()
+        msgs = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+        if proc.returncode != 0:
+            failed.append(f"hipcc failed for {os.path.basename(out)}:\n" + "\n".join(msgs))
+        elif verbose and msgs:
+            print("\n".join(msgs))
+    if failed:
+        raise RuntimeError("\n".join(failed))
+    for out, _ in jobs:
+        os.replace(out + ".tmp", out)
     return LIB_PATH
 
 

@@ -13,14 +13,19 @@ import scaled_quantize_fp8_amd as F
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    names = []
-    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
-        if fn.endswith(".h"):
-            text = open(os.path.join(ROOT, "include", fn)).read()
-            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            names += re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(fp8_[a-z_0-9]+)\s*\(", text, re.M)
-    return names
+HEADERS = {"fp8linear.h": "libfp8linear.so", "fp8probe.h": "libfp8probe.so"}
+
+
+def _declared_functions(header="fp8linear.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(fp8[a-z_0-9]*_[a-z_0-9]+)\s*\(",
+                      text, re.M)
+
+
+def test_every_header_has_its_library():
+    assert sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")) == \
+        sorted(HEADERS)
 
 
 @pytest.fixture(scope="module")
@@ -42,6 +47,21 @@ def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
         assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_probe_library_exports_its_symbols():
+    from scaled_quantize_fp8_amd import probe
+    names = set(_declared_functions("fp8probe.h"))
+    assert names == set(probe.C_SYMBOLS)
+    L = probe.lib()
+    for name in names:
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+    # argument checks return before any launch
+    assert L.fp8probe_mfma(0, 1, 1, 1, None) == 2
+    assert L.fp8probe_mfma(4, 1, None, 1, None) == 1
+    assert L.fp8probe_stream(1, 1, 17, 0, 1, 1, None) == 2
+    assert L.fp8probe_stream(1, 1, 16, 3, 1, 1, None) == 2
+    assert L.fp8probe_stream(None, 1, 16, 0, 1, 1, None) == 1
 
 
 def test_version_and_status_strings(lib):

@@ -150,3 +150,34 @@ def test_layer_step_order_forwards_then_backwards_then_join():
     step(hook)
     assert seen == [("fwd", 0), ("fwd", 1), ("fwd", 2), ("bwd", 2), ("bwd", 1), ("bwd", 0)]
     assert log[-1] == ("join", "side")
+
+
+def test_trace_record_per_kind_averages(tmp_path):
+    """The trace record averages each GEMM kind's dispatch durations from a
+    kernel-trace CSV and turns the average flops per launch of the
+    workload's linears over that duration into a fraction of the peak."""
+    import csv
+    path = tmp_path / "trace.csv"
+    names = {"fwd": "void fp8l::gemm4_kernel<0, 0, 0, 0, 0, 0>(fp8l::GemmArgs)",
+             "dx": "void fp8l::gemm5_kernel<0, 1, 1, 0>(fp8l::GemmArgs)",
+             "dw": "void fp8l::gemm3_kernel<128, 128, 2, 2, 1, 1, 1, 0, 0, 0>(fp8l::GemmArgs)",
+             "q": "void fp8l::quantize_flat_kernel<2, 0, 0>(fp8l::QArgs)",
+             "f8": "void fp8l::gemm3_kernel<128, 128, 2, 2, 0, 0, 0, 0, 1, 0>(fp8l::GemmArgs)"}
+    rows = [("fwd", 20000), ("fwd", 30000), ("dx", 10000), ("dw", 40000), ("q", 5000),
+            ("f8", 99000)]
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        t = 1000
+        for k, d in rows:
+            w.writerow([names[k], t, t + d])
+            t += d
+    rec = bench.trace_record(str(path), "dim1536_m2048")
+    assert rec["kinds"]["fwd"] == {"launches": 2, "avg_us": 25.0,
+                                   "frac": pytest.approx(rec["flops_per_launch_avg"] / 25e-6 / 1e12
+                                                         / bench.MI355X_FP8_DENSE_TFLOPS, abs=1e-4)}
+    assert rec["kinds"]["dx"]["avg_us"] == 10.0 and rec["kinds"]["dw"]["avg_us"] == 40.0
+    assert set(rec["kinds"]) == {"fwd", "dx", "dw"}  # quantize and fp8-output GEMM not counted
+    from scaled_quantize_fp8_amd import workloads as WL
+    wl = WL.WORKLOADS["dim1536_m2048"]
+    assert rec["flops_per_launch_avg"] == sum(2.0 * wl.M * L.N * L.K for L in wl.linears) / 5
