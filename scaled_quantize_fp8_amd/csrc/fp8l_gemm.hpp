@@ -102,8 +102,7 @@ struct GemmArgs {
 // S(window max), mark the ring seeded, write amax_out.  The quantize launch
 // ran before this kernel on the same stream and has completed, so every
 // group max is in place; nothing else touches the ring while this kernel
-// runs.  The loads and the atomic exchange are waited for here, before the
-// caller issues any operand load.
+// runs.  The loads and the atomic exchange are waited for here.
 FP8L_DEV void ring_fold_wave(const RingFold& f) {
   const int lane = threadIdx.x & 63;
   const uint32_t gm = atom_xchg(&f.ring->group[lane].amax, 0u);
@@ -122,8 +121,9 @@ FP8L_DEV void ring_fold_wave(const RingFold& f) {
   }
 }
 
-// Block (0, 0)'s wave 0 folds the rings before its first operand load (one
-// device round trip on one wave of one block).
+// Block (0, 0)'s wave 0 folds the rings: one device round trip on one wave
+// of one block.  The pipelined kernels do it after their K loop (side_work),
+// the general kernel at its start.
 FP8L_DEV void ring_folds(const GemmArgs& g) {
   if (blockIdx.x != 0 || blockIdx.y != 0 || (threadIdx.x >> 6) != 0) return;
   if (g.fold[0].ring) ring_fold_wave(g.fold[0]);
@@ -293,7 +293,7 @@ FP8L_DEV void tile_coords(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
 template <int LA, int LB, int FA, int FB>
 __global__ __launch_bounds__(kGThreads, 2) void gemm_kernel(GemmArgs g) {
   batch_slice(g);
-  ring_folds(g);  // before any operand load of this block
+  ring_folds(g);
   __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][kTileBytes];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;

@@ -211,13 +211,14 @@ FP8L_DEV EpiScales load_scales(const GemmArgs& g) {
 }
 
 // Work beside the tile: block 0's snapshot copies for pre-quantized
-// operands and the bias-gradient finalize (shared by all blocks; one
-// thread per entry walking all rows, in the first tile column's blocks
-// only, made those blocks the launch's last by many microseconds).  Kernels
-// call it after the K loop and the MFMA drain, when no operand DMA is in
-// flight: a wait for these loads then waits for nothing else (in the
-// prologue the first such wait held every stage in flight).
-// NT: threads per block.
+// operands and ring folds, and the bias-gradient finalize (shared by all
+// blocks; one thread per entry walking all rows, in the first tile column's
+// blocks only, made those blocks the launch's last by many microseconds).
+// Kernels call it after the K loop and the MFMA drain, when no operand DMA
+// is in flight: a wait for these loads then waits for nothing else (in the
+// prologue the first such wait held every stage in flight; the ring folds
+// there delayed block 0's first stage by a device round trip and measured
+// ~0.5 us slower per GEMM).  NT: threads per block.
 template <int NT>
 FP8L_DEV void side_work(const GemmArgs& g) {
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
@@ -227,6 +228,7 @@ FP8L_DEV void side_work(const GemmArgs& g) {
     if (g.aux_amax_dst1) *g.aux_amax_dst1 = 0.0f;
   }
   if (g.db) db_finalize<NT>(g);
+  ring_folds(g);
 }
 
 // Bias of the block's BN output columns, staged in LDS for the epilogue so
@@ -655,7 +657,6 @@ template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB, int 
 __global__ __launch_bounds__(64 * WGM * WGN, (BM * BN <= 128 * 128) ? 2 : 1)
 void gemm3_kernel(GemmArgs g) {
   batch_slice(g);
-  ring_folds(g);  // before any operand load of this block
   constexpr int NW = WGM * WGN;
   using OA = Op3<LA, BM, NW>;
   using OB = Op3<LB, BN, NW>;

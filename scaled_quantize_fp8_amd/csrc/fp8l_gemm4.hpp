@@ -31,7 +31,6 @@ constexpr int kGemm4BiasOff =
 template <int LA, int LB, int FA, int FB, int EPI = kEpiBF16, int OF = kE4M3>
 __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   batch_slice(g);
-  ring_folds(g);  // before any operand load of this block
   constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4, NW = WGM * WGN;
   using OA = Op3<LA, BM, NW>;
   using OB = Op3<LB, BN, NW>;

@@ -181,7 +181,6 @@ constexpr int kGemm5BiasOff = kStages3 * 2 * 256 * kBK3 > 128 * (128 * 2 + 16)
 template <int LA, int LB, int FA, int FB>
 __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
   batch_slice(g);
-  ring_folds(g);  // before any operand load of this block
   constexpr int BM = 128, BN = 128, NW = 8;
   using OA = Stage128<LA, BM, NW>;  // 16 KB per stage, two DMA loads per wave
   using OB = Stage128<LB, BN, NW>;
