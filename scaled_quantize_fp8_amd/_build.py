@@ -17,7 +17,8 @@ SOURCES = [os.path.join(CSRC, "fp8l_api.hip")]
 PROBE_LIB_PATH = os.path.join(HERE, "libfp8probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "fp8l_probe.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("fp8l_device.hpp", "fp8l_quantize.hpp", "fp8l_gemm.hpp",
-                                                     "fp8l_gemm3.hpp", "fp8l_gemm4.hpp", "fp8l_gemm5.hpp")] + [
+                                                     "fp8l_gemm3.hpp", "fp8l_gemm4.hpp", "fp8l_gemm5.hpp",
+                                                     "fp8l_gemm_pair.hpp")] + [
     os.path.join(ROOT, "include", "fp8linear.h")
 ]
 

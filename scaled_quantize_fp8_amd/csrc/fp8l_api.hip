@@ -19,6 +19,7 @@
 #include "fp8l_device.hpp"
 #include "fp8l_gemm.hpp"
 #include "fp8l_gemm5.hpp"
+#include "fp8l_gemm_pair.hpp"
 #include "fp8l_quantize.hpp"
 
 namespace fp8l {
@@ -467,6 +468,64 @@ void launch_gemm_l(GemmArgs& g, int fa, int fb, hipStream_t st) {
   else launch_gemm_t<LA, LB, kE5M2, kE5M2>(g, st);
 }
 
+// The grouped backward (fp8l_gemm_pair.hpp): dX (A = G8 k-contiguous, B =
+// W8 crosswise) and dW (both crosswise) in one launch.  Each problem takes
+// the tile its own launch would (256x256 when its tiles fill at least half
+// the CUs, else 128x128 with 8 waves; the 4-wave 128x128 block that a lone
+// launch may pick is replaced by the 8-wave one, since the grid runs
+// 512-thread blocks).  The problem whose tiles take longer (tile area times
+// K) gets the first block range.
+template <class BX, class BW>
+void launch_pair_t(GemmArgs& dx, GemmArgs& dw, hipStream_t st) {
+  constexpr int lds = pair_lds_bytes<BX, BW>();
+  static bool attr_set[64] = {false};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+    (void)hipFuncSetAttribute((const void*)gemm_pair_kernel<BX, BW>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr_set[dev] = true;
+  }
+  auto tiles = [](GemmArgs& g, int bm, int bn) {
+    g.tiles_m = (int32_t)((g.Mc + bm - 1) / bm);
+    g.tiles_n = (int32_t)((g.Nc + bn - 1) / bn);
+    if (g.tiles_m < 1) g.tiles_m = 1;
+    if (g.tiles_n < 1) g.tiles_n = 1;
+    return g.tiles_m * g.tiles_n;
+  };
+  const int nx = tiles(dx, BX::kBM, BX::kBN), nw = tiles(dw, BW::kBM, BW::kBN);
+  const double work_x = (double)BX::kBM * BX::kBN * (double)dx.Kc;
+  const double work_w = (double)BW::kBM * BW::kBN * (double)dw.Kc;
+  GemmArgs& first = work_x >= work_w ? dx : dw;
+  GemmArgs& second = work_x >= work_w ? dw : dx;
+  first.blk0 = 0;
+  first.nblk = work_x >= work_w ? nx : nw;
+  second.blk0 = (first.nblk + 7) & ~7;
+  second.nblk = work_x >= work_w ? nw : nx;
+  hipLaunchKernelGGL((gemm_pair_kernel<BX, BW>), dim3((unsigned)(second.blk0 + second.nblk)),
+                     dim3(512), lds, st, dx, dw);
+}
+
+// Grouped launch when both problems take the fast kernels with the standard
+// recipe's formats (G in e5m2, W8 and X8 in e4m3) and no tile is forced;
+// false: the caller launches them one by one.
+bool launch_pair(GemmArgs& dx, GemmArgs& dw, int fmt_g, int fmt_w, int fmt_x, hipStream_t st) {
+  if (fmt_g != kE5M2 || fmt_w != kE4M3 || fmt_x != kE4M3 || forced_tile() != kTileAuto) return false;
+  if (dx.batch != 1 || dw.batch != 1) return false;
+  if (!fast_path_ok<kKContig, kCross>(dx) || !fast_path_ok<kCross, kCross>(dw)) return false;
+  const bool big_x = choose_tile(dx.Mc, dx.Nc, 1) == kTile256x256w8;
+  const bool big_w = choose_tile(dw.Mc, dw.Nc, 1) == kTile256x256w8;
+  using X4 = Body4<kKContig, kCross, kE5M2, kE4M3>;
+  using X5 = Body5<kKContig, kCross, kE5M2, kE4M3>;
+  using W4 = Body4<kCross, kCross, kE5M2, kE4M3>;
+  using W5 = Body5<kCross, kCross, kE5M2, kE4M3>;
+  if (big_x && big_w) launch_pair_t<X4, W4>(dx, dw, st);
+  else if (big_x) launch_pair_t<X4, W5>(dx, dw, st);
+  else if (big_w) launch_pair_t<X5, W4>(dx, dw, st);
+  else launch_pair_t<X5, W5>(dx, dw, st);
+  return true;
+}
+
 void finish_gemm_args(GemmArgs& g) {
   const int64_t tm = (g.Mc + kBM - 1) / kBM, tn = (g.Nc + kBN - 1) / kBN;
   g.tiles_m = (int32_t)(tm < 1 ? 1 : tm);
@@ -732,10 +791,9 @@ static int bwd_prepare(int64_t M, int64_t N, fp8_operand_t g, int32_t fmt_g, fp8
 // The dX GEMM of a backward: dX = G8 W8 / (sg sw).  pre: g was given
 // pre-quantized, so this launch's block 0 also snapshots its scale into
 // sg_used and clears amax_g.
-static void enqueue_dx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* g8, const float* sg,
-                            int32_t fmt_g, fp8_operand_t w8, void* dx, bool pre, const float* g_scale,
-                            float* sg_used, float* amax_g, hipStream_t stream,
-                            const RingFold& fold = RingFold{}) {
+static GemmArgs dx_gemm_args(int64_t M, int64_t N, int64_t K, const uint8_t* g8, const float* sg,
+                             fp8_operand_t w8, void* dx, bool pre, const float* g_scale,
+                             float* sg_used, float* amax_g, const RingFold& fold) {
   GemmArgs a = {};
   a.fold[0] = fold;
   a.a = g8;  // [M, N], contraction n contiguous
@@ -755,6 +813,14 @@ static void enqueue_dx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* g8, 
     a.aux_amax_dst0 = amax_g;
   }
   finish_gemm_args(a);
+  return a;
+}
+
+static void enqueue_dx_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* g8, const float* sg,
+                            int32_t fmt_g, fp8_operand_t w8, void* dx, bool pre, const float* g_scale,
+                            float* sg_used, float* amax_g, hipStream_t stream,
+                            const RingFold& fold = RingFold{}) {
+  GemmArgs a = dx_gemm_args(M, N, K, g8, sg, w8, dx, pre, g_scale, sg_used, amax_g, fold);
   launch_gemm_l<kKContig, kCross>(a, fmt_g, dtype_fmt(w8.dtype), stream);
 }
 
@@ -774,10 +840,10 @@ static void enqueue_db_colsum_pre(int64_t M, int64_t N, const uint8_t* g8, int32
 // The dW GEMM of a backward: dW = G8^T X8 / (sg sx), and db from the column
 // partials in db_ws.  aux: snapshot a pre-quantized g's scale (see
 // enqueue_dx_gemm).
-static void enqueue_dw_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* g8, const float* sg,
-                            int32_t fmt_g, fp8_operand_t x8, void* dw, void* db, float* db_ws,
-                            bool pre, bool aux, const float* g_scale, float* sg_used,
-                            float* amax_g, hipStream_t stream, const RingFold& fold = RingFold{}) {
+static GemmArgs dw_gemm_args(int64_t M, int64_t N, int64_t K, const uint8_t* g8, const float* sg,
+                             fp8_operand_t x8, void* dw, void* db, float* db_ws, bool pre, bool aux,
+                             const float* g_scale, float* sg_used, float* amax_g,
+                             const RingFold& fold) {
   GemmArgs a = {};
   a.fold[0] = fold;
   a.a = g8;  // G8 [M, N] as A(i = n, k = m): crosswise
@@ -803,6 +869,15 @@ static void enqueue_dw_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* g8, 
     a.aux_amax_dst0 = amax_g;
   }
   finish_gemm_args(a);
+  return a;
+}
+
+static void enqueue_dw_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* g8, const float* sg,
+                            int32_t fmt_g, fp8_operand_t x8, void* dw, void* db, float* db_ws,
+                            bool pre, bool aux, const float* g_scale, float* sg_used,
+                            float* amax_g, hipStream_t stream, const RingFold& fold = RingFold{}) {
+  GemmArgs a = dw_gemm_args(M, N, K, g8, sg, x8, dw, db, db_ws, pre, aux, g_scale, sg_used, amax_g,
+                            fold);
   launch_gemm_l<kCross, kCross>(a, fmt_g, dtype_fmt(x8.dtype), stream);
 }
 
@@ -933,6 +1008,14 @@ int fp8_linear_bwd(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt
               stream, &g8, &sg, &pre, &fold);
   if (want_db && pre) enqueue_db_colsum_pre(M, N, g8, fmt_g, db_ws, stream);
   if ((st = hip_status())) return st;
+  if (stream_dw == stream) {
+    // one stream: both GEMMs in one grouped launch where they qualify
+    GemmArgs ax = dx_gemm_args(M, N, K, g8, sg, w8, dx, pre, g.scale, sg_used, amax_g, fold);
+    GemmArgs aw = dw_gemm_args(M, N, K, g8, sg, x8, dw, db, db_ws, pre, false, g.scale, sg_used,
+                               amax_g, RingFold{});
+    if (launch_pair(ax, aw, fmt_g, dtype_fmt(w8.dtype), dtype_fmt(x8.dtype), stream))
+      return hip_status();
+  }
   if (stream_dw != stream && (st = fork_after(stream, stream_dw))) return st;
   // the dX GEMM snapshots a pre-quantized g's scale; the dW GEMM reads
   // g's own scale, so the two streams touch no common output

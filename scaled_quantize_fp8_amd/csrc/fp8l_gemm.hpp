@@ -95,7 +95,17 @@ struct GemmArgs {
   float* oamax;
   // ring folds left by the quantizes of this GEMM's operands (block 0)
   RingFold fold[2];
+  // This problem's blocks within the launch: x indices blk0 .. blk0 + nblk - 1
+  // (nblk 0: the whole grid).  A launch that runs two problems (the grouped
+  // backward) gives each its own range; a problem's block b is launch block
+  // blk0 + b, and blk0 is a multiple of 8, so b and the launch block sit on
+  // the same XCD (workgroups are dealt round-robin over the 8 XCDs).
+  int32_t blk0, nblk;
 };
+
+// This block's index within its problem, and the problem's block count (x).
+FP8L_DEV int prob_block(const GemmArgs& g) { return (int)blockIdx.x - g.blk0; }
+FP8L_DEV int prob_nblk(const GemmArgs& g) { return g.nblk ? g.nblk : (int)gridDim.x; }
 
 // The fold of one ring by one full wave: take the 64 group maxima (leaving
 // zeros), fold the launch amax into hist[idx], advance idx, publish
@@ -125,7 +135,7 @@ FP8L_DEV void ring_fold_wave(const RingFold& f) {
 // of one block.  The pipelined kernels do it after their K loop (side_work),
 // the general kernel at its start.
 FP8L_DEV void ring_folds(const GemmArgs& g) {
-  if (blockIdx.x != 0 || blockIdx.y != 0 || (threadIdx.x >> 6) != 0) return;
+  if (prob_block(g) != 0 || blockIdx.y != 0 || (threadIdx.x >> 6) != 0) return;
   if (g.fold[0].ring) ring_fold_wave(g.fold[0]);
   if (g.fold[1].ring) ring_fold_wave(g.fold[1]);
 }
@@ -242,8 +252,8 @@ FP8L_DEV float bias_at(const GemmArgs& g, int64_t j, float inv_bs) {
 template <int NT>
 FP8L_DEV void db_finalize(const GemmArgs& g) {
   const int tid = threadIdx.x;
-  const int64_t nblk = (int64_t)gridDim.x * gridDim.y;
-  const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  const int64_t nblk = (int64_t)prob_nblk(g) * gridDim.y;
+  const int64_t b = (int64_t)blockIdx.y * prob_nblk(g) + prob_block(g);
   constexpr int per = NT / 16;  // entries per block and pass
   const int q = tid & 15;
   for (int64_t i = b * per + tid / 16; i - tid / 16 < g.Mc; i += nblk * per) {

@@ -221,7 +221,7 @@ FP8L_DEV EpiScales load_scales(const GemmArgs& g) {
 // ~0.5 us slower per GEMM).  NT: threads per block.
 template <int NT>
 FP8L_DEV void side_work(const GemmArgs& g) {
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+  if (prob_block(g) == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
     if (g.aux_scale_dst0) *g.aux_scale_dst0 = *g.aux_scale_src0;
     if (g.aux_amax_dst0) *g.aux_amax_dst0 = 0.0f;
     if (g.aux_scale_dst1) *g.aux_scale_dst1 = *g.aux_scale_src1;
@@ -594,7 +594,7 @@ FP8L_DEV void fp8_out_epilogue(const GemmArgs& g, const v16f (&acc)[FM][FN], flo
                                int64_t i0, int64_t j0, int wm, int wn) {
   constexpr int RSB = BN + 16;  // LDS bytes per staged row of codes
   const int tid = threadIdx.x, lane = tid & 63;
-  const uint32_t bid = blockIdx.y * gridDim.x + blockIdx.x, total = gridDim.x * gridDim.y;
+  const uint32_t bid = blockIdx.y * prob_nblk(g) + prob_block(g), total = prob_nblk(g) * gridDim.y;
   const int64_t rows_left = g.Mc - i0, cols_left = g.Nc - j0;
   uint32_t mx = 0;
 #pragma unroll
@@ -669,7 +669,7 @@ void gemm3_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int tm, tn;
-  tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  tile_coords_xcd(prob_block(g), g.tiles_m, g.tiles_n, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
   uint8_t* const sbias = smem3 + gemm3_bias_off<BM, BN>();  // BiasStage area
 

@@ -28,8 +28,10 @@ namespace fp8l {
 constexpr int kGemm4BiasOff =
     kStages3 * 512 * kBK3 > 256 * (256 * 2 + 16) ? kStages3 * 512 * kBK3 : 256 * (256 * 2 + 16);
 
+// The kernel's work for one block, on the dynamic LDS at smem4 (also run by
+// the grouped launch of fp8l_gemm_pair.hpp).
 template <int LA, int LB, int FA, int FB, int EPI = kEpiBF16, int OF = kE4M3>
-__global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
+FP8L_DEV void gemm4_body(GemmArgs& g, uint8_t* smem4) {
   batch_slice(g);
   constexpr int BM = 256, BN = 256, WGM = 2, WGN = 4, NW = WGM * WGN;
   using OA = Op3<LA, BM, NW>;
@@ -40,11 +42,10 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
   constexpr int kStep = OA::kBytes + OB::kBytes;
   constexpr int kDma = OA::kPerWave + OB::kPerWave;  // 2 + 2
   static_assert(kDma == 4, "one DMA load after each of the four read groups");
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem4[];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int tm, tn;
-  tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  tile_coords_xcd(prob_block(g), g.tiles_m, g.tiles_n, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
   uint8_t* const sbias = smem4 + kGemm4BiasOff;  // BiasStage area
 
@@ -252,6 +253,12 @@ __global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
       __builtin_nontemporal_store(*reinterpret_cast<const v4u*>(smem4 + r * RS + ch * 16),
                                   reinterpret_cast<v4u*>(g.c + (i0 + r) * g.ldc + j0 + 8 * ch));
   }
+}
+
+template <int LA, int LB, int FA, int FB, int EPI = kEpiBF16, int OF = kE4M3>
+__global__ __launch_bounds__(512, 1) void gemm4_kernel(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem4[];
+  gemm4_body<LA, LB, FA, FB, EPI, OF>(g, smem4);
 }
 
 constexpr int gemm4_lds_bytes() { return kGemm4BiasOff + BiasStage<256>::kBytes; }

@@ -178,8 +178,10 @@ constexpr int kGemm5BiasOff = kStages3 * 2 * 256 * kBK3 > 128 * (128 * 2 + 16)
                                   ? kStages3 * 2 * 256 * kBK3
                                   : 128 * (128 * 2 + 16);
 
+// The kernel's work for one block, on the dynamic LDS at smem5 (also run by
+// the grouped launch of fp8l_gemm_pair.hpp).
 template <int LA, int LB, int FA, int FB>
-__global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
+FP8L_DEV void gemm5_body(GemmArgs& g, uint8_t* smem5) {
   batch_slice(g);
   constexpr int BM = 128, BN = 128, NW = 8;
   using OA = Stage128<LA, BM, NW>;  // 16 KB per stage, two DMA loads per wave
@@ -187,11 +189,10 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
   static_assert(OA::kLoads == 2 && OB::kLoads == 2, "two loads per operand per stage");
   constexpr int kStage = OA::kBytes + OB::kBytes;  // 128 bytes of K: A then B
   constexpr int kDma = 4;                          // loads per wave per stage
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem5[];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int tm, tn;
-  tile_coords_xcd(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn);
+  tile_coords_xcd(prob_block(g), g.tiles_m, g.tiles_n, tm, tn);
   const int64_t i0 = (int64_t)tm * BM, j0 = (int64_t)tn * BN;
   uint8_t* const sbias = smem5 + kGemm5BiasOff;  // BiasStage area
 
@@ -397,6 +398,12 @@ __global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
       __builtin_nontemporal_store(*reinterpret_cast<const v4u*>(smem5 + r * RS + ch * 16),
                                   reinterpret_cast<v4u*>(g.c + (i0 + r) * g.ldc + j0 + 8 * ch));
   }
+}
+
+template <int LA, int LB, int FA, int FB>
+__global__ __launch_bounds__(512, 1) void gemm5_kernel(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem5[];
+  gemm5_body<LA, LB, FA, FB>(g, smem5);
 }
 
 constexpr int gemm5_lds_bytes() { return kGemm5BiasOff + BiasStage<128>::kBytes; }

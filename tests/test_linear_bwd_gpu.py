@@ -1,12 +1,15 @@
-"""GPU parity of the two-stream backward (fp8_linear_bwd).
+"""GPU parity of the backward entry point fp8_linear_bwd: on two streams,
+and on one stream, where the dX and dW GEMMs run as one grouped launch.
 
 By contract its results are those of fp8_linear_bwd_dw followed by
 fp8_linear_bwd_dx from the same g: the kernels are the same and
 deterministic, so every output byte (G8, dX, dW, db, scales, amax, ring
-state) must equal the one-stream pair's, run on copies of the same inputs.
-One small case is also checked against the oracle directly.  The two
-streams are torch streams of default priority; the dW stream is joined
-back before anything is read.
+state) must equal the pair's, run on copies of the same inputs, wherever
+the grouped launch keeps each GEMM's own tile.  Where it does not (the qkv
+projection's dW: 8-wave 128x128 tiles in the group, 4-wave alone) every
+element is compared with the oracle instead.  Two cases are also checked
+against the oracle directly.  The two streams are torch streams of default
+priority; the dW stream is joined back before anything is read.
 """
 
 import numpy as np
@@ -130,6 +133,53 @@ def test_two_stream_matches_pair(M, N, K, mode):
         _assert_same(a.snapshot(), b.snapshot(), f"step {step}")
 
 
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("mode", ["ring", "dynamic", "prequantized"])
+def test_grouped_one_stream_matches_pair(M, N, K, mode):
+    """stream_dw = stream: dX and dW as one grouped launch (the 200x264x136
+    case takes the general kernel one GEMM at a time)."""
+    G, x8, w8, rng = _inputs(M, N, K, seed=M + 5 * N + K)
+    g_pre = None
+    if mode == "prequantized":
+        tab = O.decode_table(O.E5M2)
+        fin = np.array([c for c in range(256) if np.isfinite(tab[c])], np.uint8)
+        g_pre = (rng.choice(fin, size=(M, N)), 64.0)
+    ring_a = F.ScaleRing(4) if mode == "ring" else None
+    ring_b = F.ScaleRing(4) if mode == "ring" else None
+    a = Bwd(G, x8, 2.0, w8, 0.5, ring_a, g_pre)
+    b = Bwd(G, x8, 2.0, w8, 0.5, ring_b, g_pre)
+    steps = 3 if mode == "ring" else 1
+    for step in range(steps):
+        f = 1.0 + step
+        a.G.copy_((a.G.float() * f).to(torch.bfloat16))
+        b.G.copy_((b.G.float() * f).to(torch.bfloat16))
+        a.run_pair()
+        b.run_two_stream(None)
+        _assert_same(a.snapshot(), b.snapshot(), f"step {step}")
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 4608, 1536), (512, 1536, 6912)])
+def test_grouped_against_oracle_full(M, N, K):
+    """The grouped launch where it changes a GEMM's tile (2048 x 4608 x 1536,
+    the qkv projection's backward: dW on 8-wave 128x128 tiles) and a
+    few-tile small-M case (the down projection at M = 512), every element of
+    dX, dW and db against the oracle over two ring steps."""
+    G, x8, w8, _ = _inputs(M, N, K, seed=23 + M)
+    ring, oring = F.ScaleRing(4), O.ScaleRing(4)
+    b = Bwd(G, x8, 2.0, w8, 0.5, ring)
+    for step in range(2):
+        Gs = (G.float() * (1.0 + step)).to(torch.bfloat16)
+        b.G.copy_(Gs.to(DEV))
+        b.run_two_stream(None)
+        og8, osg, oag = O.quantize_step(f32(Gs), O.E5M2, oring)
+        assert np.array_equal(u8(b.g8), og8)
+        assert f32_scalar(b.sg) == osg and f32_scalar(b.ag) == oag
+        assert_ring_matches(ring, oring)
+        check_gemm(bf16_bits(b.dx), O.linear_bwd_dx(og8, O.E5M2, w8, O.E4M3, osg, 0.5), "dx")
+        check_gemm(bf16_bits(b.dw), O.linear_bwd_dw(og8, O.E5M2, x8, O.E4M3, osg, 2.0), "dw")
+        check_gemm(bf16_bits(b.db), O.bias_grad(f32(Gs).astype(np.float64)), "db")
+
+
 # empty problems: no G rows (dW and db are zeros), no G columns (dX is
 # zeros), no features (only db has elements)
 @pytest.mark.parametrize("M,N,K", [(0, 64, 32), (48, 0, 32), (48, 64, 0)])
@@ -156,13 +206,14 @@ def test_two_stream_degenerate_sizes(M, N, K, mode):
 
 
 def test_same_stream_and_no_db():
+    """stream_dw = stream (the grouped launch), without db."""
     M, N, K = 384, 512, 256
     G, x8, w8, _ = _inputs(M, N, K, seed=5)
     a = Bwd(G, x8, 1.0, w8, 4.0, F.ScaleRing(8), want_db=False)
     b = Bwd(G, x8, 1.0, w8, 4.0, F.ScaleRing(8), want_db=False)
     for _ in range(2):
         a.run_pair()
-        b.run_two_stream(None)  # stream_dw = stream: all in order on one stream
+        b.run_two_stream(None)  # stream_dw = stream: one grouped launch
         _assert_same(a.snapshot(), b.snapshot(), "same stream")
 
 
