@@ -145,6 +145,10 @@ class Layer:
         self.bwd = F.bind_fp8_linear_bwd(self.G, F.FP8_E5M2, x8q, w8q, self.dx, self.dw, self.db,
                                          self.ws, self.rg, self.g8, self.sg, self.ag,
                                          stream=stream, stream_dw=side)
+        # the backward on one stream: the dX and dW GEMMs as one grouped launch
+        self.bwd_one = F.bind_fp8_linear_bwd(self.G, F.FP8_E5M2, x8q, w8q, self.dx, self.dw,
+                                             self.db, self.ws, self.rg, self.g8, self.sg, self.ag,
+                                             stream=stream, stream_dw=stream)
         # the same backward as two one-stream calls (the dW call quantizes G),
         # for a step that brackets the dX GEMM alone
         self.bwd_dw = F.bind_fp8_linear_bwd_dw(self.G, F.FP8_E5M2, x8q, self.dw, self.db, self.ws,
@@ -588,7 +592,7 @@ def ceilings(torch, stream):
     return res
 
 
-def layer_step(layers, stream, side):
+def layer_step(layers, stream, side, grouped=False):
     """One training step over the linears in a training step's order: every
     forward (the quantize launch, then the GEMM), then every backward in
     reverse order, each one fp8_linear_bwd (G quantized once, with db's
@@ -599,7 +603,8 @@ def layer_step(layers, stream, side):
 
     launch(kind, li, fn) issues call fn of kind "fwd" or "bwd" of linear li
     (the timed region brackets one of them with events); by default it just
-    calls fn."""
+    calls fn.  grouped: each backward on stream alone, its dX and dW GEMMs
+    in one grouped launch (no second stream, no join)."""
     def plain(kind, li, fn):
         fn()
 
@@ -607,8 +612,9 @@ def layer_step(layers, stream, side):
         for li, L in enumerate(layers):
             launch("fwd", li, L.fwd)
         for li in reversed(range(len(layers))):
-            launch("bwd", li, layers[li].bwd)
-        stream.wait_stream(side)
+            launch("bwd", li, layers[li].bwd_one if grouped else layers[li].bwd)
+        if not grouped:
+            stream.wait_stream(side)
     return step
 
 
@@ -1056,28 +1062,35 @@ def main():
             "flops": sum(layers[ev_layer[si]].flops for si in brack) / len(brack),
             "launches": len(live_ms)}
 
-    # ---- the same step captured as one HIP graph and replayed
-    graph_ms_per_step = None
-    try:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            step()
-        torch.cuda.synchronize()
-        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            g.replay()
-            gs.record(stream)
-            for _ in range(args.steps):
+    # ---- the same step captured as one HIP graph and replayed (one copy),
+    # with the two-stream backward and with the grouped one-stream backward
+    def graph_ms(fn):
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                fn()
+            torch.cuda.synchronize()
+            gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
                 g.replay()
-            ge.record(stream)
-        torch.cuda.synchronize()
-        graph_ms_per_step = gs.elapsed_time(ge) / args.steps
-    except Exception as exc:  # graph capture is an extra measurement only
-        print(f"graph capture skipped: {exc}", file=sys.stderr)
+                gs.record(stream)
+                for _ in range(args.steps):
+                    g.replay()
+                ge.record(stream)
+            torch.cuda.synchronize()
+            return gs.elapsed_time(ge) / args.steps
+        except Exception as exc:  # graph capture is an extra measurement only
+            print(f"graph capture skipped: {exc}", file=sys.stderr)
+            return None
+    step_grouped = layer_step(layers, stream, side, grouped=True)
+    graph_ms_per_step = graph_ms(step)
+    graph_grouped_ms = graph_ms(step_grouped)
 
     # ---- the warm step beside it: copy 0 of the layer every step, so its
-    # inputs stay in the MALL from one step to the next
+    # inputs stay in the MALL from one step to the next; and the same with
+    # the grouped one-stream backward
     warm_ms = timed_steps_ms(torch, step, args.steps, stream)
+    warm_grouped_ms = timed_steps_ms(torch, step_grouped, args.steps, stream)
     rotation = {"copies": R, "input_MB": round(R * per_set / 1e6, 1)}
     del steps_of, sets
     torch.cuda.synchronize()
@@ -1161,6 +1174,11 @@ def main():
         "graph_ms_per_step": None if graph_ms_per_step is None else round(graph_ms_per_step, 4),
         "graph_TFLOPs": None if graph_ms_per_step is None else
         round(step_flops / (graph_ms_per_step * 1e-3) / 1e12, 2),
+        "grouped_backward": {
+            "note": "each backward as fp8_linear_bwd on one stream: G quantize, then dX and dW "
+                    "GEMMs in one grouped launch",
+            "warm_ms_per_step": round(warm_grouped_ms, 4),
+            "graph_ms_per_step": None if graph_grouped_ms is None else round(graph_grouped_ms, 4)},
         "gemm_us_per_step": {g: round(v, 1) for g, v in tot.items()},
         "per_linear": per,
         "timing_method": "isolated kernels: 20 warm-up launches, then 200 launches in batches of "
