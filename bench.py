@@ -577,6 +577,21 @@ def ceilings(torch, stream):
                                   reps=20, warm=3, batch=5)
             res["mfma_TFLOPs"][f"{label}_{blocks}cu"] = round(
                 P.mfma_flops(blocks, iters) / (st["median"] * 1e-6) / 1e12, 1)
+    # fixed cost of a GEMM launch: the layer's output shapes at K = 64 (one
+    # K step: prologue, one stage, epilogue, launch and block-end spread)
+    # beside K = 1536, through the forward entry point on zero codes
+    import scaled_quantize_fp8_amd as F
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    res["gemm_fixed_us"] = {}
+    for M, N in ((2048, 6912), (2048, 4608), (2048, 1536)):
+        y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        row = {}
+        for K in (64, 1536):
+            a = F.Quantized(torch.zeros(M, K, dtype=torch.uint8, device="cuda"), F.FP8_E4M3, one)
+            b = F.Quantized(torch.zeros(N, K, dtype=torch.uint8, device="cuda"), F.FP8_E4M3, one)
+            fn = F.bind_fp8_linear_fwd(a, b, None, F.FP8_E4M3, y, stream=stream)
+            row[f"K{K}"] = batched_stats_us(torch, fn, stream, reps=100, warm=10)["median"]
+        res["gemm_fixed_us"][f"{M}x{N}"] = row
     nbytes = 512 << 20
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
