@@ -592,6 +592,24 @@ def ceilings(torch, stream):
             fn = F.bind_fp8_linear_fwd(a, b, None, F.FP8_E4M3, y, stream=stream)
             row[f"K{K}"] = batched_stats_us(torch, fn, stream, reps=100, warm=10)["median"]
         res["gemm_fixed_us"][f"{M}x{N}"] = row
+    # fixed cost of a quantize launch: the standalone quantize (seeded ring,
+    # last-block election) of bf16 tensors from one block's worth of
+    # elements to the layer's largest, and a launch of the stream probe over
+    # 16 bytes (the floor of any launch)
+    res["quantize_us"] = {}
+    for n in (4096, 1 << 20, 3 << 20, 14 << 20):
+        x = torch.randn(n, device="cuda").to(torch.bfloat16)
+        q = torch.empty(n, dtype=torch.uint8, device="cuda")
+        su, am = (torch.zeros(1, dtype=torch.float32, device="cuda") for _ in range(2))
+        ring = F.ScaleRing(16, stream=stream)
+        fn = F.bind_fp8_quantize(x, F.FP8_E4M3, q, ring, su, am, stream=stream)
+        fn()
+        res["quantize_us"][f"n{n}"] = batched_stats_us(torch, fn, stream, reps=100, warm=10)["median"]
+    tiny = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    sink0 = torch.zeros(4, dtype=torch.int32, device="cuda")
+    res["launch_floor_us"] = batched_stats_us(
+        torch, lambda: P.stream(tiny, tiny, 16, 0, 1, sink0, stream), stream, reps=100,
+        warm=10)["median"]
     nbytes = 512 << 20
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
