@@ -934,6 +934,10 @@ def main():
             f.write("\n")
         print(json.dumps(rec))
         return
+    if args.steps < 2:
+        print("bench.py needs --steps >= 2 (the live GEMM timing pairs two bracketed steps)",
+              file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is a design note, not a built path)", file=sys.stderr)
@@ -1024,46 +1028,53 @@ def main():
     qsweep = cold_quant_sweep(torch, sets, stream)
 
     # ---- timed region: exactly args.steps eager steps, step s on copy s mod R
-    # of the layer.  In every other step (s even) one launch of the GEMM
-    # kind that dominates the isolated timings (forward or dX) is bracketed
-    # with events on stream, of linear (s / 2) mod n, so that every linear's
-    # launch is timed live at least once while only half the steps carry an
-    # event pair (an event record costs the stream a few microseconds).  A
-    # bracketed forward runs as fp8_quantize_pair + fp8_linear_fwd(X8, W8);
-    # a bracketed dX GEMM needs the backward as two calls on stream
-    # (fp8_linear_bwd_dw, then the dX alone).  The event pairs are created up
-    # front, outside the timed region.
+    # of the layer.  Every other step (s even) carries one event pair on
+    # stream, around the forward of linear (i / 2) mod n for the i-th such
+    # step, issued as its two calls: the paired X/W quantize
+    # (fp8_quantize_pair) and the GEMM (fp8_linear_fwd on X8, W8).  For
+    # even i the pair brackets quantize and GEMM, for odd i the quantize
+    # alone (the GEMM follows outside the bracket), so per linear
+    #   GEMM time = [quantize + GEMM] - [quantize],
+    # the GEMM's launch-to-launch time in a busy stream, with the events'
+    # own cost (a marker after a kernel adds a dispatch round trip to what
+    # it brackets) and the quantize cancelling out.  A bracket around the
+    # GEMM alone is reported beside it (raw, and less an overhead measured
+    # on isolated launches).  The event pairs are created up front, outside
+    # the timed region.  (Where the dX GEMM dominates the isolated timings,
+    # the same scheme brackets fp8_linear_bwd_dw + the dX GEMM against
+    # fp8_linear_bwd_dw alone.)
     dom = "fwd" if tot["fwd"] >= tot["dx"] else "dx"
     brack = [si for si in range(args.steps) if si % 2 == 0]
-    if len(brack) < len(layers):
+    if len(brack) < 2 * len(layers):
         brack = list(range(args.steps))
     ev = {si: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for si in brack}
-    ev_layer = {}
+    ev_what = {}  # step -> (linear, with_gemm)
 
     def bracketing(step_i):
         ls = sets[step_i % R]
-        target = (brack.index(step_i) % len(ls)) if step_i in ev else -1
+        if step_i in ev:
+            i = brack.index(step_i)
+            target, with_gemm = (i // 2) % len(ls), i % 2 == 0
+        else:
+            target, with_gemm = -1, False
 
         def launch(kind, li, fn):
             if li != target or kind != ("fwd" if dom == "fwd" else "bwd"):
                 fn()
                 return
             a, b_ = ev[step_i]
-            ev_layer[step_i] = li
-            if dom == "fwd":
-                # the same forward as two calls, so the GEMM launch can be
-                # bracketed alone: the quantize (with its ring election),
-                # then the GEMM on the quantized operands
-                ls[li].quant_xw()
-                a.record(stream)
-                ls[li].gemm_fwd()
+            ev_what[step_i] = (li, with_gemm)
+            first, gemm = ((ls[li].quant_xw, ls[li].gemm_fwd) if dom == "fwd"
+                           else (ls[li].bwd_dw, ls[li].bwd_dx))
+            a.record(stream)
+            first()
+            if with_gemm:
+                gemm()
                 b_.record(stream)
             else:
-                ls[li].bwd_dw()
-                a.record(stream)
-                ls[li].bwd_dx()
                 b_.record(stream)
+                gemm()
         return launch
 
     t_start = torch.cuda.Event(enable_timing=True)
@@ -1082,18 +1093,23 @@ def main():
     step_flops = sum(3 * L.flops for L in layers)
     tflops = step_flops / (ms_per_step * 1e-3) / 1e12
 
-    # live launch durations of the dominant kind: average over the bracketed
-    # launches, with the average flops of the same launches; per step, the
-    # sum over the linears of each one's average live duration
-    live_ms = [ev[si][0].elapsed_time(ev[si][1]) for si in brack]
-    by_layer = {}
-    for si, ms in zip(brack, live_ms):
-        by_layer.setdefault(ev_layer[si], []).append(ms)
-    live = {"avg_ms": sum(live_ms) / len(live_ms),
-            "total_ms": (sum(sum(v) / len(v) for v in by_layer.values())
-                         if len(by_layer) == len(layers) else None),
-            "flops": sum(layers[ev_layer[si]].flops for si in brack) / len(brack),
-            "launches": len(live_ms)}
+    # per linear: mean bracketed [first call + GEMM] and [first call] times;
+    # the GEMM's live time is their difference
+    sums = {}
+    for si in brack:
+        li, with_gemm = ev_what[si]
+        ms = ev[si][0].elapsed_time(ev[si][1])
+        sums.setdefault(li, {True: [], False: []})[with_gemm].append(ms)
+    covered = sorted(li for li, d in sums.items() if d[True] and d[False])
+    mean = lambda v: sum(v) / len(v)
+    gemm_us = {li: 1e3 * (mean(sums[li][True]) - mean(sums[li][False])) for li in covered}
+    live = {"avg_us": mean(list(gemm_us.values())),
+            "flops": mean([layers[li].flops for li in covered]),
+            "per_linear_us": {layers[li].name: round(v, 2) for li, v in gemm_us.items()},
+            "bracketed_with_gemm_us": {layers[li].name: round(1e3 * mean(sums[li][True]), 2)
+                                       for li in covered},
+            "launches": sum(len(sums[li][True]) for li in covered),
+            "total_us": sum(gemm_us.values()) if len(covered) == len(layers) else None}
 
     # ---- the same step captured as one HIP graph and replayed (one copy),
     # with the two-stream backward and with the grouped one-stream backward
@@ -1144,24 +1160,39 @@ def main():
     }
     overhead_us = sum(bracket_overhead_us(torch, getattr(L, {"fwd": "gemm_fwd", "dx": "bwd_dx"}[dom]),
                                           20, stream) for L in layers) / len(layers)
-    raw = live["flops"] / (live["avg_ms"] * 1e-3) / 1e12
-    corrected_us = live["avg_ms"] * 1e3 - overhead_us
-    achieved = live["flops"] / (corrected_us * 1e-6) / 1e12
+    achieved = live["flops"] / (live["avg_us"] * 1e-6) / 1e12
+    # beside it: a bracket around the GEMM alone (its first call outside the
+    # bracket), taken after the timed region on copy 0, raw and less the
+    # isolated bracket overhead
+    alone = []
+    for L in layers:
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            (L.quant_xw if dom == "fwd" else L.bwd_dw)()
+            a.record(stream)
+            (L.gemm_fwd if dom == "fwd" else L.bwd_dx)()
+            b_.record(stream)
+        b_.synchronize()
+        alone.append(1e3 * a.elapsed_time(b_))
+    alone_us = sum(alone) / len(alone)
     traffic = load_traffic(traffic_key(dom, args.workload))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_FP8_DENSE_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP8_DENSE_TFLOPS, 4),
                 "traffic": traffic,
                 "kernel": kernel_names[dom],
-                "launch_avg_us": round(corrected_us, 2),
-                "launch_avg_us_raw": round(live["avg_ms"] * 1e3, 2),
-                "live_bracket_overhead_us": round(overhead_us, 2),
-                "achieved_raw": round(raw, 2),
-                "frac_raw": round(raw / MI355X_FP8_DENSE_TFLOPS, 4),
+                "launch_avg_us": round(live["avg_us"], 2),
+                "live_method": "per linear, bracketed [first call + GEMM] minus bracketed [first "
+                               "call], in the timed steps (events on the kernel's stream)",
+                "live_per_linear_us": live["per_linear_us"],
+                "live_bracketed_with_gemm_us": live["bracketed_with_gemm_us"],
+                "gemm_alone_bracket_us_raw": round(alone_us, 2),
+                "gemm_alone_bracket_us_less_overhead": round(alone_us - overhead_us, 2),
+                "isolated_bracket_overhead_us": round(overhead_us, 2),
                 "trace": load_trace_record(dom, args.workload),
                 "flops_per_launch": live["flops"],
                 "live_launches": live["launches"],
-                "live_us_per_step": (None if live["total_ms"] is None
-                                     else round(live["total_ms"] * 1e3, 1)),
+                "live_us_per_step": (None if live["total_us"] is None
+                                     else round(live["total_us"], 1)),
                 "isolated_gemm_us_per_step": {k: round(v, 1) for k, v in tot.items()},
                 "mfma_util_pct_by_kind": load_mfma(args.workload),
                 "dominant_gemm_by_isolated_totals": dominant_isolated}
@@ -1183,8 +1214,8 @@ def main():
                    "gemms_per_step": 3 * len(layers)},
         "step_schedule": "every forward in order as fp8_linear_fwd(X, W) (quantize without "
                          "election; the GEMM folds the rings), in every other step one of them "
-                         "split into fp8_quantize_pair + fp8_linear_fwd(X8, W8) for the event "
-                         "bracket; then every backward in reverse order as fp8_linear_bwd (dX on "
+                         "split into fp8_quantize_pair + fp8_linear_fwd(X8, W8) inside an event "
+                         "pair; then every backward in reverse order as fp8_linear_bwd (dX on "
                          "the main stream, dW and db on a second stream after the G quantize); "
                          "one join of the two streams per step",
         "pct_fp8_peak": round(100 * tflops / MI355X_FP8_DENSE_TFLOPS, 2),
