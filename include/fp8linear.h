@@ -341,11 +341,9 @@ int fp8_linear_bwd_dw_noalloc(int64_t M, int64_t N, int64_t K, fp8_operand_t g, 
  * then never waits for a dW GEMM, which fills the CUs the dX work leaves
  * idle.  stream_dw == stream runs everything on stream, the dX and dW GEMMs
  * as one grouped launch (both problems' tiles in one grid, the longer tiles
- * first) when G8 is e5m2, W8 and X8 are e4m3 and both operand sets take the
- * tiled kernels (16-byte aligned, dimensions multiples of 16); otherwise
- * one after the other.  The results are the same bits as the two calls
- * wherever the grouped launch keeps the tile each lone GEMM would use (it
- * runs 128x128 tiles on 8 waves where a lone launch may pick 4 waves).
+ * first) when G8 is e5m2, W8 and X8 are e4m3 and each GEMM alone would run
+ * on one of the 8-wave tiled kernels; otherwise one after the other.  The
+ * results are the same bits either way.
  *
  *   g, ring_g, g8_out, sg_used, amax_g: as in fp8_linear_bwd_dw.
  *   x8, dw, db, db_ws: as in fp8_linear_bwd_dw (dw, db written on stream_dw;

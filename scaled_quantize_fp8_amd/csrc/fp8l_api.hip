@@ -331,9 +331,14 @@ int forced_tile() {
 }
 
 // Tile choice (measured crossovers on the layer shapes; tiles counted over
-// all batch slices).  Larger tiles move
-// fewer operand bytes per MFMA but leave CUs idle when the output has few
-// tiles, and one tile per CU cannot overlap its epilogue with another loop.
+// all batch slices).  Larger tiles move fewer operand bytes per MFMA but
+// leave CUs idle when the output has few tiles, and one tile per CU cannot
+// overlap its epilogue with another loop.
+//  * 128x128, 4 waves, two blocks per CU (gemm3): when K <= 1024 and the
+//    tiles fit one round at two blocks per CU.  With a short K loop the
+//    fixed phases (first stage, epilogue burst) weigh most, and the second
+//    block on each CU overlaps them (2048 x 4096 x 1024: 16.1 us against
+//    19.4 on 256x256; 4608 x 1536 x 512: 8.6 against 10.1 on 256x128).
 //  * 256x256, 8 waves (gemm4): when its tiles fill at least half the CUs.
 //  * 128x128, 8 waves (gemm5): when the 128x128 tiles fit one per CU; the
 //    block's 8 waves give each SIMD two waves.
@@ -341,11 +346,12 @@ int forced_tile() {
 //    256x128 tiles fit one per CU (the 4608 x 1536 weight gradient at
 //    K = 2048: 18.7 us against 21.3 us for two 128x128 blocks per CU).
 //  * 128x128, 4 waves, two blocks per CU (gemm3): otherwise.
-int choose_tile(int64_t Mc, int64_t Nc, int64_t batch) {
+int choose_tile(int64_t Mc, int64_t Nc, int64_t Kc, int64_t batch) {
   const int64_t cus = cu_count();
   const int64_t tiles256 = batch * ((Mc + 255) / 256) * ((Nc + 255) / 256);
   const int64_t tiles128 = batch * ((Mc + 127) / 128) * ((Nc + 127) / 128);
   const int64_t tiles256x128 = batch * ((Mc + 255) / 256) * ((Nc + 127) / 128);
+  if (Kc <= 1024 && tiles128 <= 2 * cus) return kTile128x128;
   if (2 * tiles256 >= cus) return kTile256x256w8;
   if (tiles128 <= cus) return kTile128x128w8;
   return tiles256x128 <= cus ? kTile256x128 : kTile128x128;
@@ -458,7 +464,7 @@ template <int LA, int LB>
 void launch_gemm_l(GemmArgs& g, int fa, int fb, hipStream_t st) {
   int tile = forced_tile();
   if (!fast_path_ok<LA, LB>(g)) tile = kTileV1;
-  if (tile == kTileAuto) tile = choose_tile(g.Mc, g.Nc, g.batch);
+  if (tile == kTileAuto) tile = choose_tile(g.Mc, g.Nc, g.Kc, g.batch);
   switch (tile) {
     case kTile256x256: launch_gemm3_f<256, 256, 2, 2, LA, LB>(g, fa, fb, st); return;
     case kTile256x128: launch_gemm3_f<256, 128, 2, 2, LA, LB>(g, fa, fb, st); return;
@@ -474,12 +480,10 @@ void launch_gemm_l(GemmArgs& g, int fa, int fb, hipStream_t st) {
 }
 
 // The grouped backward (fp8l_gemm_pair.hpp): dX (A = G8 k-contiguous, B =
-// W8 crosswise) and dW (both crosswise) in one launch.  Each problem takes
-// the tile its own launch would (256x256 when its tiles fill at least half
-// the CUs, else 128x128 with 8 waves; the 4-wave 128x128 block that a lone
-// launch may pick is replaced by the 8-wave one, since the grid runs
-// 512-thread blocks).  The problem whose tiles take longer (tile area times
-// K) gets the first block range.
+// W8 crosswise) and dW (both crosswise) in one launch, each problem on the
+// 8-wave kernel its own launch would take (256x256 or 128x128).  The
+// problem whose tiles take longer (tile area times K) gets the first block
+// range.
 template <class BX, class BW>
 void launch_pair_t(GemmArgs& dx, GemmArgs& dw, hipStream_t st) {
   constexpr int lds = pair_lds_bytes<BX, BW>();
@@ -511,15 +515,20 @@ void launch_pair_t(GemmArgs& dx, GemmArgs& dw, hipStream_t st) {
                      dim3(512), lds, st, dx, dw);
 }
 
-// Grouped launch when both problems take the fast kernels with the standard
-// recipe's formats (G in e5m2, W8 and X8 in e4m3) and no tile is forced;
-// false: the caller launches them one by one.
+// Grouped launch when both problems would take an 8-wave kernel on their
+// own (so the grouped results are the two launches' bits), with the
+// standard recipe's formats (G in e5m2, W8 and X8 in e4m3) and no tile
+// forced; false: the caller launches them one by one.
 bool launch_pair(GemmArgs& dx, GemmArgs& dw, int fmt_g, int fmt_w, int fmt_x, hipStream_t st) {
   if (fmt_g != kE5M2 || fmt_w != kE4M3 || fmt_x != kE4M3 || forced_tile() != kTileAuto) return false;
   if (dx.batch != 1 || dw.batch != 1) return false;
   if (!fast_path_ok<kKContig, kCross>(dx) || !fast_path_ok<kCross, kCross>(dw)) return false;
-  const bool big_x = choose_tile(dx.Mc, dx.Nc, 1) == kTile256x256w8;
-  const bool big_w = choose_tile(dw.Mc, dw.Nc, 1) == kTile256x256w8;
+  const int tx = choose_tile(dx.Mc, dx.Nc, dx.Kc, 1), tw = choose_tile(dw.Mc, dw.Nc, dw.Kc, 1);
+  const bool eight = [](int t) { return t == kTile256x256w8 || t == kTile128x128w8; }(tx) &&
+                     (tw == kTile256x256w8 || tw == kTile128x128w8);
+  if (!eight) return false;
+  const bool big_x = tx == kTile256x256w8;
+  const bool big_w = tw == kTile256x256w8;
   using X4 = Body4<kKContig, kCross, kE5M2, kE4M3>;
   using X5 = Body5<kKContig, kCross, kE5M2, kE4M3>;
   using W4 = Body4<kCross, kCross, kE5M2, kE4M3>;

@@ -4,11 +4,9 @@ and on one stream, where the dX and dW GEMMs run as one grouped launch.
 By contract its results are those of fp8_linear_bwd_dw followed by
 fp8_linear_bwd_dx from the same g: the kernels are the same and
 deterministic, so every output byte (G8, dX, dW, db, scales, amax, ring
-state) must equal the pair's, run on copies of the same inputs, wherever
-the grouped launch keeps each GEMM's own tile.  Where it does not (the qkv
-projection's dW: 8-wave 128x128 tiles in the group, 4-wave alone) every
-element is compared with the oracle instead.  Two cases are also checked
-against the oracle directly.  The two streams are torch streams of default
+state) must equal the pair's, run on copies of the same inputs (the
+grouped launch runs each GEMM on the kernel its own launch would take).
+Three cases are also checked against the oracle directly, every element.  The two streams are torch streams of default
 priority; the dW stream is joined back before anything is read.
 """
 
@@ -160,10 +158,10 @@ def test_grouped_one_stream_matches_pair(M, N, K, mode):
 
 @pytest.mark.parametrize("M,N,K", [(2048, 4608, 1536), (512, 1536, 6912)])
 def test_grouped_against_oracle_full(M, N, K):
-    """The grouped launch where it changes a GEMM's tile (2048 x 4608 x 1536,
-    the qkv projection's backward: dW on 8-wave 128x128 tiles) and a
-    few-tile small-M case (the down projection at M = 512), every element of
-    dX, dW and db against the oracle over two ring steps."""
+    """The one-stream backward of the qkv projection (its dW on 256x128
+    tiles, launched alone) and a few-tile small-M case (the down projection
+    at M = 512), every element of dX, dW and db against the oracle over two
+    ring steps."""
     G, x8, w8, _ = _inputs(M, N, K, seed=23 + M)
     ring, oring = F.ScaleRing(4), O.ScaleRing(4)
     b = Bwd(G, x8, 2.0, w8, 0.5, ring)
