@@ -244,6 +244,11 @@ RingFold fold_of(const fp8_ring_t* r, int32_t fmt, float* amax_out) {
   return f;
 }
 
+// The fold of a ring whose groups a deferring launch filled, as a launch of
+// its own (one wave): the FP8-output GEMM's codes have no consuming GEMM
+// here to hand the fold to.
+__global__ __launch_bounds__(64) void ring_fold_kernel(RingFold f) { ring_fold_wave(f); }
+
 // One quantize.  may_defer: the caller launches a GEMM on the codes next,
 // on the same stream, which folds the ring when this returns true.
 bool enqueue_quant(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, uint8_t* q,
@@ -1164,10 +1169,16 @@ int fp8_gemm_fp8out(int64_t M, int64_t N, int64_t K, fp8_operand_t a, fp8_operan
     if (e4) launch_fp8out<kEpiFp8Seed, kE4M3>(g, fa, fb, stream);
     else launch_fp8out<kEpiFp8Seed, kE5M2>(g, fa, fb, stream);
     ring_out->seeded = 1;
-  } else if (e4) {
-    launch_fp8out<kEpiFp8Ring, kE4M3>(g, fa, fb, stream);
   } else {
-    launch_fp8out<kEpiFp8Ring, kE5M2>(g, fa, fb, stream);
+    // steady state: the blocks end without an election and a one-wave
+    // launch folds the ring after the GEMM (a window longer than one wave
+    // keeps the last-block fold)
+    g.odefer = can_defer(ring_out) ? 1 : 0;
+    if (e4) launch_fp8out<kEpiFp8Ring, kE4M3>(g, fa, fb, stream);
+    else launch_fp8out<kEpiFp8Ring, kE5M2>(g, fa, fb, stream);
+    if (g.odefer)
+      hipLaunchKernelGGL(ring_fold_kernel, dim3(1), dim3(64), 0, stream,
+                         fold_of(ring_out, fmt_out, amax_out));
   }
   return hip_status();
 }

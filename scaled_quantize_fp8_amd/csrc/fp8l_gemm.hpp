@@ -86,13 +86,16 @@ struct GemmArgs {
   int64_t bsa, bsb, bsc;
   int32_t batch;  // >= 1
   // FP8 output (fp8_gemm_fp8out): codes c8 [Mc, ldc], made with the output
-  // ring's scale; the launch's last block folds max |y| into that ring.
+  // ring's scale; the launch's last block folds max |y| into that ring, or,
+  // with odefer, each block only adds its max to its election group and a
+  // one-wave launch after the GEMM folds the groups (ring_fold_wave).
   uint8_t* c8;
   RingHdr* oring;
   float* ohist;
   int32_t ohist_len;
   float* oscale_used;
   float* oamax;
+  int32_t odefer;
   // ring folds left by the quantizes of this GEMM's operands (block 0)
   RingFold fold[2];
   // This problem's blocks within the launch: x indices blk0 .. blk0 + nblk - 1

@@ -567,7 +567,8 @@ enum { kEpiBF16 = 0, kEpiFp8Ring = 1, kEpiFp8Seed = 2, kEpiAmax = 3 };
 // and stored as 16-byte row pieces (the ragged end of a row byte by byte).
 // max |y| over the block's outputs inside M x N goes to the launch's
 // last-block election, which folds it into the output ring as a quantize
-// launch does; kEpiAmax computes and elects max |y| only, leaving it for
+// launch does (with g.odefer, to the block's election group only, for the
+// fold launch that follows the GEMM); kEpiAmax computes and elects max |y| only, leaving it for
 // the converting pass of a seeding call.  acc: the block's accumulators in
 // the pipelined kernels' fragment layout; s: the output scale (out_scale);
 // sbias: the BiasStage area; NT: threads per block.
@@ -596,6 +597,8 @@ FP8L_DEV void fp8_out_epilogue(const GemmArgs& g, const v16f (&acc)[FM][FN], flo
   const int tid = threadIdx.x, lane = tid & 63;
   const uint32_t bid = blockIdx.y * prob_nblk(g) + prob_block(g), total = prob_nblk(g) * gridDim.y;
   const int64_t rows_left = g.Mc - i0, cols_left = g.Nc - j0;
+  // a tile inside M x N needs no per-element mask on its max
+  const bool interior = rows_left >= BM && cols_left >= BN;
   uint32_t mx = 0;
 #pragma unroll
   for (int b = 0; b < FN; ++b) {
@@ -613,13 +616,17 @@ FP8L_DEV void fp8_out_epilogue(const GemmArgs& g, const v16f (&acc)[FM][FN], flo
         float v[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[t] = __builtin_fmaf(acc[a][b][4 * grp + t], dq, bias[t]);
-        if (il < rows_left) {
+        // max |v| bits of the four (above the infinity's bits: a NaN among them)
+        const uint32_t m4 = max(max(absbits(v[0]), absbits(v[1])), max(absbits(v[2]), absbits(v[3])));
+        if (interior) {
+          mx = max(mx, m4);
+        } else if (il < rows_left) {
 #pragma unroll
           for (int t = 0; t < 4; ++t)
             if (jl + t < cols_left) mx = max(mx, absbits(v[t]));
         }
         if constexpr (EPI != kEpiAmax)
-          *reinterpret_cast<uint32_t*>(smem + il * RSB + jl) = quant4<OF>(v, s);
+          *reinterpret_cast<uint32_t*>(smem + il * RSB + jl) = quant4_m<OF>(v, s, m4);
       }
     }
   }
@@ -648,7 +655,10 @@ FP8L_DEV void fp8_out_epilogue(const GemmArgs& g, const v16f (&acc)[FM][FN], flo
     qa.hist_len = g.ohist_len;
     qa.scale_used = g.oscale_used;
     qa.amax_out = g.oamax;
-    finish_launch<OF, EPI == kEpiFp8Seed ? kScaleSeed : kScaleRing, NT>(qa, mx, s, bid, total);
+    if (EPI == kEpiFp8Ring && g.odefer)
+      finish_launch<OF, kScaleDefer, NT>(qa, mx, s, bid, total);
+    else
+      finish_launch<OF, EPI == kEpiFp8Seed ? kScaleSeed : kScaleRing, NT>(qa, mx, s, bid, total);
   }
 }
 

@@ -136,6 +136,14 @@ FP8L_DEV uint32_t quant4(const float v[4], float s) {
   return w;
 }
 
+// quant4 when m4, the max of the four |v| bits, is known: the NaN repair
+// runs only when one of them is a NaN.
+template <int FMT>
+FP8L_DEV uint32_t quant4_m(const float v[4], float s, uint32_t m4) {
+  if (m4 > 0x7f800000u) return quant4<FMT>(v, s);
+  return cvt4<FMT>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+}
+
 // Elements [e, e + cnt), cnt <= 8, one at a time (ragged or unaligned).
 // vals receives the values (0 past cnt).  Returns the max |x| bits.
 template <int IN, int FMT>

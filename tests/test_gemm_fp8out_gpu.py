@@ -82,6 +82,43 @@ def test_fp8out_exact_steps(fa, fb, M, K, N, fmt_out):
         assert_ring_matches(ring, oring)
 
 
+# A NaN code in a row of A makes that row of y NaN: its codes are 0x7F with
+# a sign (the sign of a NaN the GEMM makes is not fixed), every other code
+# is exact; amax is NaN, the window then holds a NaN and the scale stays
+# where it was.  (160, 384, 272): 128x128 blocks, ragged; (2000, 256, 4096):
+# 256x256 blocks, inside tiles and a ragged tile row.
+@pytest.mark.parametrize("M,K,N", [(160, 384, 272), (2000, 256, 4096)])
+@pytest.mark.parametrize("fmt_out", [O.E4M3, O.E5M2])
+def test_fp8out_nan_rows(M, K, N, fmt_out):
+    fa = fb = O.E4M3
+    rng = np.random.default_rng(29 + fmt_out + M)
+    b8 = _int_codes((N, K), fb, rng)
+    ring, oring = F.ScaleRing(4), O.ScaleRing(4)
+    for step in range(4):
+        a8 = _int_codes((M, K), fa, rng)
+        if step in (1, 2):
+            for r in (0, M // 2 + step, M - 1):
+                a8[r, 3 + step] = 0x7F  # an e4m3 NaN code
+        bias_t, bias_bits = _bf16(rng.integers(-8, 9, size=N) * 0.5)
+        q, su, am = _run(a8, fa, b8, fb, 2.0, 4.0, bias_t, fmt_out, ring)
+        oq, osu, oam, ref = O.gemm_fp8out(a8, fa, b8, fb, 2.0, 4.0,
+                                          O.bias_values(bias_bits, "bf16"), fmt_out, oring)
+        nan = np.isnan(ref.r)
+        assert nan.any() == (step in (1, 2))
+        assert np.all((q[nan] & 0x7F) == 0x7F), f"step {step}: NaN outputs not coded as NaN"
+        assert np.array_equal(q[~nan], oq[~nan]), f"step {step}: codes differ"
+        assert su == osu, (step, su, osu)
+        assert (np.isnan(am) and np.isnan(oam)) or am == oam, (step, am, oam)
+        st = ring_state(ring)
+        assert st["scale"].tobytes() == np.float32(oring.scale).tobytes(), (step, st["scale"])
+        assert st["idx"] == oring.idx
+        oh = oring.hist.astype(np.float32)
+        assert np.array_equal(np.isnan(st["hist"]), np.isnan(oh))
+        assert st["hist"][~np.isnan(oh)].tobytes() == oh[~np.isnan(oh)].tobytes()
+        assert st["top_amax"] == 0 and st["top_count"] == 0
+        assert not st["group_count"].any() and not st["group_amax"].any()
+
+
 # (200, 640, 528): 128x128 blocks (4 waves, two per CU), ragged rows;
 # (2048, 1536, 6912): the up projection's forward, 216 tiles of 256x256 (the
 # 8-wave kernel and its fp8 epilogue), every element compared
