@@ -1037,10 +1037,14 @@ int fp8_linear_bwd(int64_t M, int64_t N, int64_t K, fp8_operand_t g, int32_t fmt
   }
   if (stream_dw != stream && (st = fork_after(stream, stream_dw))) return st;
   // the dX GEMM snapshots a pre-quantized g's scale; the dW GEMM reads
-  // g's own scale, so the two streams touch no common output
+  // g's own scale, so the two streams touch no common output.  dX is
+  // enqueued first: a captured graph's replay dispatches ready nodes in
+  // capture order, and the dX GEMM, which the next layer's backward waits
+  // for, should take the CUs before the dW GEMM fills what it leaves (as
+  // the eager streams do by themselves)
+  enqueue_dx_gemm(M, N, K, g8, sg, fmt_g, w8, dx, pre, g.scale, sg_used, amax_g, stream, fold);
   enqueue_dw_gemm(M, N, K, g8, sg, fmt_g, x8, dw, db, db_ws, pre, false, g.scale, sg_used, amax_g,
                   stream_dw);
-  enqueue_dx_gemm(M, N, K, g8, sg, fmt_g, w8, dx, pre, g.scale, sg_used, amax_g, stream, fold);
   return hip_status();
 }
 
