@@ -420,10 +420,12 @@ int fp8_gemm(int64_t batch, int64_t M, int64_t N, int64_t K, fp8_operand_t a, in
  * (round to nearest even, saturating, NaN -> 0x7F | sign).  s_out comes from
  * the output's delayed-scaling ring exactly as fp8_quantize takes it: the
  * ring's current scale, or, on the ring's first use, S(max |y|) from an
- * extra amax pass over the same GEMM (two launches instead of one).  The
- * launch's last block then folds max |y| (over the M x N outputs) into
- * hist[idx], advances idx and publishes fmt_max / max(hist) as the next
- * scale, as a quantize launch does.
+ * extra amax pass over the same GEMM.  max |y| (over the M x N outputs) is
+ * then folded into hist[idx], idx advanced and fmt_max / max(hist)
+ * published as the next scale, as a quantize launch does: in the steady
+ * state of a window of at most 64 entries by a one-wave launch that follows
+ * the GEMM on the same stream (the GEMM's blocks only leave their maxima in
+ * the ring's election groups), otherwise by the GEMM's last block.
  *
  *   a, b       fp8 codes (E4M3 or E5M2) with device scales: A [M,K] and
  *              B [N,K], both k-contiguous (rows of K codes).
