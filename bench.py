@@ -1043,10 +1043,14 @@ def main():
     # the timed region.  (Where the dX GEMM dominates the isolated timings,
     # the same scheme brackets fp8_linear_bwd_dw + the dX GEMM against
     # fp8_linear_bwd_dw alone.)
+    # The odd steps carry the brackets: the timed region starts on an idle
+    # stream, and a bracket in its first step would time the GPU catching up
+    # with the host's first submissions as well as the kernels.
     dom = "fwd" if tot["fwd"] >= tot["dx"] else "dx"
-    brack = [si for si in range(args.steps) if si % 2 == 0]
+    brack = [si for si in range(args.steps) if si % 2 == 1]
     if len(brack) < 2 * len(layers):
-        brack = list(range(args.steps))
+        brack = (list(range(1, args.steps)) if args.steps > 2 * len(layers)
+                 else list(range(args.steps)))
     ev = {si: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for si in brack}
     ev_what = {}  # step -> (linear, with_gemm)
