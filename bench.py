@@ -377,24 +377,50 @@ def traffic_record(kind, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, w
                if kind == "quant" else {})}
 
 
+# MI355X: 8 XCDs x 4 shader engines, 256 CUs x 4 SIMDs
+MI355X_SHADER_ENGINES = 32
+MI355X_SIMDS = 1024
+
+
 def mfma_record(csv_path, workload):
-    """MFMA utilisation (MfmaUtil: MFMA-busy cycles over active cycles x
-    SIMDs, in percent) of each GEMM kind, averaged over its dispatches in a
-    rocprofv3 --pmc MfmaUtil run of '--only gemm'."""
-    by = {}
-    for name, v in _pmc_per_dispatch(csv_path, "MfmaUtil").values():
+    """MFMA utilisation of each GEMM kind, averaged over its dispatches in a
+    rocprofv3 --pmc run of '--only gemm' with MfmaUtil, SQ_VALU_MFMA_BUSY_CYCLES
+    and SQ_BUSY_CYCLES:
+
+      mfma_util_pct   rocprofv3's MfmaUtil: MFMA-busy cycles over
+                      GRBM_GUI_ACTIVE x SIMDs.  GRBM_GUI_ACTIVE spans more
+                      than the dispatch under counter collection (a 2.8 us
+                      copy reads ~287k cycles), so this under-reads.
+      mfma_busy_pct   MFMA-busy cycles (summed over the SIMDs) over the
+                      dispatch's own shader-engine busy cycles
+                      (SQ_BUSY_CYCLES summed over the engines, divided by
+                      their count) x SIMDs: the share of the dispatch's
+                      cycles the matrix pipes were busy, over all SIMDs."""
+    util = _pmc_per_dispatch(csv_path, "MfmaUtil")
+    mbusy = _pmc_per_dispatch(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES")
+    sbusy = _pmc_per_dispatch(csv_path, "SQ_BUSY_CYCLES")
+    by, busy = {}, {}
+    for d, (name, v) in util.items():
         kind = gemm_kind_of(name)
-        if kind:
-            by.setdefault(kind, []).append(v)
+        if not kind:
+            continue
+        by.setdefault(kind, []).append(v)
+        if d in mbusy and d in sbusy and sbusy[d][1] > 0:
+            cycles = sbusy[d][1] / MI355X_SHADER_ENGINES
+            busy.setdefault(kind, []).append(100.0 * mbusy[d][1] / (cycles * MI355X_SIMDS))
     if not by:
         raise SystemExit(f"{csv_path}: no GEMM dispatch with MfmaUtil")
+    counters = "MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES"
     cmds = ["cd /tmp && export TMPDIR=/tmp",
-            "rocprofv3 --pmc MfmaUtil --output-format csv -d $REPO/gpurun_out/traffic -o t_gemm_MfmaUtil "
-            "-- python3 $REPO/bench.py --only gemm --steps 3",
+            f"rocprofv3 --pmc {counters} --output-format csv -d $REPO/gpurun_out/traffic "
+            "-o t_gemm_MfmaUtil -- python3 $REPO/bench.py --only gemm --steps 3",
             "python3 bench.py --mfma-from gpurun_out/traffic/t_gemm_MfmaUtil_counter_collection.csv"]
-    return {"workload": workload, "kernel_source_hash": kernel_source_hash(), "commands": cmds,
-            "mfma_util_pct": {k: round(sum(v) / len(v), 2) for k, v in sorted(by.items())},
-            "dispatches": {k: len(v) for k, v in sorted(by.items())}}
+    rec = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "commands": cmds,
+           "mfma_util_pct": {k: round(sum(v) / len(v), 2) for k, v in sorted(by.items())},
+           "dispatches": {k: len(v) for k, v in sorted(by.items())}}
+    if busy:
+        rec["mfma_busy_pct"] = {k: round(sum(v) / len(v), 2) for k, v in sorted(busy.items())}
+    return rec
 
 
 def trace_record(trace_csv, workload):
@@ -449,8 +475,9 @@ def load_trace_record(kind, workload):
 
 
 def load_mfma(workload):
-    """Per-kind MFMA utilisation (percent) from the committed record, or None
-    if absent or taken on different kernel sources."""
+    """Per-kind MFMA utilisation (percent, as rocprofv3's MfmaUtil and as
+    busy cycles of the dispatch; see mfma_record) from the committed record,
+    or None if absent or taken on different kernel sources."""
     path = os.path.join(PROFILE_DIR, f"mfma_util_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -458,7 +485,7 @@ def load_mfma(workload):
         rec = json.load(f)
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("mfma_util_pct")
+    return {"mfma_util_pct": rec.get("mfma_util_pct"), "mfma_busy_pct": rec.get("mfma_busy_pct")}
 
 
 def load_quant_traffic(workload):
@@ -592,6 +619,38 @@ def ceilings(torch, stream):
             fn = F.bind_fp8_linear_fwd(a, b, None, F.FP8_E4M3, y, stream=stream)
             row[f"K{K}"] = batched_stats_us(torch, fn, stream, reps=100, warm=10)["median"]
         res["gemm_fixed_us"][f"{M}x{N}"] = row
+    # the 2048 x 6912 forward (the up projection's shape) on random finite
+    # e4m3 codes at K = 512 .. 2048: a least-squares line through the
+    # medians splits the launch into a fixed part and a cost per 64-byte K
+    # step, to set beside the MFMA-only time of one step (16 MFMAs of
+    # 32x32x64 per SIMD on 216 CUs at the random-data rate above)
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    M, N = 2048, 6912
+    y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    ks, us = [], []
+    for K in (512, 1024, 1536, 2048):
+        def rnd(r):
+            c = torch.randint(0, 254, (r, K), generator=gen, dtype=torch.int32)
+            return torch.where(c >= 0x7F, c + 1, c).to(torch.uint8).to("cuda")  # no NaN code
+        a = F.Quantized(rnd(M), F.FP8_E4M3, one)
+        b = F.Quantized(rnd(N), F.FP8_E4M3, one)
+        fn = F.bind_fp8_linear_fwd(a, b, None, F.FP8_E4M3, y, stream=stream)
+        ks.append(K)
+        us.append(batched_stats_us(torch, fn, stream, reps=100, warm=10)["median"])
+    n = len(ks)
+    steps = [k / 64 for k in ks]
+    mx, my = sum(steps) / n, sum(us) / n
+    slope = (sum((x - mx) * (v - my) for x, v in zip(steps, us)) /
+             sum((x - mx) ** 2 for x in steps))
+    mfma_step_us = None
+    r216 = res["mfma_TFLOPs"].get("random_216cu")
+    if r216:
+        mfma_step_us = 216 * 4 * 16 * 2 * 32 * 32 * 64 / (r216 * 1e12) * 1e6
+    res["gemm_kslope_2048x6912"] = {
+        "us_by_K": {f"K{k}": round(v, 3) for k, v in zip(ks, us)},
+        "us_per_64B_step": round(slope, 4), "fixed_us": round(my - slope * mx, 3),
+        "mfma_only_us_per_step": None if mfma_step_us is None else round(mfma_step_us, 4),
+        "loop_efficiency": None if mfma_step_us is None else round(mfma_step_us / slope, 3)}
     # fixed cost of a quantize launch: the standalone quantize (seeded ring,
     # last-block election) of bf16 tensors from one block's worth of
     # elements to the layer's largest, and a launch of the stream probe over

@@ -181,3 +181,31 @@ def test_trace_record_per_kind_averages(tmp_path):
     from scaled_quantize_fp8_amd import workloads as WL
     wl = WL.WORKLOADS["dim1536_m2048"]
     assert rec["flops_per_launch_avg"] == sum(2.0 * wl.M * L.N * L.K for L in wl.linears) / 5
+
+
+def test_mfma_record_busy_over_dispatch_cycles(tmp_path):
+    """mfma_busy_pct divides the MFMA-busy cycles (summed over the SIMDs) by
+    the dispatch's engine-busy cycles (summed over the engines, so divided
+    by their count) times the SIMDs; MfmaUtil is kept as measured."""
+    fwd = GEMM4.format("0, 0, 0, 0")
+    dx = GEMM5.format("0, 1, 1, 0")
+    path = tmp_path / "m.csv"
+    se, simds = bench.MI355X_SHADER_ENGINES, bench.MI355X_SIMDS
+    rows = [  # dispatch, kernel, counter, value
+        (1, fwd, "MfmaUtil", 20.0), (1, fwd, "SQ_VALU_MFMA_BUSY_CYCLES", 0.4 * 1000 * simds),
+        (1, fwd, "SQ_BUSY_CYCLES", 1000.0 * se),
+        (2, fwd, "MfmaUtil", 22.0), (2, fwd, "SQ_VALU_MFMA_BUSY_CYCLES", 0.2 * 500 * simds),
+        (2, fwd, "SQ_BUSY_CYCLES", 500.0 * se),
+        (3, dx, "MfmaUtil", 30.0),  # no busy counters: only MfmaUtil for this kind
+    ]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=_FIELDS)
+        w.writeheader()
+        for d, name, c, v in rows:
+            w.writerow({"Correlation_Id": d, "Dispatch_Id": d, "Agent_Id": "Agent 1",
+                        "Kernel_Name": name, "Counter_Name": c, "Counter_Value": v})
+    rec = bench.mfma_record(str(path), "dim1536_m2048")
+    assert rec["mfma_util_pct"] == {"dx": 30.0, "fwd": 21.0}
+    assert rec["mfma_busy_pct"] == {"fwd": pytest.approx(30.0)}
+    assert rec["dispatches"] == {"dx": 1, "fwd": 2}
+    assert "SQ_BUSY_CYCLES" in rec["commands"][1]
