@@ -360,15 +360,15 @@ def traffic_record(kind, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, w
     w_scale = COPY_BYTES / (copy_kib(copy_write_csv, "WRITE_SIZE") * 1024)
     rd = fetch_kib * 1024 * f_scale
     wr = write_kib * 1024 * w_scale
-    runs = [f"rocprofv3 --pmc {c} --output-format csv -d $REPO/gpurun_out/traffic -o t_{w}_{c} -- "
+    runs = [f"rocprofv3 --pmc {c} --output-format csv -d $OUT/traffic -o t_{w}_{c} -- "
             f"python3 $REPO/bench.py --only {w} --steps 3"
             for w in (kind, "copy") for c in ("FETCH_SIZE", "WRITE_SIZE")]
     cmds = ["cd /tmp && export TMPDIR=/tmp"] + runs + [
         f"python3 bench.py --traffic-from {kind} " + " ".join(
-            f"gpurun_out/traffic/t_{w}_{c}_counter_collection.csv"
+            f"$OUT/traffic/t_{w}_{c}_counter_collection.csv"
             for w in (kind, "copy") for c in ("FETCH_SIZE", "WRITE_SIZE"))]
     return {"kernel_kind": kind, "workload": workload, "kernel_source_hash": kernel_source_hash(),
-            "commands": cmds,
+            "commands": cmds, "paths": CMD_PATHS,
             "dispatches": [n_f, n_w], "fetch_kib_raw": fetch_kib, "write_kib_raw": write_kib,
             "fetch_scale": f_scale, "write_scale": w_scale,
             "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
@@ -380,6 +380,10 @@ def traffic_record(kind, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, w
 # MI355X: 8 XCDs x 4 shader engines, 256 CUs x 4 SIMDs
 MI355X_SHADER_ENGINES = 32
 MI355X_SIMDS = 1024
+
+# placeholders in the commands a profile record carries
+CMD_PATHS = {"$REPO": "the repository root",
+             "$OUT": "the directory rocprofv3 wrote its output to (outside the sources)"}
 
 
 def mfma_record(csv_path, workload):
@@ -399,7 +403,8 @@ def mfma_record(csv_path, workload):
     util = _pmc_per_dispatch(csv_path, "MfmaUtil")
     mbusy = _pmc_per_dispatch(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES")
     sbusy = _pmc_per_dispatch(csv_path, "SQ_BUSY_CYCLES")
-    by, busy = {}, {}
+    mops = _pmc_per_dispatch(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_F8")
+    by, busy, flops = {}, {}, {}
     for d, (name, v) in util.items():
         kind = gemm_kind_of(name)
         if not kind:
@@ -408,18 +413,29 @@ def mfma_record(csv_path, workload):
         if d in mbusy and d in sbusy and sbusy[d][1] > 0:
             cycles = sbusy[d][1] / MI355X_SHADER_ENGINES
             busy.setdefault(kind, []).append(100.0 * mbusy[d][1] / (cycles * MI355X_SIMDS))
+        if d in mops:  # the counter books fp8 multiply-adds / 512
+            flops.setdefault(kind, []).append(512.0 * mops[d][1])
     if not by:
         raise SystemExit(f"{csv_path}: no GEMM dispatch with MfmaUtil")
-    counters = "MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES"
+    counters = "MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F8"
     cmds = ["cd /tmp && export TMPDIR=/tmp",
-            f"rocprofv3 --pmc {counters} --output-format csv -d $REPO/gpurun_out/traffic "
+            f"rocprofv3 --pmc {counters} --output-format csv -d $OUT/traffic "
             "-o t_gemm_MfmaUtil -- python3 $REPO/bench.py --only gemm --steps 3",
-            "python3 bench.py --mfma-from gpurun_out/traffic/t_gemm_MfmaUtil_counter_collection.csv"]
+            "python3 bench.py --mfma-from $OUT/traffic/t_gemm_MfmaUtil_counter_collection.csv"]
     rec = {"workload": workload, "kernel_source_hash": kernel_source_hash(), "commands": cmds,
            "mfma_util_pct": {k: round(sum(v) / len(v), 2) for k, v in sorted(by.items())},
            "dispatches": {k: len(v) for k, v in sorted(by.items())}}
     if busy:
         rec["mfma_busy_pct"] = {k: round(sum(v) / len(v), 2) for k, v in sorted(busy.items())}
+    if flops:
+        # every linear's GEMM of a kind is launched equally often, so the
+        # algorithmic average is the layer's mean 2MNK
+        from scaled_quantize_fp8_amd import workloads as WL
+        wl = WL.WORKLOADS[workload]
+        alg = sum(2.0 * wl.M * L.N * L.K for L in wl.linears) / len(wl.linears)
+        rec["f8_mfma_flops_per_dispatch"] = {k: sum(v) / len(v) for k, v in sorted(flops.items())}
+        rec["algorithmic_flops_per_dispatch"] = alg
+    rec["paths"] = CMD_PATHS
     return rec
 
 
@@ -448,13 +464,13 @@ def trace_record(trace_csv, workload):
         kinds[k] = {"launches": len(v), "avg_us": round(avg_us, 3),
                     "frac": round(flops / (avg_us * 1e-6) / 1e12 / MI355X_FP8_DENSE_TFLOPS, 4)}
     cmds = ["cd /tmp && export TMPDIR=/tmp",
-            "rocprofv3 --kernel-trace --stats --output-format csv -d $REPO/gpurun_out/prof_step "
+            "rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/prof_step "
             "-o step -- python3 $REPO/bench.py --steps 20 --warmup 5 --no-widened "
             "--no-other-configs --no-cpu-baseline --no-ceilings",
             f"python3 bench.py --workload {workload} --trace-from "
-            "gpurun_out/prof_step/step_kernel_trace.csv"]
+            "$OUT/prof_step/step_kernel_trace.csv"]
     return {"workload": workload, "kernel_source_hash": kernel_source_hash(), "commands": cmds,
-            "flops_per_launch_avg": flops, "kinds": kinds}
+            "paths": CMD_PATHS, "flops_per_launch_avg": flops, "kinds": kinds}
 
 
 def trace_record_path(workload):

@@ -9,6 +9,7 @@ import csv
 import pytest
 
 import bench
+from scaled_quantize_fp8_amd import workloads as WL
 
 GEMM3 = "void fp8l::gemm3_kernel<128, 128, 2, 2, {}>(fp8l::GemmArgs)"
 GEMM4 = "void fp8l::gemm4_kernel<{}, 0, 0>(fp8l::GemmArgs)"
@@ -196,6 +197,7 @@ def test_mfma_record_busy_over_dispatch_cycles(tmp_path):
         (1, fwd, "SQ_BUSY_CYCLES", 1000.0 * se),
         (2, fwd, "MfmaUtil", 22.0), (2, fwd, "SQ_VALU_MFMA_BUSY_CYCLES", 0.2 * 500 * simds),
         (2, fwd, "SQ_BUSY_CYCLES", 500.0 * se),
+        (1, fwd, "SQ_INSTS_VALU_MFMA_MOPS_F8", 1000.0), (2, fwd, "SQ_INSTS_VALU_MFMA_MOPS_F8", 3000.0),
         (3, dx, "MfmaUtil", 30.0),  # no busy counters: only MfmaUtil for this kind
     ]
     with open(path, "w", newline="") as f:
@@ -209,3 +211,9 @@ def test_mfma_record_busy_over_dispatch_cycles(tmp_path):
     assert rec["mfma_busy_pct"] == {"fwd": pytest.approx(30.0)}
     assert rec["dispatches"] == {"dx": 1, "fwd": 2}
     assert "SQ_BUSY_CYCLES" in rec["commands"][1]
+    # the MOPs counter books multiply-adds / 512
+    assert rec["f8_mfma_flops_per_dispatch"] == {"fwd": pytest.approx(512.0 * 2000.0)}
+    wl = WL.WORKLOADS["dim1536_m2048"]
+    assert rec["algorithmic_flops_per_dispatch"] == pytest.approx(
+        sum(2.0 * wl.M * L.N * L.K for L in wl.linears) / len(wl.linears))
+    assert set(rec["paths"]) == {"$REPO", "$OUT"}
