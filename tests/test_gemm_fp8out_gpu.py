@@ -61,16 +61,19 @@ def _run(a8, fa, b8, fb, sa, sb, bias_t, fmt_out, ring):
 # (160, 384, 272): a ragged block row (160 = 128 + 32), three block columns;
 # (1024, 256, 1536): 96 blocks, more than the 64 election groups;
 # (2000, 256, 4096): 128 tiles of 256x256 (the 8-wave kernel), a ragged last
-# tile row (2000 = 7 x 256 + 208)
+# tile row (2000 = 7 x 256 + 208).  H: a window of 4 (the steady state folds
+# in a one-wave launch after the GEMM) and of 100 (longer than a wave: the
+# GEMM's last block folds).
 @pytest.mark.parametrize("fa,fb,M,K,N", [(O.E4M3, O.E4M3, 160, 384, 272),
                                          (O.E5M2, O.E4M3, 160, 384, 272),
                                          (O.E4M3, O.E4M3, 1024, 256, 1536),
                                          (O.E4M3, O.E5M2, 2000, 256, 4096)])
 @pytest.mark.parametrize("fmt_out", [O.E4M3, O.E5M2])
-def test_fp8out_exact_steps(fa, fb, M, K, N, fmt_out):
+@pytest.mark.parametrize("H", [4, 100])
+def test_fp8out_exact_steps(fa, fb, M, K, N, fmt_out, H):
     rng = np.random.default_rng(7 + 3 * fa + fmt_out + M)
     b8 = _int_codes((N, K), fb, rng)
-    ring, oring = F.ScaleRing(4), O.ScaleRing(4)
+    ring, oring = F.ScaleRing(H), O.ScaleRing(H)
     for step in range(4):
         a8 = _int_codes((M, K), fa, rng)
         bias_t, bias_bits = _bf16(rng.integers(-8, 9, size=N) * 0.5)

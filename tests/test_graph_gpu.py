@@ -148,3 +148,57 @@ def test_unseeded_ring_refused_under_capture():
     F.fp8_quantize(x, FX, q, ring, su, stream=stream)  # eager: seeds
     stream.synchronize()
     assert ring.seeded and ring_state(ring)["idx"] == 1
+
+
+def test_graph_fp8out_replays_match_eager():
+    """The FP8-output GEMM in a graph: its steady state is the GEMM launch
+    and the one-wave launch that folds the output ring.  Two copies of the
+    call on the same codes, seeded eagerly; one captured and replayed while
+    the other runs eagerly, with the operand scale changed between replays
+    (so max |y| and the ring move); every replay must give the eager call's
+    codes, scale, amax and ring state exactly."""
+    M, K, N = 2048, 256, 4096  # the 256x256 8-wave kernel
+    rng = np.random.default_rng(41)
+    tab_ok = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    a8 = torch.from_numpy(rng.choice(tab_ok, size=(M, K)).astype(np.uint8)).to(DEV)
+    b8 = torch.from_numpy(rng.choice(tab_ok, size=(N, K)).astype(np.uint8)).to(DEV)
+    stream = torch.cuda.Stream()
+
+    class Call:
+        def __init__(self):
+            self.sa = torch.full((1,), 3.0, dtype=torch.float32, device=DEV)
+            self.sb = torch.full((1,), 5.0, dtype=torch.float32, device=DEV)
+            self.c8 = torch.empty(M, N, dtype=torch.uint8, device=DEV)
+            self.su = torch.zeros(1, dtype=torch.float32, device=DEV)
+            self.am = torch.zeros(1, dtype=torch.float32, device=DEV)
+            self.ring = F.ScaleRing(4, stream=stream)
+            self.fn = F.bind_fp8_gemm_fp8out(F.Quantized(a8, FX, self.sa), F.Quantized(b8, FX, self.sb),
+                                             self.c8, FX, self.ring, self.su, self.am, stream=stream)
+
+        def snapshot(self):
+            out = {k: getattr(self, k).cpu().view(torch.uint8).numpy().copy()
+                   for k in ("c8", "su", "am")}
+            for k, v in ring_state(self.ring).items():
+                out[f"ring.{k}"] = np.asarray(v).copy()
+            return out
+
+    eager, graphed = Call(), Call()
+    with torch.cuda.stream(stream):
+        eager.fn()  # seeding call: the amax pass and the converting pass
+        graphed.fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        graphed.fn()
+    torch.cuda.synchronize()
+    for i, sa in enumerate((3.0, 0.5, 12.0, 3.0)):
+        with torch.cuda.stream(stream):
+            eager.sa.fill_(sa)
+            graphed.sa.fill_(sa)
+            eager.fn()
+            g.replay()
+        torch.cuda.synchronize()
+        a, r = eager.snapshot(), graphed.snapshot()
+        for k in a:
+            assert np.array_equal(a[k], r[k]), f"replay {i}: {k} differs from the eager call"
+
