@@ -245,9 +245,14 @@ RingFold fold_of(const fp8_ring_t* r, int32_t fmt, float* amax_out) {
 }
 
 // The fold of a ring whose groups a deferring launch filled, as a launch of
-// its own (one wave): the FP8-output GEMM's codes have no consuming GEMM
-// here to hand the fold to.
+// its own (one wave): for codes that no GEMM of the same call consumes (a
+// standalone quantize, the FP8-output GEMM's output), so that no block of
+// the converting launch waits on an election.
 __global__ __launch_bounds__(64) void ring_fold_kernel(RingFold f) { ring_fold_wave(f); }
+__global__ __launch_bounds__(64) void ring_fold2_kernel(RingFold f0, RingFold f1) {
+  ring_fold_wave(f0);
+  ring_fold_wave(f1);
+}
 
 // One quantize.  may_defer: the caller launches a GEMM on the codes next,
 // on the same stream, which folds the ring when this returns true.
@@ -255,12 +260,17 @@ bool enqueue_quant(const void* x, int32_t in_dtype, int64_t n, int32_t fmt, uint
                    fp8_ring_t* ring, float* scale_used, float* amax_out, const ColsumSpec* cs,
                    hipStream_t st, bool may_defer = false) {
   const bool defer = may_defer && can_defer(ring);
+  // no consuming GEMM to hand the fold to: a one-wave launch folds it
+  const bool fold_after = !may_defer && can_defer(ring);
+  const bool groups_only = defer || fold_after;
   if (in_dtype == FP8_DT_F32)
-    enqueue_quant_in<kInF32>(x, n, fmt, q, ring, scale_used, amax_out, cs, st, defer);
+    enqueue_quant_in<kInF32>(x, n, fmt, q, ring, scale_used, amax_out, cs, st, groups_only);
   else if (in_dtype == FP8_DT_F16)
-    enqueue_quant_in<kInF16>(x, n, fmt, q, ring, scale_used, amax_out, cs, st, defer);
+    enqueue_quant_in<kInF16>(x, n, fmt, q, ring, scale_used, amax_out, cs, st, groups_only);
   else
-    enqueue_quant_in<kInBF16>(x, n, fmt, q, ring, scale_used, amax_out, cs, st, defer);
+    enqueue_quant_in<kInBF16>(x, n, fmt, q, ring, scale_used, amax_out, cs, st, groups_only);
+  if (fold_after)
+    hipLaunchKernelGGL(ring_fold_kernel, dim3(1), dim3(64), 0, st, fold_of(ring, fmt, amax_out));
   return defer;
 }
 
@@ -278,13 +288,22 @@ void enqueue_quant_pair(const void* x0, int32_t dt0, int64_t n0, uint8_t* q0, fp
     f0 = enqueue_quant(x0, dt0, n0, fmt, q0, r0, su0, am0, nullptr, st, may_defer);
     f1 = enqueue_quant(x1, dt1, n1, fmt, q1, r1, su1, am1, nullptr, st, may_defer);
   } else {
-    f0 = f1 = may_defer && can_defer(r0) && can_defer(r1);
+    const bool both = can_defer(r0) && can_defer(r1);
+    f0 = f1 = may_defer && both;
+    const bool fold_after = !may_defer && both;  // as in enqueue_quant
+    const bool groups_only = f0 || fold_after;
     if (dt0 == FP8_DT_F32)
-      enqueue_quant2_in<kInF32>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st, f0);
+      enqueue_quant2_in<kInF32>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st,
+                                groups_only);
     else if (dt0 == FP8_DT_F16)
-      enqueue_quant2_in<kInF16>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st, f0);
+      enqueue_quant2_in<kInF16>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st,
+                                groups_only);
     else
-      enqueue_quant2_in<kInBF16>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st, f0);
+      enqueue_quant2_in<kInBF16>(fmt, x0, n0, q0, r0, su0, am0, x1, n1, q1, r1, su1, am1, st,
+                                 groups_only);
+    if (fold_after)
+      hipLaunchKernelGGL(ring_fold2_kernel, dim3(1), dim3(64), 0, st, fold_of(r0, fmt, am0),
+                         fold_of(r1, fmt, am1));
   }
   if (d0) *d0 = f0;
   if (d1) *d1 = f1;
