@@ -108,8 +108,8 @@ typedef struct {
  *             aligned: a 128-byte header {float scale; u32 top_count;
  *             u32 top_amax; u32 idx; u32 hist_len; u32 seeded; ...}, 64
  *             election groups of 128 bytes {u32 count; ...; u32 amax; ...}
- *             used by the last-block election of each launch (all zero
- *             between launches), then float hist[hist_len].
+ *             that collect a launch's block maxima for the fold (all zero
+ *             between calls), then float hist[hist_len].
  *   hist_len  H, 1..1024.
  *   seeded    host mirror, 0 until the first quantize through the ring has
  *             been enqueued.  That first quantize seeds the scale from its
@@ -164,9 +164,14 @@ int fp8_ring_init(fp8_ring_t* ring, void* dev, int32_t hist_len, hipStream_t str
  *   ring       NULL: dynamic scaling, s_used = fmt_max / amax(x) (two
  *              passes).  Otherwise delayed scaling: s_used = the ring's
  *              current scale (seeded from amax(x) on the ring's first use);
- *              the launch's last block folds amax(x) into hist[idx],
- *              advances idx and publishes fmt_max / max(hist) as the next
- *              scale (kept unchanged if that max is 0 or not finite).
+ *              then amax(x) is folded into hist[idx], idx advanced and
+ *              fmt_max / max(hist) published as the next scale (kept
+ *              unchanged if that max is 0 or not finite).  The fold runs in
+ *              a one-wave launch after the converting launch when the ring
+ *              is seeded and H <= 64 (the converting blocks only leave their
+ *              maxima in the election groups), otherwise in the converting
+ *              launch's last block, elected by atomic tickets; the results
+ *              are the same bits either way.
  *   scale_used device float out, required: the s the bytes were made with.
  *   amax_out   device float out: max |x_i| over the input values.
  *              Required when ring is NULL (it is also the accumulator),
