@@ -43,9 +43,10 @@ constexpr int kTileBytes = 128 * 128;
 enum { kKContig = 0, kCross = 1 };
 enum { kBiasNone = 0, kBiasBF16 = 1, kBiasE4M3 = 2, kBiasE5M2 = 3 };
 
-// The ring fold of a quantize launch that ran in kScaleDefer mode (its
-// blocks left their maxima in the ring's election groups), done by the GEMM
-// that consumes the codes.  ring null: nothing to fold.
+// The ring fold of a launch that ran in kScaleDefer mode (its blocks left
+// their maxima in the ring's election groups), done by one wave of a later
+// launch on the same stream: the GEMM that consumes the codes, or a one-wave
+// fold launch.  ring null: nothing to fold.
 struct RingFold {
   RingHdr* ring;
   float* hist;

@@ -1,8 +1,11 @@
 // Per-tensor FP8 quantize for gfx950: amax over the input values, a
-// saturating RNE conversion, and the delayed-scaling ring finalize in the
-// launch's last block ([P1] entry on finalizing scale rings inside the
-// quantize kernels; [P4] entry on the atomic ticket; [P3] entries on the
-// quantize templated on bf16/fp16/fp32 input and on fp32-domain amax).
+// saturating RNE conversion, and the delayed-scaling ring finalize ([P1]
+// entry on finalizing scale rings inside the quantize kernels; [P4] entry on
+// the atomic ticket; [P3] entries on the quantize templated on bf16/fp16/fp32
+// input and on fp32-domain amax).  The finalize runs in the launch's last
+// block (Ring, Seed below), or one wave of a later launch folds the maxima
+// the blocks left in the ring's election groups (Defer: the GEMM that
+// consumes the codes, or a one-wave launch after a standalone quantize).
 //
 // Memory access: a wave converts 1024 consecutive elements per step; each of
 // its load instructions covers 1 KB of contiguous input (16 bytes per lane)
@@ -34,8 +37,8 @@ namespace fp8l {
 // Scale modes of a converting launch: the ring's scale with the ring fold
 // in the last block (Ring); the seed from the amax pass, then the fold
 // (Seed); dynamic, from the amax pass (Dyn); the ring's scale with the fold
-// left to the launch that consumes the codes (Defer: each block only folds
-// its max into its election group; see finish_launch and RingFold).
+// left to a later launch on the stream (Defer: each block only folds its max
+// into its election group; see finish_launch and RingFold).
 enum { kScaleRing = 0, kScaleSeed = 1, kScaleDyn = 2, kScaleDefer = 3 };
 
 constexpr int kQThreads = 256;
