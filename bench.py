@@ -1330,7 +1330,16 @@ def main():
         "roofline": roofline,
     }
     if not args.no_ceilings:
-        out["ceilings"] = ceilings(torch, stream)
+        out["ceilings"] = c = ceilings(torch, stream)
+        # the same figures against this chip's own ceilings, measured in this
+        # run: the MFMA-only rate on random e4m3 codes with every CU busy,
+        # and a plain HBM copy
+        mfma = c["mfma_TFLOPs"].get(f"random_{c['cus']}cu")
+        if mfma:
+            roofline["frac_of_measured_mfma_ceiling"] = round(achieved / mfma, 4)
+        if c["hbm_GBps"].get("copy"):
+            out["quantize_pct_measured_copy"] = round(
+                100 * qsweep["cold"]["GBps"] / c["hbm_GBps"]["copy"], 2)
     if not args.no_widened:
         out["widened"] = widened_rows(torch, F, WL, wl, layers, stream, args.kernel_reps)
     if not args.no_other_configs:
