@@ -13,6 +13,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "../../include/fp8linear.h"
@@ -25,17 +26,31 @@
 namespace fp8l {
 namespace {
 
+// Per-device host caches are atomics: library calls may come from several
+// host threads, and two first calls on one device may both fill an entry
+// (with the same value).
 int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
+}
+
+// Raise a kernel's dynamic LDS limit to lds bytes, once per device (the
+// flag is published after the attribute is set, so a thread that sees it
+// launches after the setting).
+void set_lds_limit(const void* kernel, int lds, std::atomic<bool> (&done)[64]) {
+  int dev = 0;
+  const bool known = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64;
+  if (known && done[dev].load(std::memory_order_acquire)) return;
+  (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (known) done[dev].store(true, std::memory_order_release);
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -320,14 +335,9 @@ template <int BM, int BN, int WGM, int WGN, int LA, int LB, int FA, int FB, int 
           int OF = kE4M3>
 void launch_gemm3_t(GemmArgs& g, hipStream_t st) {
   constexpr int lds = gemm3_lds_bytes<BM, BN, WGM, WGN>();
-  static bool attr_set[64] = {false};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    (void)hipFuncSetAttribute((const void*)gemm3_kernel<BM, BN, WGM, WGN, LA, LB, FA, FB, EPI, OF>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    attr_set[dev] = true;
-  }
+  static std::atomic<bool> lds_set[64];
+  set_lds_limit((const void*)gemm3_kernel<BM, BN, WGM, WGN, LA, LB, FA, FB, EPI, OF>, lds,
+                lds_set);
   g.tiles_m = (int32_t)((g.Mc + BM - 1) / BM);
   g.tiles_n = (int32_t)((g.Nc + BN - 1) / BN);
   if (g.tiles_m < 1) g.tiles_m = 1;
@@ -394,14 +404,8 @@ void launch_gemm3_f(GemmArgs& g, int fa, int fb, hipStream_t st) {
 template <int LA, int LB, int FA, int FB, int EPI = kEpiBF16, int OF = kE4M3>
 void launch_gemm4_t(GemmArgs& g, hipStream_t st) {
   constexpr int lds = gemm4_lds_bytes();
-  static bool attr_set[64] = {false};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    (void)hipFuncSetAttribute((const void*)gemm4_kernel<LA, LB, FA, FB, EPI, OF>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    attr_set[dev] = true;
-  }
+  static std::atomic<bool> lds_set[64];
+  set_lds_limit((const void*)gemm4_kernel<LA, LB, FA, FB, EPI, OF>, lds, lds_set);
   g.tiles_m = (int32_t)((g.Mc + 255) / 256);
   g.tiles_n = (int32_t)((g.Nc + 255) / 256);
   if (g.tiles_m < 1) g.tiles_m = 1;
@@ -442,14 +446,8 @@ void launch_fp8out(GemmArgs& g, int fa, int fb, hipStream_t st) {
 template <int LA, int LB, int FA, int FB>
 void launch_gemm5_t(GemmArgs& g, hipStream_t st) {
   constexpr int lds = gemm5_lds_bytes();
-  static bool attr_set[64] = {false};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    (void)hipFuncSetAttribute((const void*)gemm5_kernel<LA, LB, FA, FB>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    attr_set[dev] = true;
-  }
+  static std::atomic<bool> lds_set[64];
+  set_lds_limit((const void*)gemm5_kernel<LA, LB, FA, FB>, lds, lds_set);
   g.tiles_m = (int32_t)((g.Mc + 127) / 128);
   g.tiles_n = (int32_t)((g.Nc + 127) / 128);
   if (g.tiles_m < 1) g.tiles_m = 1;
@@ -511,14 +509,8 @@ void launch_gemm_l(GemmArgs& g, int fa, int fb, hipStream_t st) {
 template <class BX, class BW>
 void launch_pair_t(GemmArgs& dx, GemmArgs& dw, hipStream_t st) {
   constexpr int lds = pair_lds_bytes<BX, BW>();
-  static bool attr_set[64] = {false};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    (void)hipFuncSetAttribute((const void*)gemm_pair_kernel<BX, BW>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    attr_set[dev] = true;
-  }
+  static std::atomic<bool> lds_set[64];
+  set_lds_limit((const void*)gemm_pair_kernel<BX, BW>, lds, lds_set);
   auto tiles = [](GemmArgs& g, int bm, int bn) {
     g.tiles_m = (int32_t)((g.Mc + bm - 1) / bm);
     g.tiles_n = (int32_t)((g.Nc + bn - 1) / bn);

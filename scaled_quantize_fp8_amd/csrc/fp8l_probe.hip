@@ -1,5 +1,7 @@
 // Measurement kernels (libfp8probe.so): the MFMA-only ceiling and a plain
 // HBM stream.  See include/fp8probe.h.  Not part of the FP8 linear path.
+#include <atomic>
+
 #include "../../include/fp8probe.h"
 #include "fp8l_gemm3.hpp"
 
@@ -80,11 +82,14 @@ int fp8probe_mfma(int32_t blocks, int32_t iters, const uint32_t* codes, float* o
   // 96 KB of dynamic LDS: two blocks do not fit one CU, so each block has
   // a CU of its own while blocks <= the CU count
   constexpr int kLds = 96 * 1024;
-  static bool attr = false;
-  if (!attr) {
+  // once per device; the flag is published after the attribute is set
+  static std::atomic<bool> attr[64];
+  int dev = 0;
+  const bool known = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64;
+  if (!known || !attr[dev].load(std::memory_order_acquire)) {
     (void)hipFuncSetAttribute((const void*)mfma_peak_kernel,
                               hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    attr = true;
+    if (known) attr[dev].store(true, std::memory_order_release);
   }
   hipLaunchKernelGGL(mfma_peak_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), kLds, stream,
                      codes, iters, out);
