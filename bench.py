@@ -1118,14 +1118,15 @@ def main():
     # the timed region.  (Where the dX GEMM dominates the isolated timings,
     # the same scheme brackets fp8_linear_bwd_dw + the dX GEMM against
     # fp8_linear_bwd_dw alone.)
-    # The odd steps carry the brackets: the timed region starts on an idle
-    # stream, and a bracket in its first step would time the GPU catching up
-    # with the host's first submissions as well as the kernels.
+    # Every step from the second carries a bracket: the timed region starts
+    # on an idle stream, and a bracket in its first step would time the GPU
+    # catching up with the host's first submissions as well as the kernels.
+    # (Measured, a bracket in every step against one in every other step
+    # moves the step time by less than its run-to-run spread.)
     dom = "fwd" if tot["fwd"] >= tot["dx"] else "dx"
-    brack = [si for si in range(args.steps) if si % 2 == 1]
+    brack = list(range(1, args.steps))
     if len(brack) < 2 * len(layers):
-        brack = (list(range(1, args.steps)) if args.steps > 2 * len(layers)
-                 else list(range(args.steps)))
+        brack = list(range(args.steps))
     ev = {si: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for si in brack}
     ev_what = {}  # step -> (linear, with_gemm)
@@ -1292,9 +1293,9 @@ def main():
         "config": {"workload": workload_label(wl), "global_batch": wl.M,
                    "gemms_per_step": 3 * len(layers)},
         "step_schedule": "every forward in order as fp8_linear_fwd(X, W) (quantize without "
-                         "election; the GEMM folds the rings), in every other step one of them "
-                         "split into fp8_quantize_pair + fp8_linear_fwd(X8, W8) inside an event "
-                         "pair; then every backward in reverse order as fp8_linear_bwd (dX on "
+                         "election; the GEMM folds the rings), in every step after the first one of "
+                         "them split into fp8_quantize_pair + fp8_linear_fwd(X8, W8) inside an "
+                         "event pair; then every backward in reverse order as fp8_linear_bwd (dX on "
                          "the main stream, dW and db on a second stream after the G quantize); "
                          "one join of the two streams per step",
         "pct_fp8_peak": round(100 * tflops / MI355X_FP8_DENSE_TFLOPS, 2),
