@@ -249,16 +249,19 @@ def test_full_size_layer_tensors(wl_name):
 
 
 @pytest.mark.parametrize("dtypes", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.bfloat16)])
-def test_quantize_pair_matches_two_rings(dtypes):
+@pytest.mark.parametrize("hist", [(16, 16), (16, 100)])
+def test_quantize_pair_matches_two_rings(dtypes, hist):
     """fp8_quantize_pair over several delayed steps: step 0 seeds both rings
     (two launches); later steps with matching input types run as one launch.
     Every step matches the oracle for both tensors: bytes, scale_used, amax
-    and ring state."""
+    and ring state.  hist: the two windows; two of 16 fold in a one-wave
+    launch after the paired launch, a 100-entry one makes both rings fold in
+    the paired launch's last-block elections."""
     shapes = ((2048, 1536), (6912, 1536)) if dtypes[0] == dtypes[1] else ((333, 77), (4097, 3))
     x0 = WL.normal_bf16(shapes[0], 1.0, 21).float()
     x1 = WL.normal_bf16(shapes[1], 0.02, 22).float()
-    rings = [F.ScaleRing(16), F.ScaleRing(16)]
-    orings = [O.ScaleRing(16), O.ScaleRing(16)]
+    rings = [F.ScaleRing(hist[0]), F.ScaleRing(hist[1])]
+    orings = [O.ScaleRing(hist[0]), O.ScaleRing(hist[1])]
     for t, (c0, c1) in enumerate(((1.0, 1.0), (4.0, 0.5), (0.25, 2.0), (1.0, 1.0))):
         xs = [(x0 * c0).to(dtypes[0]), (x1 * c1).to(dtypes[1])]
         q = [torch.empty(x.numel(), dtype=torch.uint8, device=DEV) for x in xs]
