@@ -889,11 +889,14 @@ def widened_rows(torch, F, WL, wl, layers, stream, reps):
     x8t = torch.empty(K, M, dtype=torch.uint8, device=dev)
     g8 = torch.empty(M, N, dtype=torch.uint8, device=dev)
     s1, a1, s2, a2 = (torch.zeros(1, dtype=torch.float32, device=dev) for _ in range(4))
-    dual = F.bind_fp8_quantize_2d(up.G, F.FP8_E5M2, F.FP8_QUANT_DUAL, g8, g8t, None, s1, a1,
+    # delayed scaling through seeded rings, as in the step (the first calls
+    # seed them): one pass over the input, 2 B read and 1 B per output
+    rg, rx = (F.ScaleRing(wl.hist_len, stream=stream) for _ in range(2))
+    dual = F.bind_fp8_quantize_2d(up.G, F.FP8_E5M2, F.FP8_QUANT_DUAL, g8, g8t, rg, s1, a1,
                                   stream=stream)
-    tq = F.bind_fp8_quantize_2d(up.G, F.FP8_E5M2, F.FP8_QUANT_TRANSPOSED, None, g8t, None, s1, a1,
+    tq = F.bind_fp8_quantize_2d(up.G, F.FP8_E5M2, F.FP8_QUANT_TRANSPOSED, None, g8t, rg, s1, a1,
                                 stream=stream)
-    tx = F.bind_fp8_quantize_2d(up.X, F.FP8_E4M3, F.FP8_QUANT_TRANSPOSED, None, x8t, None, s2, a2,
+    tx = F.bind_fp8_quantize_2d(up.X, F.FP8_E4M3, F.FP8_QUANT_TRANSPOSED, None, x8t, rx, s2, a2,
                                 stream=stream)
     for fn in (dual, tq, tx):
         fn()
