@@ -46,8 +46,9 @@ justification in the repository's design notes):
 Parity pins: every function here is checked in ``tests/test_oracle_*.py``
 against closed forms, an independent library (torch CPU float8 casts and
 float64 matmul), exact rational arithmetic on small cases, or hand-worked
-sequences.  None is "parity unpinned" except NaN-input amax, whose value no
-configuration reaches (documented there).
+sequences.  The amax of an input holding a NaN (the pages are silent; the
+reading taken is that NaN propagates, as IEEE 754-2019 maximum does) is
+pinned against torch's CPU amax.
 """
 
 from __future__ import annotations

@@ -36,6 +36,28 @@ def test_amax_brute_force():
     assert O.amax(np.array([-3.0, 2.0], np.float32)) == 3.0
 
 
+def test_amax_nan_propagates_like_torch():
+    """A NaN among the inputs: the pages are silent; the reading taken is
+    that it propagates (IEEE 754-2019 maximum returns NaN when an operand is
+    NaN).  Pinned against torch's CPU amax, which propagates NaN, at every
+    position of a small tensor and with either sign, and against the
+    infinities, which are ordinary values of the max."""
+    base = np.array([0.5, -3.0, 2.0, -0.0, 1e-30, 7.25], np.float32)
+    for i in range(base.size):
+        for nan in (np.float32(np.nan), np.float32(-np.nan)):
+            x = base.copy()
+            x[i] = nan
+            ref = torch.from_numpy(np.abs(x)).amax().item()
+            assert np.isnan(ref) and np.isnan(O.amax(x)), i
+    for inf in (np.inf, -np.inf):
+        x = base.copy()
+        x[2] = inf
+        assert O.amax(x) == np.float32(torch.from_numpy(np.abs(x)).amax().item()) == np.inf
+    # and the scale of a NaN amax keeps the previous one, like any amax that
+    # is not finite and positive
+    assert O.scale_from_amax(np.float32(np.nan), O.E4M3, 5.0) == 5.0
+
+
 def test_scale_closed_forms():
     assert O.scale_from_amax(1.0, O.E4M3, 7.0) == 448.0
     assert O.scale_from_amax(448.0, O.E4M3, 7.0) == 1.0
